@@ -1,0 +1,243 @@
+"""Benchmark of partitioned attention with selective state reuse on one MI355X.
+
+One step = one denoising step of one attention layer through the whole hot
+path: build the step's selection mask, fresh partial attention for every
+COMPUTE pair (states written into the cache), cache metadata update, and the
+LSE-weighted merge of all P states per row.  Inputs of every step are
+resident in HBM before timing; the anchor step (all fresh) runs untimed first,
+then warm-up and timed steps cycle over the workload's steady-state steps
+t = 1 .. steps-1 with their masks.
+
+Prints one JSON line.  value = effective (dense-equivalent) attention
+TFLOP/s = 4 N^2 d H / time per step, so reuse can lift it above what the
+fresh work alone would run at.  "roofline" describes the dominant kernel,
+timed with HIP events on the stream it runs on; "cpu_baseline" times the fp64
+oracle on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "effective attention TFLOP/s and ms/denoise-step at given reuse ratio, 1 GPU"
+DEFAULT_WORKLOAD = "image"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40, help="timed steps")
+    ap.add_argument("--warmup", type=int, default=8, help="untimed steady-state steps after the anchor")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    help="image | video_100 | video_50 | video_25 | long | stress | tiny")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the oracle sample (0: auto)")
+    return ap.parse_args()
+
+
+def fresh_flops(w, mask) -> float:
+    """4 * len_q * len_k * d per fresh pair and head (QK^T and PV)."""
+    lens = np.array([min(w.S, w.N - p * w.S) for p in range(w.P)], dtype=np.float64)
+    return float(4.0 * w.d * w.H * (np.outer(lens, lens) * mask).sum())
+
+
+def merge_bytes(w) -> float:
+    """Per row and head: read P states of d+1 floats, write one."""
+    return float(w.H * w.N * (w.P + 1) * (w.d + 1) * 4)
+
+
+def state_store_bytes(w, mask) -> float:
+    lens = np.array([min(w.S, w.N - p * w.S) for p in range(w.P)], dtype=np.float64)
+    return float(w.H * (w.d + 1) * 4 * (lens[:, None] * mask).sum())
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "context_state_reuse_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str, workload: str, src_hash: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as f:
+        for ln in f:
+            if ln.startswith("- ") and ":" in ln:
+                k, v = ln[2:].split(":", 1)
+                rec[k.strip()] = v.strip().strip("`")
+    if rec.get("kernel_source_sha") != src_hash:
+        return None
+    try:
+        return float(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, heads: int):
+    """fp64 oracle on one steady-state step of `heads` heads (anchor untimed)."""
+    from oracle.reuse import StateReuseOracle
+    from oracle.masks import step_mask
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    hs = list(range(heads))
+    stream = synth.InputStream(w, hs)
+    orc = StateReuseOracle(w.N, w.P, w.d)
+    t_step = None
+    for t in range(2):
+        qb, kb, vb = stream.next()
+        inp = {h: (synth.bf16_bits_to_f64(qb[i]), synth.bf16_bits_to_f64(kb[i]), synth.bf16_bits_to_f64(vb[i]))
+               for i, h in enumerate(hs)}
+        t0 = time.perf_counter()
+        orc.step(t, step_mask(w, t), inp)
+        t_step = time.perf_counter() - t0
+    dense = 4.0 * w.N * w.N * w.d * heads
+    return {"value": dense / t_step / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{w.name}: steady-state step t=1 (after an untimed anchor step) for {heads} of {w.H} "
+                      f"heads, all {w.N} rows; fp64 NumPy, {t_step:.2f} s; effective TFLOP/s counts "
+                      f"4*N^2*d per sampled head"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the path runs all P partitions on one device and has no "
+              "multi-GPU mode; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import context_state_reuse_amd as lib
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+    w = synth.get(args.workload)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    # ---- inputs of every step resident in HBM
+    stream = synth.InputStream(w)
+    qkv = []
+    for t in range(w.steps):
+        bits = stream.next()
+        qkv.append(tuple(torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev) for b in bits))
+    del stream
+    cache = lib.StateCache(w.H, w.N, w.d, w.P)
+    O = torch.empty((w.H, w.N, w.d), dtype=torch.float32, device=dev)
+    LSE = torch.empty((w.H, w.N), dtype=torch.float32, device=dev)
+
+    step_no = [0]
+
+    def step(t: int, events=None):
+        mask = lib.workload_mask(w, t)
+        Q, K, V = qkv[t]
+        if events is not None:
+            events[0].record()
+        lib.ditango_attn_partial(Q, K, V, mask, cache)
+        if events is not None:
+            events[1].record()
+        lib.ditango_state_cache_update(cache, mask, step_no[0])
+        lib.ditango_state_merge(cache, O, LSE)
+        if events is not None:
+            events[2].record()
+        step_no[0] += 1
+        return mask
+
+    steady = list(range(1, w.steps)) or [0]
+    step(0)                                         # anchor: all fresh
+    for i in range(args.warmup):
+        step(steady[i % len(steady)])
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    masks = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        masks.append(step(steady[i % len(steady)], evs[i]))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    ms_step = elapsed * 1e3 / args.steps
+    t_partial = np.mean([e[0].elapsed_time(e[1]) for e in evs])      # ms
+    t_merge = np.mean([e[1].elapsed_time(e[2]) for e in evs])
+    dense = 4.0 * w.N * w.N * w.d * w.H
+    value = dense / (ms_step * 1e-3) / 1e12
+    fresh = np.mean([fresh_flops(w, m) for m in masks])
+    reuse = 1.0 - np.mean([m.mean() for m in masks])
+    mb = merge_bytes(w)
+    sb = np.mean([state_store_bytes(w, m) for m in masks])
+
+    partial_tflops = fresh / (t_partial * 1e-3) / 1e12
+    merge_gbs = mb / (t_merge * 1e-3) / 1e9
+    src = source_hash("partial.hip")
+    if t_partial >= t_merge:
+        roof = {"kernel": "partial_kernel", "bound": "mfma", "achieved": round(partial_tflops, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(partial_tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": stored_traffic("partial", w.name, src),
+                "avg_launch_ms": round(float(t_partial), 4),
+                "algorithmic_per_launch": f"{fresh:.4e} FLOP (4*len_q*len_k*d per fresh pair and head)"}
+    else:
+        roof = {"kernel": "merge_kernel", "bound": "hbm", "achieved": round(merge_gbs, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(merge_gbs / PEAK_HBM_GBS, 4),
+                "traffic": stored_traffic("merge", w.name, source_hash("merge.hip")),
+                "avg_launch_ms": round(float(t_merge), 4),
+                "algorithmic_per_launch": f"{mb:.4e} B (P*(d+1)*4 read + (d+1)*4 written per row and head)"}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.F}x{w.Hh}x{w.W} = {w.N} tokens, H={w.H}, d={w.d}, P={w.P}, "
+                               f"{w.policy}-{w.n_fresh} mask", "tokens": w.N, "heads": w.H, "head_dim": w.d,
+                   "partitions": w.P, "reuse_ratio": round(float(reuse), 4),
+                   "fresh_pairs_per_step": float(np.mean([m.sum() for m in masks])),
+                   "parallelism": "none (all partitions on one GPU)"},
+        "roofline": roof,
+        "kernels": {
+            "partial": {"ms": round(float(t_partial), 4), "tflops": round(partial_tflops, 2),
+                        "mfma_frac": round(partial_tflops / PEAK_BF16_TFLOPS, 4), "fresh_flop": fresh,
+                        "state_store_bytes": sb},
+            "merge": {"ms": round(float(t_merge), 4), "gbs": round(merge_gbs, 1),
+                      "hbm_frac": round(merge_gbs / PEAK_HBM_GBS, 4), "bytes": mb},
+        },
+    }
+    if not args.no_cpu_baseline:
+        heads = args.cpu_heads or 1
+        out["cpu_baseline"] = cpu_baseline(w, heads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

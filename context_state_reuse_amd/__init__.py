@@ -1,0 +1,12 @@
+"""Partitioned softmax attention with selective attention-state reuse on MI355X.
+
+Python face of libditango.so (C ABI in include/ditango.h).  All work runs in
+the library's HIP kernels for gfx950; this package only marshals torch
+tensors, host masks and streams into the C calls.
+"""
+from .binding import (DITANGO_EHIP, DITANGO_EINVAL, DITANGO_ENOCACHE,  # noqa: F401
+                      DITANGO_MASK_ALL, DITANGO_MASK_NEAREST, DITANGO_MASK_NONE,
+                      DITANGO_MASK_RADIUS, DITANGO_MASK_RANDOM, DITANGO_OK, EXPORTED,
+                      DitangoError, StateCache, ditango_attn_partial, ditango_mask_build,
+                      ditango_state_cache_update, ditango_state_merge, ditango_states_bytes,
+                      ditango_version, make_shape, workload_mask)

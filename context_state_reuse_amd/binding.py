@@ -1,0 +1,198 @@
+"""ctypes binding of libditango.so: argument marshalling only.
+
+The functions keep the C names of include/ditango.h.  Torch tensors supply
+device memory and the current HIP stream; every computation runs in the
+library's HIP kernels.  There is no fallback: if the library is not built,
+importing this module raises.
+
+torch is imported before the library is opened: torch ships its own HIP
+runtime under the same soname (libamdhip64.so.7) as the system one the
+library was linked against, and loading torch first makes both use torch's
+copy, so the process has a single HIP runtime.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch  # noqa: F401  -- must precede the library: one HIP runtime per process
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libditango.so")
+
+DITANGO_OK = 0
+DITANGO_EINVAL = -1
+DITANGO_ENOCACHE = -2
+DITANGO_EHIP = -3
+DITANGO_MAX_P = 32
+
+DITANGO_MASK_ALL = 0
+DITANGO_MASK_NONE = 1
+DITANGO_MASK_RADIUS = 2
+DITANGO_MASK_NEAREST = 3
+DITANGO_MASK_RANDOM = 4
+
+MASK_POLICIES = {"all": DITANGO_MASK_ALL, "none": DITANGO_MASK_NONE, "radius": DITANGO_MASK_RADIUS,
+                 "nearest": DITANGO_MASK_NEAREST, "random": DITANGO_MASK_RANDOM}
+
+EXPORTED = ("ditango_states_bytes", "ditango_states_init", "ditango_attn_partial",
+            "ditango_state_cache_update", "ditango_state_merge", "ditango_mask_build",
+            "ditango_last_error", "ditango_version")
+
+
+class DitangoError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"ditango error {code}: {message}")
+        self.code = code
+
+
+class ditango_shape_t(ctypes.Structure):
+    _fields_ = [("H", ctypes.c_int32), ("N", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("P", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class ditango_states_t(ctypes.Structure):
+    _fields_ = [("shape", ditango_shape_t), ("S", ctypes.c_int32), ("O", ctypes.c_void_p),
+                ("LSE", ctypes.c_void_p), ("tc", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it first (python -m context_state_reuse_amd.build)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, u8p = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_uint8)
+    lib.ditango_states_bytes.restype = ctypes.c_size_t
+    lib.ditango_states_bytes.argtypes = [ctypes.POINTER(ditango_shape_t), ctypes.POINTER(ctypes.c_size_t),
+                                         ctypes.POINTER(ctypes.c_size_t)]
+    lib.ditango_states_init.restype = ctypes.c_int
+    lib.ditango_states_init.argtypes = [ctypes.POINTER(ditango_states_t), ctypes.POINTER(ditango_shape_t),
+                                        vp, vp, vp]
+    lib.ditango_attn_partial.restype = ctypes.c_int
+    lib.ditango_attn_partial.argtypes = [vp, vp, vp, u8p, ctypes.POINTER(ditango_states_t), vp]
+    lib.ditango_state_cache_update.restype = ctypes.c_int
+    lib.ditango_state_cache_update.argtypes = [ctypes.POINTER(ditango_states_t), u8p, i32, u8p]
+    lib.ditango_state_merge.restype = ctypes.c_int
+    lib.ditango_state_merge.argtypes = [ctypes.POINTER(ditango_states_t), vp, vp, vp]
+    lib.ditango_mask_build.restype = ctypes.c_int
+    lib.ditango_mask_build.argtypes = [i32, i32, i32, ctypes.c_uint64, u8p]
+    lib.ditango_last_error.restype = ctypes.c_char_p
+    lib.ditango_last_error.argtypes = []
+    lib.ditango_version.restype = ctypes.c_int32
+    lib.ditango_version.argtypes = []
+    return lib
+
+
+lib = _load()
+
+
+def _check(rc: int) -> None:
+    if rc != DITANGO_OK:
+        raise DitangoError(rc, lib.ditango_last_error().decode())
+
+
+def _u8(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+
+
+def _mask(mask, P: int) -> np.ndarray:
+    m = np.ascontiguousarray(np.asarray(mask, dtype=np.uint8))
+    if m.shape != (P, P):
+        raise ValueError(f"mask must be ({P}, {P}), got {m.shape}")
+    return m
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_shape(H: int, N: int, d: int, P: int, scale: float | None = None) -> ditango_shape_t:
+    return ditango_shape_t(H, N, d, P, float(1.0 / np.sqrt(d) if scale is None else scale))
+
+
+def ditango_states_bytes(shape: ditango_shape_t) -> tuple[int, int]:
+    ob, lb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    if lib.ditango_states_bytes(ctypes.byref(shape), ctypes.byref(ob), ctypes.byref(lb)) == 0:
+        raise DitangoError(DITANGO_EINVAL, lib.ditango_last_error().decode())
+    return ob.value, lb.value
+
+
+class StateCache:
+    """The attention-state cache: device O/LSE slots (torch) and host t_c."""
+
+    def __init__(self, H: int, N: int, d: int, P: int, scale: float | None = None, device="cuda"):
+        import torch
+        self.shape = make_shape(H, N, d, P, scale)
+        ob, lb = ditango_states_bytes(self.shape)
+        S = -(-N // P)
+        assert ob == H * P * P * S * d * 4 and lb == H * P * P * S * 4
+        self.O = torch.empty((H, P * P, S, d), dtype=torch.float32, device=device)
+        self.LSE = torch.empty((H, P * P, S), dtype=torch.float32, device=device)
+        self.tc = np.full(P * P, -1, dtype=np.int32)
+        self.st = ditango_states_t()
+        _check(lib.ditango_states_init(ctypes.byref(self.st), ctypes.byref(self.shape),
+                                       ctypes.c_void_p(self.O.data_ptr()), ctypes.c_void_p(self.LSE.data_ptr()),
+                                       ctypes.c_void_p(self.tc.ctypes.data)))
+        self.H, self.N, self.d, self.P, self.S = H, N, d, P, S
+
+    @property
+    def tc_matrix(self) -> np.ndarray:
+        return self.tc.reshape(self.P, self.P).copy()
+
+
+def _qkv(x, cache: StateCache, name: str):
+    import torch
+    if not (isinstance(x, torch.Tensor) and x.is_cuda and x.dtype == torch.bfloat16 and x.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous bfloat16 device tensor")
+    if tuple(x.shape) != (cache.H, cache.N, cache.d):
+        raise ValueError(f"{name} must have shape {(cache.H, cache.N, cache.d)}, got {tuple(x.shape)}")
+    return ctypes.c_void_p(x.data_ptr())
+
+
+def ditango_attn_partial(Q, K, V, mask, cache: StateCache, stream=None) -> None:
+    m = _mask(mask, cache.P)
+    _check(lib.ditango_attn_partial(_qkv(Q, cache, "Q"), _qkv(K, cache, "K"), _qkv(V, cache, "V"),
+                                    _u8(m), ctypes.byref(cache.st), _stream(stream)))
+
+
+def ditango_state_cache_update(cache: StateCache, mask, step: int) -> np.ndarray:
+    m = _mask(mask, cache.P)
+    reused = np.zeros((cache.P, cache.P), dtype=np.uint8)
+    _check(lib.ditango_state_cache_update(ctypes.byref(cache.st), _u8(m), int(step), _u8(reused)))
+    return reused
+
+
+def ditango_state_merge(cache: StateCache, O=None, LSE=None, stream=None):
+    import torch
+    if O is None:
+        O = torch.empty((cache.H, cache.N, cache.d), dtype=torch.float32, device=cache.O.device)
+    if LSE is None:
+        LSE = torch.empty((cache.H, cache.N), dtype=torch.float32, device=cache.O.device)
+    for t, shp, nm in ((O, (cache.H, cache.N, cache.d), "O"), (LSE, (cache.H, cache.N), "LSE")):
+        if not (t.is_cuda and t.dtype == torch.float32 and t.is_contiguous() and tuple(t.shape) == shp):
+            raise ValueError(f"{nm} must be a contiguous float32 device tensor of shape {shp}")
+    _check(lib.ditango_state_merge(ctypes.byref(cache.st), ctypes.c_void_p(O.data_ptr()),
+                                   ctypes.c_void_p(LSE.data_ptr()), _stream(stream)))
+    return O, LSE
+
+
+def ditango_mask_build(policy, P: int, n: int = 0, seed: int = 0) -> np.ndarray:
+    pol = MASK_POLICIES[policy] if isinstance(policy, str) else int(policy)
+    out = np.zeros((P, P), dtype=np.uint8) if 1 <= P <= DITANGO_MAX_P else np.zeros(1, dtype=np.uint8)
+    _check(lib.ditango_mask_build(pol, int(P), int(n), ctypes.c_uint64(seed & ((1 << 64) - 1)), _u8(out)))
+    return out
+
+
+def ditango_version() -> int:
+    return int(lib.ditango_version())
+
+
+def workload_mask(w, t: int) -> np.ndarray:
+    """Mask of step t of a workload, built by the library (step 0: all fresh)."""
+    if t == 0:
+        return ditango_mask_build("all", w.P)
+    return ditango_mask_build(w.policy, w.P, w.n_fresh, 1000 * w.cfg_id + t)

@@ -1,0 +1,147 @@
+/*
+ * ditango.h -- C ABI of the MI355X (gfx950) library for partitioned softmax
+ * attention with selective attention-state reuse across denoising steps.
+ *
+ * Source of the method: "DiTango: Cost-Effective Parallel Diffusion
+ * Generation with Selective Attention State Reuse" (the DiTango page).
+ *
+ *   - A DiT layer's 3D-flattened token sequence of N tokens is cut into P
+ *     contiguous partitions of S = ceil(N/P) tokens (the last one may be
+ *     shorter); sequence-wise partitioning as in Ring-CP (introduction).
+ *   - For a (query partition q, KV partition k) pair, the attention state is
+ *     (OUT, LSE) per query row (attention-state section): with scaled scores
+ *     z_j = scale * q.k_j over the keys j of partition k,
+ *         LSE = log sum_j exp(z_j)              (natural log)
+ *         OUT = sum_j exp(z_j - LSE) * v_j      (normalised within the pair)
+ *   - Each step, every pair is either computed fresh (COMPUTE) or reused from
+ *     the state cache (REUSE), per a P x P selection mask (state selection
+ *     section; the Fig. 6 example).  t_c is the last step a pair was computed.
+ *   - The final output of a row is the composition (Eq. 4) of its P states:
+ *         LSE = log sum_k exp(LSE_k),   OUT = sum_k exp(LSE_k - LSE) * OUT_k.
+ *
+ * Conventions shared by every call:
+ *   - All device buffers are allocated and owned by the caller; the library
+ *     allocates no device memory, keeps no global state besides a
+ *     thread-local error string, and never synchronises the stream.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued on it and the call returns.
+ *   - Q, K, V are bfloat16, laid out [H][N][d] contiguous, in device memory.
+ *   - The mask is a host array uint8 [P][P] (row = query partition q, column
+ *     = KV partition k); 1 = COMPUTE (fresh), 0 = REUSE.
+ *   - Return value: DITANGO_OK (0) or a negative code; the message of the
+ *     last failure on the calling thread is ditango_last_error().
+ *   - One ditango_states_t must not be used by two threads at once.
+ */
+#ifndef DITANGO_H
+#define DITANGO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DITANGO_OK        0
+#define DITANGO_EINVAL   (-1)  /* bad argument: null pointer, bad shape, bad mask   */
+#define DITANGO_ENOCACHE (-2)  /* a pair marked REUSE has never been computed       */
+#define DITANGO_EHIP     (-3)  /* a HIP runtime call or kernel launch failed        */
+
+#define DITANGO_MAX_P 32       /* largest partition count                             */
+
+/* Shape of one attention layer.  d must be 64, 72 or 128; 1 <= P <= 32;
+ * every partition must be non-empty (P * ceil(N/P) - N < ceil(N/P)). */
+typedef struct {
+  int32_t H;      /* attention heads                                   */
+  int32_t N;      /* tokens in the flattened sequence                  */
+  int32_t d;      /* head dimension                                    */
+  int32_t P;      /* partitions                                        */
+  float   scale;  /* score scale applied to q.k, normally 1/sqrt(d)    */
+} ditango_shape_t;
+
+/* The attention-state cache (attention-state section and the
+ * ring-based composed attention section: fresh states are stored for
+ * reuse at later steps).  One slot per (head, pair), pair id = q*P + k:
+ *   O   device fp32 [H][P*P][S][d]  -- row r of slot (h, q*P+k) is OUT of
+ *                                     query row q*S + r against partition k
+ *   LSE device fp32 [H][P*P][S]     -- its log-sum-exp
+ *   tc  host int32 [P*P]            -- step at which the pair was last fresh,
+ *                                     -1 if never (t_c of the state-selection
+ *                                     section)
+ * Rows at or beyond the length of a ragged last partition are never written
+ * or read.  The struct borrows the three buffers; the caller frees them. */
+typedef struct {
+  ditango_shape_t shape;
+  int32_t  S;     /* rows per partition, ceil(N/P); set by ditango_states_init */
+  float*   O;
+  float*   LSE;
+  int32_t* tc;
+} ditango_states_t;
+
+/* Bytes the caller must allocate for the cache of `shape`: *o_bytes for O
+ * and *lse_bytes for LSE (either pointer may be NULL).  Returns their sum, or
+ * 0 if the shape is invalid (message in ditango_last_error()). */
+size_t ditango_states_bytes(const ditango_shape_t* shape, size_t* o_bytes, size_t* lse_bytes);
+
+/* Bind caller-owned buffers to `st` and mark every pair empty (tc[] = -1).
+ * O and LSE must be 16-byte aligned device pointers of the sizes above.
+ * Errors: DITANGO_EINVAL. */
+int ditango_states_init(ditango_states_t* st, const ditango_shape_t* shape,
+                        float* O, float* LSE, int32_t* tc);
+
+/* Fresh partial attention for every pair with mask[q][k] = 1 (COMPUTE), on
+ * every head: writes that pair's (OUT, LSE) over its slot, overwriting the
+ * stale state.  Pairs with mask = 0 (REUSE) are not touched and no work is
+ * launched for them.  Computes with bf16 inputs, fp32 accumulation, fp32
+ * softmax statistics; probabilities are rounded to bf16 before the product
+ * with V.  Checks before launching anything that every REUSE pair holds a
+ * state (tc >= 0), else returns DITANGO_ENOCACHE.  Does not change tc (see
+ * ditango_state_cache_update).  Errors: EINVAL, ENOCACHE, EHIP. */
+int ditango_attn_partial(const void* Q, const void* K, const void* V,
+                         const uint8_t* mask, ditango_states_t* st, void* stream);
+
+/* Commit step `step` to the cache metadata (host only, no device work):
+ * tc[p] = step for every pair with mask = 1; REUSE pairs keep their tc.
+ * If reused_out is not NULL it receives uint8 [P][P] with 1 exactly where
+ * the pair is reused this step.  A mask of all ones is an anchor step: every
+ * t_c becomes `step` (anchor-step section).  Errors: EINVAL (step < 0, step
+ * below an existing tc, or a REUSE pair that was never computed). */
+int ditango_state_cache_update(ditango_states_t* st, const uint8_t* mask, int32_t step,
+                               uint8_t* reused_out);
+
+/* Compose (Eq. 4) the P pair states of every row into the final output:
+ *   O   device fp32 [H][N][d],  LSE device fp32 [H][N] (natural log).
+ * Reads every slot of the cache; every pair must hold a state (tc >= 0),
+ * else DITANGO_ENOCACHE.  Errors: EINVAL, ENOCACHE, EHIP. */
+int ditango_state_merge(const ditango_states_t* st, float* O, float* LSE, void* stream);
+
+/* Selection-mask builder for the locality policies used by the workloads
+ * (state-selection section; locality of Fig. 5a).  Writes uint8 [P][P]:
+ *   DITANGO_MASK_ALL      every pair fresh (an anchor step)
+ *   DITANGO_MASK_NONE     every pair reused
+ *   DITANGO_MASK_RADIUS   fresh iff |q - k| <= n
+ *   DITANGO_MASK_NEAREST  per row q, the n partitions k with the smallest
+ *                         |q - k|, ties to the lower k
+ *   DITANGO_MASK_RANDOM   per row q, q plus n-1 distinct others drawn with
+ *                         SplitMix64(seed): rows in order, candidates
+ *                         c = [k != q] ascending, for i < n-1 swap c[i] with
+ *                         c[i + next() % (P-1-i)], take c[0..n-2]
+ * Errors: EINVAL (bad policy, P outside 1..32, n outside its range). */
+#define DITANGO_MASK_ALL     0
+#define DITANGO_MASK_NONE    1
+#define DITANGO_MASK_RADIUS  2
+#define DITANGO_MASK_NEAREST 3
+#define DITANGO_MASK_RANDOM  4
+int ditango_mask_build(int32_t policy, int32_t P, int32_t n, uint64_t seed, uint8_t* mask_out);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* ditango_last_error(void);
+
+/* Library ABI version (this header: 1). */
+int32_t ditango_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DITANGO_H */

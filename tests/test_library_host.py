@@ -1,0 +1,173 @@
+"""The C-ABI library on the CPU: it loads, exports what include/ditango.h
+declares, and its host logic (masks, t_c, argument checks) is right.  No
+call here launches GPU work."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+from oracle.masks import step_mask as oracle_step_mask
+from oracle.masks import nearest_mask, radius_mask, random_mask
+
+import context_state_reuse_amd as lib
+from context_state_reuse_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "ditango.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ditango_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 8
+    assert set(names) == set(binding.EXPORTED)
+    for n in names:
+        assert hasattr(binding.lib, n), n
+        ctypes.CDLL(binding._LIB_PATH)[n]  # raises AttributeError if missing
+
+
+def test_version_and_struct_layout():
+    assert lib.ditango_version() == 1
+    assert ctypes.sizeof(binding.ditango_shape_t) == 20
+    assert binding.ditango_states_t.O.offset == 24 and ctypes.sizeof(binding.ditango_states_t) == 48
+
+
+@pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
+def test_states_bytes(name):
+    w = synth.get(name)
+    ob, lb = lib.ditango_states_bytes(lib.make_shape(w.H, w.N, w.d, w.P))
+    assert ob == w.H * w.P * w.P * w.S * w.d * 4
+    assert lb == w.H * w.P * w.P * w.S * 4
+    # a state holds d+1 floats per row, about half the 2*d of a KV pair per
+    # key before the fp32-versus-bf16 factor (attention-state section)
+    assert ob // (w.H * w.P * w.P * w.S) == 2 * (2 * w.d)
+
+
+@pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
+def test_mask_builder_matches_oracle(name):
+    w = synth.get(name)
+    for t in range(w.steps):
+        assert np.array_equal(lib.workload_mask(w, t), oracle_step_mask(w, t)), (name, t)
+
+
+def test_mask_builder_policies_sweep():
+    for P in (1, 2, 3, 5, 8, 16, 31, 32):
+        for n in range(0, P + 1):
+            assert np.array_equal(lib.ditango_mask_build("radius", P, n), radius_mask(P, n))
+        for n in range(1, P + 1):
+            assert np.array_equal(lib.ditango_mask_build("nearest", P, n), nearest_mask(P, n))
+            for seed in (0, 1, 12345, 2**63 + 7):
+                assert np.array_equal(lib.ditango_mask_build("random", P, n, seed), random_mask(P, n, seed))
+        assert lib.ditango_mask_build("all", P).sum() == P * P
+        assert lib.ditango_mask_build("none", P).sum() == 0
+
+
+@pytest.mark.parametrize("args", [("nearest", 8, 0), ("nearest", 8, 9), ("random", 8, 0),
+                                  ("radius", 8, -1), ("all", 33, 0), ("all", 0, 0), (9, 4, 1)])
+def test_mask_builder_rejects(args):
+    with pytest.raises(lib.DitangoError) as e:
+        lib.ditango_mask_build(*args)
+    assert e.value.code == lib.DITANGO_EINVAL
+
+
+@pytest.mark.parametrize("H,N,d,P", [(1, 10, 96, 2), (1, 10, 64, 0), (1, 10, 64, 33), (0, 10, 64, 2),
+                                     (1, 3, 64, 4), (1, 10, 64, 6)])
+def test_shape_rejected(H, N, d, P):
+    ob = ctypes.c_size_t(0)
+    assert binding.lib.ditango_states_bytes(ctypes.byref(lib.make_shape(H, N, d, P)), ctypes.byref(ob), None) == 0
+    assert binding.lib.ditango_last_error()
+
+
+class _FakeStates:
+    """A states struct bound to fake (never dereferenced) device addresses."""
+
+    def __init__(self, H=2, N=100, d=64, P=4):
+        self.shape = lib.make_shape(H, N, d, P)
+        self.tc = np.zeros(P * P, np.int32)
+        self.st = binding.ditango_states_t()
+        rc = binding.lib.ditango_states_init(ctypes.byref(self.st), ctypes.byref(self.shape),
+                                             ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000),
+                                             ctypes.c_void_p(self.tc.ctypes.data))
+        assert rc == 0
+        self.P = P
+
+
+def _u8(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+
+
+def test_init_marks_all_pairs_empty():
+    f = _FakeStates()
+    assert np.all(f.tc == -1) and f.st.S == 25
+
+
+def test_partial_refuses_reuse_of_empty_pair_before_launch():
+    f = _FakeStates()
+    mask = radius_mask(4, 1)
+    fake = ctypes.c_void_p(0x30000)
+    rc = binding.lib.ditango_attn_partial(fake, fake, fake, _u8(mask), ctypes.byref(f.st), None)
+    assert rc == lib.DITANGO_ENOCACHE
+    assert "never computed" in binding.lib.ditango_last_error().decode()
+
+
+def test_partial_and_merge_argument_checks():
+    f = _FakeStates()
+    fake = ctypes.c_void_p(0x30000)
+    ones = np.ones((4, 4), np.uint8)
+    bad = ones.copy()
+    bad[1, 2] = 2
+    assert binding.lib.ditango_attn_partial(fake, fake, fake, _u8(bad), ctypes.byref(f.st), None) == lib.DITANGO_EINVAL
+    assert binding.lib.ditango_attn_partial(None, fake, fake, _u8(ones), ctypes.byref(f.st), None) == lib.DITANGO_EINVAL
+    odd = ctypes.c_void_p(0x30002)
+    assert binding.lib.ditango_attn_partial(odd, fake, fake, _u8(ones), ctypes.byref(f.st), None) == lib.DITANGO_EINVAL
+    # merge before any state exists
+    assert binding.lib.ditango_state_merge(ctypes.byref(f.st), fake, fake, None) == lib.DITANGO_ENOCACHE
+    f.st.S = 24
+    assert binding.lib.ditango_state_merge(ctypes.byref(f.st), fake, fake, None) == lib.DITANGO_EINVAL
+
+
+def test_cache_update_bookkeeping():
+    f = _FakeStates(P=4)
+    upd = binding.lib.ditango_state_cache_update
+    reused = np.zeros((4, 4), np.uint8)
+    m1 = radius_mask(4, 1)
+    # reusing a never-computed pair is refused
+    assert upd(ctypes.byref(f.st), _u8(m1), 0, _u8(reused)) == lib.DITANGO_EINVAL
+    assert np.all(f.tc == -1)
+    # anchor
+    assert upd(ctypes.byref(f.st), _u8(np.ones((4, 4), np.uint8)), 0, _u8(reused)) == 0
+    assert np.all(f.tc == 0) and reused.sum() == 0
+    assert upd(ctypes.byref(f.st), _u8(m1), 1, _u8(reused)) == 0
+    assert np.array_equal(reused, 1 - m1)
+    want = np.where(m1.ravel() == 1, 1, 0)
+    assert np.array_equal(f.tc, want)
+    m0 = radius_mask(4, 0)
+    assert upd(ctypes.byref(f.st), _u8(m0), 2, None) == 0
+    want[m0.ravel() == 1] = 2
+    assert np.array_equal(f.tc, want)
+    # time does not run backwards, steps are non-negative
+    assert upd(ctypes.byref(f.st), _u8(m0), 1, None) == lib.DITANGO_EINVAL
+    assert upd(ctypes.byref(f.st), _u8(m0), -1, None) == lib.DITANGO_EINVAL
+    # an anchor mid-run resets every t_c
+    assert upd(ctypes.byref(f.st), _u8(np.ones((4, 4), np.uint8)), 5, None) == 0
+    assert np.all(f.tc == 5)
+
+
+def test_cache_update_matches_oracle_tc_over_a_workload():
+    """t_c after every step equals the oracle's bookkeeping (stress workload masks)."""
+    from oracle.reuse import StateReuseOracle
+    w = synth.get("stress")
+    f = _FakeStates(H=1, N=w.N, d=64, P=w.P)
+    orc = StateReuseOracle(w.N, w.P, w.d, rows=[0])  # one row: bookkeeping only
+    for t in range(w.steps):
+        m = oracle_step_mask(w, t)
+        assert binding.lib.ditango_state_cache_update(ctypes.byref(f.st), _u8(m), t, None) == 0
+        orc.tc[m == 1] = t
+        assert np.array_equal(f.tc.reshape(w.P, w.P), orc.tc)
