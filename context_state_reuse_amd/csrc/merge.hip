@@ -1,14 +1,20 @@
 // Composition of the P pair states of every row (DiTango page, Eq. 4, the
 // n-ary form of its associative and commutative state composition):
-//   m = max_k LSE_k,  w_k = exp(LSE_k - m),  Z = sum_k w_k
-//   OUT = sum_k w_k OUT_k / Z,  LSE = m + log Z
+//   m = max_k LSE_k,  w_k = exp(LSE_k - m) / Z,  Z = sum_k exp(LSE_k - m)
+//   OUT = sum_k w_k OUT_k,  LSE = m + log Z
 // The P slots of a row mix states written this step (fresh) and states
 // written at earlier steps (reused); the merge does not distinguish them.
 //
 // HBM-bound: per row and head it reads P*(d+1) floats and writes d+1.
-// Each thread owns 4 consecutive dims of one row, so a wave reads whole
-// rows of each slot as contiguous 16-byte-per-lane runs; the row's LSE
-// values are the same address for all its threads (one broadcast load).
+// A block owns R consecutive rows of one query partition of one head.
+//   1. one lane per (row, slot) loads LSE_k, the row's lanes reduce max and
+//      sum with cross-lane shuffles, and the normalised weights go to LDS;
+//   2. for every slot k the block streams the R*d contiguous floats of rows
+//      [i0, i0+R) of slot (q, k) with 16-byte loads -- all P slots' loads are
+//      issued before the first is used, about 32 per thread -- and
+//      accumulates w_k * OUT_k in registers;
+//   3. the R*d outputs are written contiguously.
+// R = 256 / PMAX keeps 32 independent loads in flight per thread at every P.
 
 #include <hip/hip_runtime.h>
 
@@ -22,55 +28,86 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 
 template <int D, int PMAX>
-__global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
-  constexpr int TPR = D / 4;  // threads per row
-  const int64_t total = static_cast<int64_t>(p.H) * p.N * TPR;
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (gid >= total) return;
-  const int ch = static_cast<int>(gid % TPR);
-  const int64_t hr = gid / TPR;                 // h * N + r
-  const int r = static_cast<int>(hr % p.N);
-  const int h = static_cast<int>(hr / p.N);
-  const int q = r / p.S;
-  const int i = r - q * p.S;
-  const size_t slot0 = (static_cast<size_t>(h) * p.P + q) * p.P;  // slot of pair (q, 0)
-  const float* L = p.LSEs + slot0 * p.S + i;                         // + k * S
-  const float* Ob = p.Os + (slot0 * p.S + i) * D + ch * 4;           // + k * S * D
-  const size_t ostride = static_cast<size_t>(p.S) * D;
+__global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p, int row_tiles) {
+  constexpr int R = kThreads / PMAX;                  // rows per block
+  constexpr int CH = R * D / 4;                       // float4 chunks per slot block
+  constexpr int PER = (CH + kThreads - 1) / kThreads; // chunks per thread
+  __shared__ float w_lds[R][PMAX];
 
-  float lse[PMAX];
-  f32x4 o[PMAX];
-  float m = -__builtin_inff();
+  const int tid = threadIdx.x;
+  const int rt = blockIdx.x % row_tiles;
+  const int hq = blockIdx.x / row_tiles;              // h * P + q
+  const int q = hq % p.P;
+  const int h = hq / p.P;
+  const int len_q = min(p.S, p.N - q * p.S);
+  const int i0 = rt * R;
+  const int rows = min(R, len_q - i0);
+  const size_t slot0 = static_cast<size_t>(hq) * p.P;  // slot of pair (q, 0) of head h
+
+  // 1. weights
+  {
+    const int r = tid / PMAX, k = tid % PMAX;
+    const bool live = k < p.P && r < rows;
+    float l = live ? p.LSEs[(slot0 + k) * p.S + i0 + r] : -__builtin_inff();
+    float m = l;
+#pragma unroll
+    for (int off = 1; off < PMAX; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+    const float e = live ? __builtin_amdgcn_exp2f((l - m) * 1.4426950408889634f) : 0.0f;
+    float z = e;
+#pragma unroll
+    for (int off = 1; off < PMAX; off <<= 1) z += __shfl_xor(z, off);
+    w_lds[r][k] = e / z;
+    if (k == 0 && r < rows)
+      p.LSE[static_cast<size_t>(h) * p.N + q * p.S + i0 + r] =
+          m + __builtin_amdgcn_logf(z) * 0.69314718055994531f;
+  }
+  __syncthreads();
+
+  // 2. stream the slots
+  const int valid = rows * (D / 4);
+  f32x4 acc[PER];
+  f32x4 o[PMAX][PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < PMAX; ++k) {
     if (k < p.P) {
-      lse[k] = L[static_cast<size_t>(k) * p.S];
-      o[k] = *reinterpret_cast<const f32x4*>(Ob + k * ostride);
-      m = fmaxf(m, lse[k]);
+      const float* src = p.Os + ((slot0 + k) * p.S + i0) * D;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int c = tid + j * kThreads;
+        if (c < valid) o[k][j] = *reinterpret_cast<const f32x4*>(src + 4 * c);
+      }
     }
   }
-  const float log2e = 1.4426950408889634f;
-  float z = 0.0f;
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int k = 0; k < PMAX; ++k) {
     if (k < p.P) {
-      const float w = __builtin_amdgcn_exp2f((lse[k] - m) * log2e);
-      z += w;
-      acc += w * o[k];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int c = tid + j * kThreads;
+        if (c < valid) acc[j] += w_lds[c / (D / 4)][k] * o[k][j];
+      }
     }
   }
-  const float inv = 1.0f / z;
-  *reinterpret_cast<f32x4*>(p.O + hr * D + ch * 4) = acc * inv;
-  if (ch == 0) p.LSE[hr] = m + __builtin_amdgcn_logf(z) * 0.69314718055994531f;
+
+  // 3. write
+  float* dst = p.O + (static_cast<size_t>(h) * p.N + q * p.S + i0) * D;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int c = tid + j * kThreads;
+    if (c < valid) *reinterpret_cast<f32x4*>(dst + 4 * c) = acc[j];
+  }
 }
 
 template <int D, int PMAX>
 hipError_t launch(const MergeParams& p, hipStream_t stream) {
-  const int64_t total = static_cast<int64_t>(p.H) * p.N * (D / 4);
-  const int64_t blocks = (total + kThreads - 1) / kThreads;
+  constexpr int R = kThreads / PMAX;
+  const int row_tiles = (p.S + R - 1) / R;
+  const int64_t blocks = static_cast<int64_t>(p.H) * p.P * row_tiles;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((merge_kernel<D, PMAX>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((merge_kernel<D, PMAX>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, p,
+                     row_tiles);
   return hipGetLastError();
 }
 

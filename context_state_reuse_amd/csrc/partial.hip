@@ -24,9 +24,11 @@
 // 256), which keeps every probability <= 256 and skips most rescales of the
 // accumulator; the final division by the row sum makes the result exact.
 //
-// Block = 4 waves; each wave owns 32*NQT query rows.  K/V tiles of 64 keys
-// are double-buffered in LDS: the next tile's global loads are in flight
-// while the current tile is multiplied.  The grid is the compacted list of
+// Block = 4 or 8 waves of 32 query rows each (128 or 256 rows), two waves
+// per SIMD (<= 256 VGPRs each, no accumulator spills to AGPRs), so one wave's
+// MFMAs overlap the other's softmax.  K/V tiles of 64 keys are
+// double-buffered in LDS: the next tile's global loads are in flight while
+// the current tile is multiplied.  The grid is the compacted list of
 // fresh (head, pair, query tile) items: no block exists for a reused pair.
 
 #include <hip/hip_runtime.h>
@@ -44,8 +46,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kBc = 64;             // keys per K/V tile
 constexpr float kRescaleSlack = 8.0f;  // base-2 headroom before the running max moves
 
@@ -62,7 +62,6 @@ struct Geometry {
   // of 8 or 24 (mod 32) dwords puts the four rows on disjoint banks.
   static constexpr int KS = DK + 8;
   static constexpr int VS = DV + 16;
-  static constexpr int loads = (kBc * chunks + kThreads - 1) / kThreads;
 };
 
 typedef __attribute__((address_space(3))) bf16x4_v lds_bf16x4;
@@ -78,10 +77,13 @@ __device__ inline bf16x8 read_v_operand(const __bf16* p0, const __bf16* p1) {
 
 __device__ inline float xor32(float x) { return __shfl_xor(x, 32); }
 
-template <int D, int NQT>
-__global__ __launch_bounds__(kThreads, 1) void partial_kernel(const PartialParams p) {
+template <int D, int WAVES>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES), amdgpu_waves_per_eu(2, 2)))
+void partial_kernel(const PartialParams p) {
   using G = Geometry<D>;
-  constexpr int BR = kWaves * 32 * NQT;
+  constexpr int kThreads = 64 * WAVES;
+  constexpr int BR = 32 * WAVES;                   // query rows per block
+  constexpr int kLoads = (kBc * G::chunks + kThreads - 1) / kThreads;
   __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][kBc * G::KS];
   __shared__ __attribute__((aligned(16))) __bf16 v_lds[2][kBc * G::VS];
 
@@ -113,20 +115,19 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(const PartialParam
   const __bf16* Kh = p.K + head + static_cast<size_t>(k0) * D;
   const __bf16* Vh = p.V + head + static_cast<size_t>(k0) * D;
   const float sl2 = p.scale_log2;
+  const int my_row = qt * BR + wave * 32 + l32;   // this lane's query row in the partition
 
   // Q^T operand: lane holds 8 consecutive dims of its query per k-step.
-  bf16x8 qf[NQT][G::kSteps];
-#pragma unroll
-  for (int c = 0; c < NQT; ++c) {
-    const int row = min(qt * BR + wave * 32 * NQT + c * 32 + l32, len_q - 1);
-    const __bf16* qrow = Qh + static_cast<size_t>(row) * D;
+  bf16x8 qf[G::kSteps];
+  {
+    const __bf16* qrow = Qh + static_cast<size_t>(min(my_row, len_q - 1)) * D;
 #pragma unroll
     for (int s = 0; s < G::kSteps; ++s) {
       const int dim = s * 16 + hw * 8;
       if (dim < D) {
-        qf[c][s] = *reinterpret_cast<const bf16x8*>(qrow + dim);
+        qf[s] = *reinterpret_cast<const bf16x8*>(qrow + dim);
       } else {
-        qf[c][s] = bf16x8{};
+        qf[s] = bf16x8{};
       }
     }
   }
@@ -138,11 +139,11 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(const PartialParam
   }
 
   const int n_tiles = (len_k + kBc - 1) / kBc;
-  u32x4 kreg[G::loads], vreg[G::loads];
+  u32x4 kreg[kLoads], vreg[kLoads];
 
   auto gload = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < G::loads; ++i) {
+    for (int i = 0; i < kLoads; ++i) {
       const int c = tid + i * kThreads;
       if (c < kBc * G::chunks) {
         const int key = c / G::chunks, ch = c % G::chunks;
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(const PartialParam
   };
   auto swrite = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < G::loads; ++i) {
+    for (int i = 0; i < kLoads; ++i) {
       const int c = tid + i * kThreads;
       if (c < kBc * G::chunks) {
         const int key = c / G::chunks, ch = c % G::chunks;
@@ -164,26 +165,19 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(const PartialParam
     }
   };
 
-  f32x16 oacc[G::vTiles][NQT];
+  f32x16 oacc[G::vTiles];
 #pragma unroll
-  for (int v = 0; v < G::vTiles; ++v)
-#pragma unroll
-    for (int c = 0; c < NQT; ++c) oacc[v][c] = f32x16{};
-  float m_run[NQT], l_run[NQT], lr_run[NQT];  // running max, exact sum, rounded sum
-#pragma unroll
-  for (int c = 0; c < NQT; ++c) {
-    m_run[c] = -__builtin_inff();
-    l_run[c] = 0.0f;
-    lr_run[c] = 0.0f;
-  }
+  for (int v = 0; v < G::vTiles; ++v) oacc[v] = f32x16{};
+  float m_run = -__builtin_inff();   // running max (base-2 units)
+  float l_run = 0.0f;                // exact sum of probabilities
+  float lr_run = 0.0f;               // sum of bf16-rounded probabilities
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // ds_read_b64_tr_b16 addressing for the V^T operand: in each 16-lane group
   // lane 4r+c supplies key row r, dims 4c..4c+3 of the group's 16 dims, and
   // receives dim (lane % 16) of the four rows.
   const int tr_r = (lane & 15) >> 2;
-  const int tr_c = lane & 3;
-  const int tr_dim = ((lane >> 4) & 1) * 16 + 4 * tr_c;
+  const int tr_dim = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
 
   gload(0);
   swrite(0);
@@ -197,17 +191,14 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(const PartialParam
     const __bf16* vl = v_lds[buf];
 
     // S^T = K Q^T for two 32-key blocks.
-    f32x16 sacc[2][NQT];
+    f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int c = 0; c < NQT; ++c) sacc[kb][c] = f32x16{};
+      sacc[kb] = f32x16{};
 #pragma unroll
       for (int s = 0; s < G::kSteps; ++s) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kl[(kb * 32 + l32) * G::KS + s * 16 + hw * 8]);
-#pragma unroll
-        for (int c = 0; c < NQT; ++c)
-          sacc[kb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c][s], sacc[kb][c], 0, 0, 0);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
       }
     }
 
@@ -217,64 +208,50 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(const PartialParam
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int c = 0; c < NQT; ++c)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kb * 32 + 8 * (i >> 2) + hw * 4 + (i & 3);
-            if (key >= lim) sacc[kb][c][i] = -__builtin_inff();
-          }
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb * 32 + 8 * (i >> 2) + hw * 4 + (i & 3);
+          if (key >= lim) sacc[kb][i] = -__builtin_inff();
+        }
     }
 
-    // Running max (raised lazily) and rescale of the accumulators.
-    float m_new[NQT];
-    bool need_any = false;
+    // Tile max (this lane's 32 keys, then the other half-wave's 32).
+    float mx = fmaxf(sacc[0][0], sacc[0][1]);
 #pragma unroll
-    for (int c = 0; c < NQT; ++c) {
-      float mx = sacc[0][c][0];
+    for (int i = 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[0][i], sacc[0][i + 1]));
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[1][i], sacc[1][i + 1]));
+    mx = fmaxf(mx, xor32(mx));
+    const float m_new = mx * sl2;
+    // Raise the running max only when the tile exceeds it by the slack.
+    const bool need = m_new > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+      m_run = need ? m_new : m_run;
+      l_run *= alpha;
+      lr_run *= alpha;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][c][i]);
-      mx = fmaxf(mx, xor32(mx));
-      m_new[c] = mx * sl2;
-      need_any |= m_new[c] > m_run[c] + kRescaleSlack;
-    }
-    if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
-#pragma unroll
-      for (int c = 0; c < NQT; ++c) {
-        const bool need = m_new[c] > m_run[c] + kRescaleSlack;
-        const float alpha = need ? __builtin_amdgcn_exp2f(m_run[c] - m_new[c]) : 1.0f;
-        if (need) m_run[c] = m_new[c];
-        l_run[c] *= alpha;
-        lr_run[c] *= alpha;
-#pragma unroll
-        for (int v = 0; v < G::vTiles; ++v) oacc[v][c] *= alpha;
-      }
+      for (int v = 0; v < G::vTiles; ++v) oacc[v] *= alpha;
     }
 
     // P = exp2(s * scale * log2e - m), rounded to bf16 for the product.
     // pb[u] is the B operand of key step u (16 keys).
-    bf16x8 pb[4][NQT];
+    bf16x8 pb[4];
 #pragma unroll
-    for (int c = 0; c < NQT; ++c) {
-      const float mc = m_run[c];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int half = 0; half < 2; ++half)
 #pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-          for (int j = 0; j < 8; j += 2) {
-            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][c][8 * half + j], sl2, -mc));
-            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][c][8 * half + j + 1], sl2, -mc));
-            bf16x2 pr;
-            pr[0] = (__bf16)e0;
-            pr[1] = (__bf16)e1;
-            pb[2 * kb + half][c][j] = pr[0];
-            pb[2 * kb + half][c][j + 1] = pr[1];
-            l_run[c] += e0 + e1;
-            lr_run[c] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lr_run[c], false);
-          }
-    }
+        for (int j = 0; j < 8; j += 2) {
+          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * half + j], sl2, -m_run));
+          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * half + j + 1], sl2, -m_run));
+          bf16x2 pr;
+          pr[0] = (__bf16)e0;
+          pr[1] = (__bf16)e1;
+          pb[2 * kb + half][j] = pr[0];
+          pb[2 * kb + half][j + 1] = pr[1];
+          l_run += e0 + e1;
+          lr_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lr_run, false);
+        }
 
     // O^T += V^T P^T.
 #pragma unroll
@@ -283,10 +260,7 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(const PartialParam
       for (int u = 0; u < 4; ++u) {
         const __bf16* p0 = &vl[(u * 16 + 4 * hw + tr_r) * G::VS + v * 32 + tr_dim];
         const __bf16* p1 = &vl[(u * 16 + 8 + 4 * hw + tr_r) * G::VS + v * 32 + tr_dim];
-        const bf16x8 a = read_v_operand(p0, p1);
-#pragma unroll
-        for (int c = 0; c < NQT; ++c)
-          oacc[v][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[u][c], oacc[v][c], 0, 0, 0);
+        oacc[v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_v_operand(p0, p1), pb[u], oacc[v], 0, 0, 0);
       }
     }
 
@@ -295,35 +269,29 @@ __global__ __launch_bounds__(kThreads, 1) void partial_kernel(const PartialParam
   }
 
   // Epilogue: OUT = O / l_rounded, LSE = ln2 * (m + log2 l), into the slot.
-  const size_t slot = static_cast<size_t>(h) * p.P * p.P + pair;
-  float* Os = p.O + slot * p.S * D;
-  float* Ls = p.LSE + slot * p.S;
+  const float l_tot = l_run + xor32(l_run);
+  const float inv = 1.0f / (lr_run + xor32(lr_run));
+  if (my_row < len_q) {
+    const size_t slot = static_cast<size_t>(h) * p.P * p.P + pair;
+    float* orow = p.O + (slot * p.S + my_row) * D;
 #pragma unroll
-  for (int c = 0; c < NQT; ++c) {
-    const float l_tot = l_run[c] + xor32(l_run[c]);
-    const float inv = 1.0f / (lr_run[c] + xor32(lr_run[c]));
-    const int row = qt * BR + wave * 32 * NQT + c * 32 + l32;
-    if (row < len_q) {
-      float* orow = Os + static_cast<size_t>(row) * D;
+    for (int v = 0; v < G::vTiles; ++v)
 #pragma unroll
-      for (int v = 0; v < G::vTiles; ++v)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int dim = v * 32 + 8 * g + 4 * hw;
-          if (dim < D) {
-            const f32x4 o = {oacc[v][c][4 * g] * inv, oacc[v][c][4 * g + 1] * inv,
-                             oacc[v][c][4 * g + 2] * inv, oacc[v][c][4 * g + 3] * inv};
-            *reinterpret_cast<f32x4*>(orow + dim) = o;
-          }
+      for (int g = 0; g < 4; ++g) {
+        const int dim = v * 32 + 8 * g + 4 * hw;
+        if (dim < D) {
+          const f32x4 o = {oacc[v][4 * g] * inv, oacc[v][4 * g + 1] * inv, oacc[v][4 * g + 2] * inv,
+                           oacc[v][4 * g + 3] * inv};
+          *reinterpret_cast<f32x4*>(orow + dim) = o;
         }
-      if (hw == 0) Ls[row] = (m_run[c] + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
-    }
+      }
+    if (hw == 0) p.LSE[slot * p.S + my_row] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
   }
 }
 
-template <int D, int NQT>
+template <int D, int WAVES>
 hipError_t launch(PartialParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((partial_kernel<D, NQT>), dim3(p.n_blocks), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((partial_kernel<D, WAVES>), dim3(p.n_blocks), dim3(64 * WAVES), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -341,9 +309,9 @@ int partial_rows_per_block(int d, int S) {
 hipError_t launch_partial(PartialParams& p, int rows, hipStream_t stream) {
   const bool wide = rows == 256;
   switch (p.d) {
-    case 64: return wide ? launch<64, 2>(p, stream) : launch<64, 1>(p, stream);
-    case 72: return wide ? launch<72, 2>(p, stream) : launch<72, 1>(p, stream);
-    case 128: return wide ? launch<128, 2>(p, stream) : launch<128, 1>(p, stream);
+    case 64: return wide ? launch<64, 8>(p, stream) : launch<64, 4>(p, stream);
+    case 72: return wide ? launch<72, 8>(p, stream) : launch<72, 4>(p, stream);
+    case 128: return wide ? launch<128, 8>(p, stream) : launch<128, 4>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
