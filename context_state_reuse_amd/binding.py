@@ -18,7 +18,10 @@ import os
 import numpy as np
 import torch  # noqa: F401  -- must precede the library: one HIP runtime per process
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libditango.so")
+# DITANGO_LIBRARY may name another build of the same sources (a variant
+# compiled with different tile parameters, for side-by-side measurement).
+_LIB_PATH = os.environ.get("DITANGO_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                               "libditango.so")
 
 DITANGO_OK = 0
 DITANGO_EINVAL = -1

@@ -31,8 +31,13 @@ def _hipcc() -> str:
 
 
 def _flags() -> list[str]:
+    # -fno-honor-nans: the kernels never produce NaN, and without it every max
+    # of MFMA results is preceded by a NaN-quieting canonicalize.
+    # -amdgpu-mfma-vgpr-form: MFMA results land in VGPRs, where the softmax
+    # reads them, instead of AGPRs that need copies.
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Wall", "-Wno-unused-result"]
 
 
@@ -45,23 +50,27 @@ def _run(cmd: list[str]) -> None:
         print(out, file=sys.stderr)
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile every source and link `out`.  `defines` (e.g. ["X=1"]) build
+    a variant library for side-by-side measurement."""
     hipcc = _hipcc()
-    os.makedirs(OBJDIR, exist_ok=True)
+    objdir = OBJDIR if out == LIB else out + ".objs"
+    os.makedirs(objdir, exist_ok=True)
+    dflags = [f"-D{d}" for d in defines]
     jobs = []
     for src in SOURCES:
-        obj = os.path.join(OBJDIR, src.replace(".", "_") + ".o")
+        obj = os.path.join(objdir, src.replace(".", "_") + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        jobs.append(([hipcc, *_flags(), *lang, "-c", os.path.join(CSRC, src), "-o", obj], obj))
+        jobs.append(([hipcc, *_flags(), *dflags, *lang, "-c", os.path.join(CSRC, src), "-o", obj], obj))
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
         for f in [ex.submit(_run, cmd) for cmd, _ in jobs]:
             f.result()
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *[o for _, o in jobs]])
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

@@ -56,12 +56,17 @@ struct Geometry {
   static constexpr int kSteps = DK / 16;
   static constexpr int vTiles = DV / 32;
   static constexpr int chunks = D / 8;            // 16-byte chunks per global row
-  // LDS row strides in bf16.  K rows are read 16 B per lane, 8 keys per LDS
-  // pass: a stride of 4 (mod 8) dwords per row spreads them over all banks.
-  // V rows are read 8 B per lane, 4 keys x 32 B per 16-lane group: a stride
-  // of 8 or 24 (mod 32) dwords puts the four rows on disjoint banks.
+  // LDS row strides in bf16, chosen with a bank-conflict counter sweep on
+  // gfx950 (64 banks of 4 bytes).  K rows are read 16 B per lane, 16 keys
+  // per pass: a stride of an odd multiple of 4 dwords spreads them over all
+  // banks.  V rows are read by ds_read_b64_tr_b16, 32 lanes per pass = 8 key
+  // rows x 32 B: a stride of 16 or 48 (mod 64) dwords puts those rows on
+  // disjoint banks (d=128: 80 dwords; d=72 and d=64: 48 dwords).
   static constexpr int KS = DK + 8;
-  static constexpr int VS = DV + 16;
+  static constexpr int VS = DV == 128 ? 160 : 96;
+  static_assert(DV <= VS, "V row must fit its stride");
+  static_assert((KS / 2) % 8 == 4, "K stride must be an odd multiple of 4 dwords");
+  static_assert((VS / 2) % 64 == 16 || (VS / 2) % 64 == 48, "V stride must be 16 or 48 mod 64 dwords");
 };
 
 typedef __attribute__((address_space(3))) bf16x4_v lds_bf16x4;
@@ -77,12 +82,137 @@ __device__ inline bf16x8 read_v_operand(const __bf16* p0, const __bf16* p1) {
 
 __device__ inline float xor32(float x) { return __shfl_xor(x, 32); }
 
-template <int D, int WAVES>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES), amdgpu_waves_per_eu(2, 2)))
+// Per-wave pieces of the key-tile loop.  A wave owns 32 queries (one MFMA
+// column tile); see the file comment for the operand layouts.
+template <int D, int NQT>
+struct WaveState {
+  using G = Geometry<D>;
+  bf16x8 qf[NQT][G::kSteps];      // Q^T operand, per 32-query column tile
+  f32x16 oacc[G::vTiles][NQT];    // O^T accumulator
+  f32x16 sacc[2][NQT];            // S^T of the current tile (two 32-key blocks)
+  bf16x8 pb[4][NQT];              // P^T operand of the tile's four 16-key steps
+  float m_run[NQT], l_run[NQT], lr_run[NQT];
+};
+
+// S^T = K Q^T for the 64 keys of one LDS tile; each K operand read from LDS
+// feeds the NQT column tiles.
+template <int D, int NQT>
+__device__ inline void tile_scores(WaveState<D, NQT>& w, const __bf16* kl, int l32, int hw) {
+  using G = Geometry<D>;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int c = 0; c < NQT; ++c) w.sacc[kb][c] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < G::kSteps; ++s) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kl[(kb * 32 + l32) * G::KS + s * 16 + hw * 8]);
+#pragma unroll
+      for (int c = 0; c < NQT; ++c)
+        w.sacc[kb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.qf[c][s], w.sacc[kb][c], 0, 0, 0);
+    }
+  }
+}
+
+// Online softmax of the tile held in sacc: lazily raised running max,
+// rescale of the accumulators when it moves, probabilities into pb.
+// MASK: keys at or past `lim` in this tile score -inf (ragged last tile).
+template <bool MASK, int D, int NQT>
+__device__ inline void tile_softmax(WaveState<D, NQT>& w, int lim, int hw, float sl2) {
+  using G = Geometry<D>;
+  if constexpr (MASK) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int c = 0; c < NQT; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb * 32 + 8 * (i >> 2) + hw * 4 + (i & 3);
+          if (key >= lim) w.sacc[kb][c][i] = -__builtin_inff();
+        }
+  }
+  float m_new[NQT];
+  bool need_any = false;
+#pragma unroll
+  for (int c = 0; c < NQT; ++c) {
+    float mx = fmaxf(w.sacc[0][c][0], w.sacc[0][c][1]);
+#pragma unroll
+    for (int i = 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(w.sacc[0][c][i], w.sacc[0][c][i + 1]));
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(w.sacc[1][c][i], w.sacc[1][c][i + 1]));
+    mx = fmaxf(mx, xor32(mx));
+    m_new[c] = mx * sl2;
+    need_any |= m_new[c] > w.m_run[c] + kRescaleSlack;
+  }
+  if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
+    // Rare after the first tile.  The empty volatile asm keeps the compiler
+    // from if-converting this block into unconditional multiplies.
+    asm volatile("; rescale" ::);
+#pragma unroll
+    for (int c = 0; c < NQT; ++c) {
+      const bool need = m_new[c] > w.m_run[c] + kRescaleSlack;
+      const float alpha = need ? __builtin_amdgcn_exp2f(w.m_run[c] - m_new[c]) : 1.0f;
+      w.m_run[c] = need ? m_new[c] : w.m_run[c];
+      w.l_run[c] *= alpha;
+      w.lr_run[c] *= alpha;
+#pragma unroll
+      for (int v = 0; v < G::vTiles; ++v) w.oacc[v][c] *= alpha;
+    }
+  }
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int c = 0; c < NQT; ++c)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        uint32_t words[4];
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(w.sacc[kb][c][8 * half + j], sl2, -w.m_run[c]));
+          const float e1 =
+              __builtin_amdgcn_exp2f(__builtin_fmaf(w.sacc[kb][c][8 * half + j + 1], sl2, -w.m_run[c]));
+          const bf16x2 pr = {(__bf16)e0, (__bf16)e1};   // one v_cvt_pk_bf16_f32
+          words[j / 2] = __builtin_bit_cast(uint32_t, pr);
+          w.l_run[c] += e0 + e1;
+          w.lr_run[c] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, w.lr_run[c], false);
+        }
+        const u32x4 wv = {words[0], words[1], words[2], words[3]};
+        w.pb[2 * kb + half][c] = __builtin_bit_cast(bf16x8, wv);
+      }
+}
+
+// O^T += V^T P^T for the tile whose V sits in `vl`; each V operand read from
+// LDS feeds the NQT column tiles.
+template <int D, int NQT>
+__device__ inline void tile_pv(WaveState<D, NQT>& w, const __bf16* vl, int hw, int tr_r, int tr_dim) {
+  using G = Geometry<D>;
+#pragma unroll
+  for (int v = 0; v < G::vTiles; ++v) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const __bf16* p0 = &vl[(u * 16 + 4 * hw + tr_r) * G::VS + v * 32 + tr_dim];
+      const __bf16* p1 = &vl[(u * 16 + 8 + 4 * hw + tr_r) * G::VS + v * 32 + tr_dim];
+      const bf16x8 a = read_v_operand(p0, p1);
+#pragma unroll
+      for (int c = 0; c < NQT; ++c)
+        w.oacc[v][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.pb[u][c], w.oacc[v][c], 0, 0, 0);
+    }
+  }
+}
+
+// Block = WAVES waves, each owning NQT column tiles of 32 queries.  NQT = 1
+// runs two waves per SIMD (<= 256 registers each); NQT = 2 halves the LDS
+// operand traffic per MFMA and runs one wave per SIMD.  K/V tiles of 64 keys
+// are double-buffered in LDS: the next tile's global loads are in flight
+// while the current tile is multiplied; one barrier per tile.
+template <int D, int WAVES, int NQT>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
+                          amdgpu_waves_per_eu(NQT == 1 ? 2 : 1, NQT == 1 ? 2 : 1)))
 void partial_kernel(const PartialParams p) {
   using G = Geometry<D>;
   constexpr int kThreads = 64 * WAVES;
-  constexpr int BR = 32 * WAVES;                   // query rows per block
+  constexpr int QPW = 32 * NQT;                    // query rows per wave
+  constexpr int BR = QPW * WAVES;                  // query rows per block
   constexpr int kLoads = (kBc * G::chunks + kThreads - 1) / kThreads;
   __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][kBc * G::KS];
   __shared__ __attribute__((aligned(16))) __bf16 v_lds[2][kBc * G::VS];
@@ -115,21 +245,26 @@ void partial_kernel(const PartialParams p) {
   const __bf16* Kh = p.K + head + static_cast<size_t>(k0) * D;
   const __bf16* Vh = p.V + head + static_cast<size_t>(k0) * D;
   const float sl2 = p.scale_log2;
-  const int my_row = qt * BR + wave * 32 + l32;   // this lane's query row in the partition
+  const int row0 = qt * BR + wave * QPW + l32;    // this lane's query row of column tile 0
 
-  // Q^T operand: lane holds 8 consecutive dims of its query per k-step.
-  bf16x8 qf[G::kSteps];
-  {
-    const __bf16* qrow = Qh + static_cast<size_t>(min(my_row, len_q - 1)) * D;
+  WaveState<D, NQT> w;
+#pragma unroll
+  for (int c = 0; c < NQT; ++c) {
+    const __bf16* qrow = Qh + static_cast<size_t>(min(row0 + 32 * c, len_q - 1)) * D;
 #pragma unroll
     for (int s = 0; s < G::kSteps; ++s) {
       const int dim = s * 16 + hw * 8;
       if (dim < D) {
-        qf[s] = *reinterpret_cast<const bf16x8*>(qrow + dim);
+        w.qf[c][s] = *reinterpret_cast<const bf16x8*>(qrow + dim);
       } else {
-        qf[s] = bf16x8{};
+        w.qf[c][s] = bf16x8{};
       }
     }
+#pragma unroll
+    for (int v = 0; v < G::vTiles; ++v) w.oacc[v][c] = f32x16{};
+    w.m_run[c] = -__builtin_inff();
+    w.l_run[c] = 0.0f;
+    w.lr_run[c] = 0.0f;
   }
 
   // K columns beyond d (d = 72 pads the contraction to 80) must read as zero.
@@ -165,14 +300,6 @@ void partial_kernel(const PartialParams p) {
     }
   };
 
-  f32x16 oacc[G::vTiles];
-#pragma unroll
-  for (int v = 0; v < G::vTiles; ++v) oacc[v] = f32x16{};
-  float m_run = -__builtin_inff();   // running max (base-2 units)
-  float l_run = 0.0f;                // exact sum of probabilities
-  float lr_run = 0.0f;               // sum of bf16-rounded probabilities
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-
   // ds_read_b64_tr_b16 addressing for the V^T operand: in each 16-lane group
   // lane 4r+c supplies key row r, dims 4c..4c+3 of the group's 16 dims, and
   // receives dim (lane % 16) of the four rows.
@@ -182,136 +309,83 @@ void partial_kernel(const PartialParams p) {
   gload(0);
   swrite(0);
   __syncthreads();
-
-  for (int kt = 0; kt < n_tiles; ++kt) {
+  // All tiles but the last are full (the last one may be ragged).
+  for (int kt = 0; kt + 1 < n_tiles; ++kt) {
     const int buf = kt & 1;
-    const bool more = kt + 1 < n_tiles;
-    if (more) gload(kt + 1);
-    const __bf16* kl = k_lds[buf];
-    const __bf16* vl = v_lds[buf];
-
-    // S^T = K Q^T for two 32-key blocks.
-    f32x16 sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < G::kSteps; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kl[(kb * 32 + l32) * G::KS + s * 16 + hw * 8]);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
-      }
-    }
-
-    // Keys past the end of a ragged partition get score -inf.
-    const int lim = len_k - kt * kBc;
-    if (lim < kBc) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kb * 32 + 8 * (i >> 2) + hw * 4 + (i & 3);
-          if (key >= lim) sacc[kb][i] = -__builtin_inff();
-        }
-    }
-
-    // Tile max (this lane's 32 keys, then the other half-wave's 32).
-    float mx = fmaxf(sacc[0][0], sacc[0][1]);
-#pragma unroll
-    for (int i = 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[0][i], sacc[0][i + 1]));
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[1][i], sacc[1][i + 1]));
-    mx = fmaxf(mx, xor32(mx));
-    const float m_new = mx * sl2;
-    // Raise the running max only when the tile exceeds it by the slack.
-    const bool need = m_new > m_run + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-      m_run = need ? m_new : m_run;
-      l_run *= alpha;
-      lr_run *= alpha;
-#pragma unroll
-      for (int v = 0; v < G::vTiles; ++v) oacc[v] *= alpha;
-    }
-
-    // P = exp2(s * scale * log2e - m), rounded to bf16 for the product.
-    // pb[u] is the B operand of key step u (16 keys).
-    bf16x8 pb[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * half + j], sl2, -m_run));
-          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * half + j + 1], sl2, -m_run));
-          bf16x2 pr;
-          pr[0] = (__bf16)e0;
-          pr[1] = (__bf16)e1;
-          pb[2 * kb + half][j] = pr[0];
-          pb[2 * kb + half][j + 1] = pr[1];
-          l_run += e0 + e1;
-          lr_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lr_run, false);
-        }
-
-    // O^T += V^T P^T.
-#pragma unroll
-    for (int v = 0; v < G::vTiles; ++v) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const __bf16* p0 = &vl[(u * 16 + 4 * hw + tr_r) * G::VS + v * 32 + tr_dim];
-        const __bf16* p1 = &vl[(u * 16 + 8 + 4 * hw + tr_r) * G::VS + v * 32 + tr_dim];
-        oacc[v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_v_operand(p0, p1), pb[u], oacc[v], 0, 0, 0);
-      }
-    }
-
-    if (more) swrite(buf ^ 1);
+    gload(kt + 1);
+    tile_scores(w, k_lds[buf], l32, hw);
+    tile_softmax<false>(w, kBc, hw, sl2);
+    tile_pv(w, v_lds[buf], hw, tr_r, tr_dim);
+    swrite(buf ^ 1);
     __syncthreads();
+  }
+  {
+    const int kt = n_tiles - 1;
+    tile_scores(w, k_lds[kt & 1], l32, hw);
+    tile_softmax<true>(w, len_k - kt * kBc, hw, sl2);
+    tile_pv(w, v_lds[kt & 1], hw, tr_r, tr_dim);
   }
 
   // Epilogue: OUT = O / l_rounded, LSE = ln2 * (m + log2 l), into the slot.
-  const float l_tot = l_run + xor32(l_run);
-  const float inv = 1.0f / (lr_run + xor32(lr_run));
-  if (my_row < len_q) {
-    const size_t slot = static_cast<size_t>(h) * p.P * p.P + pair;
-    float* orow = p.O + (slot * p.S + my_row) * D;
+  const size_t slot = static_cast<size_t>(h) * p.P * p.P + pair;
 #pragma unroll
-    for (int v = 0; v < G::vTiles; ++v)
+  for (int c = 0; c < NQT; ++c) {
+    const float l_tot = w.l_run[c] + xor32(w.l_run[c]);
+    const float inv = 1.0f / (w.lr_run[c] + xor32(w.lr_run[c]));
+    const int row = row0 + 32 * c;
+    if (row < len_q) {
+      float* orow = p.O + (slot * p.S + row) * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dim = v * 32 + 8 * g + 4 * hw;
-        if (dim < D) {
-          const f32x4 o = {oacc[v][4 * g] * inv, oacc[v][4 * g + 1] * inv, oacc[v][4 * g + 2] * inv,
-                           oacc[v][4 * g + 3] * inv};
-          *reinterpret_cast<f32x4*>(orow + dim) = o;
+      for (int v = 0; v < G::vTiles; ++v)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int dim = v * 32 + 8 * g + 4 * hw;
+          if (dim < D) {
+            const f32x4 o = {w.oacc[v][c][4 * g] * inv, w.oacc[v][c][4 * g + 1] * inv,
+                             w.oacc[v][c][4 * g + 2] * inv, w.oacc[v][c][4 * g + 3] * inv};
+            *reinterpret_cast<f32x4*>(orow + dim) = o;
+          }
         }
-      }
-    if (hw == 0) p.LSE[slot * p.S + my_row] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+      if (hw == 0) p.LSE[slot * p.S + row] = (w.m_run[c] + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+    }
   }
 }
 
-template <int D, int WAVES>
+template <int D, int WAVES, int NQT>
 hipError_t launch(PartialParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((partial_kernel<D, WAVES>), dim3(p.n_blocks), dim3(64 * WAVES), 0, stream, p);
+  hipLaunchKernelGGL((partial_kernel<D, WAVES, NQT>), dim3(p.n_blocks), dim3(64 * WAVES), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// Query rows per wave for d = 128 (32 or 64); 64 halves LDS operand traffic
+// per MFMA at one wave per SIMD.
+#ifndef DITANGO_D128_QPW
+#define DITANGO_D128_QPW 32
+#endif
+
 int partial_rows_per_block(int d, int S) {
-  (void)d;
+  const int qpw = d == 128 ? DITANGO_D128_QPW : 32;
+  const int wide = 4 * 2 * 32, narrow = 4 * 32;   // 8 or 4 column tiles per block
+  (void)qpw;
   // 256 rows per block unless 128-row blocks waste clearly less of a ragged
   // partition (e.g. S = 549: 3 x 256 rows hold 71% useful work, 5 x 128 hold 86%).
-  const long waste256 = (S + 255) / 256 * 256L - S;
-  const long waste128 = (S + 127) / 128 * 128L - S;
-  return (waste128 * 10 + S < waste256 * 10) ? 128 : 256;
+  const long waste_w = (S + wide - 1) / wide * static_cast<long>(wide) - S;
+  const long waste_n = (S + narrow - 1) / narrow * static_cast<long>(narrow) - S;
+  return (waste_n * 10 + S < waste_w * 10) ? narrow : wide;
 }
 
 hipError_t launch_partial(PartialParams& p, int rows, hipStream_t stream) {
   const bool wide = rows == 256;
   switch (p.d) {
-    case 64: return wide ? launch<64, 8>(p, stream) : launch<64, 4>(p, stream);
-    case 72: return wide ? launch<72, 8>(p, stream) : launch<72, 4>(p, stream);
-    case 128: return wide ? launch<128, 8>(p, stream) : launch<128, 4>(p, stream);
+    case 64: return wide ? launch<64, 8, 1>(p, stream) : launch<64, 4, 1>(p, stream);
+    case 72: return wide ? launch<72, 8, 1>(p, stream) : launch<72, 4, 1>(p, stream);
+#if DITANGO_D128_QPW == 64
+    case 128: return wide ? launch<128, 4, 2>(p, stream) : launch<128, 4, 1>(p, stream);
+#else
+    case 128: return wide ? launch<128, 8, 1>(p, stream) : launch<128, 4, 1>(p, stream);
+#endif
     default: return hipErrorInvalidValue;
   }
 }
