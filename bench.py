@@ -43,6 +43,9 @@ def parse():
                     help="image | video_100 | video_50 | video_25 | long | stress | tiny")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the oracle sample (0: auto)")
+    ap.add_argument("--cpu-steps", type=int, default=0, help="timed steady-state steps of the oracle (0: auto)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -90,8 +93,9 @@ def stored_traffic(kernel: str, workload: str, src_hash: str):
         return None
 
 
-def cpu_baseline(w, heads: int):
-    """fp64 oracle on one steady-state step of `heads` heads (anchor untimed)."""
+def cpu_baseline(w, heads: int, steps: int):
+    """fp64 oracle on `steps` steady-state steps of `heads` heads (the anchor
+    step 0 runs untimed first)."""
     from oracle.reuse import StateReuseOracle
     from oracle.masks import step_mask
     import synth
@@ -103,19 +107,24 @@ def cpu_baseline(w, heads: int):
     hs = list(range(heads))
     stream = synth.InputStream(w, hs)
     orc = StateReuseOracle(w.N, w.P, w.d)
-    t_step = None
-    for t in range(2):
-        qb, kb, vb = stream.next()
+    timed = 0.0
+    n = 0
+    for t in range(1 + steps):
+        tt = 1 + (t - 1) % max(w.steps - 1, 1) if t else 0
+        if t == 0 or tt > stream.t:
+            qb, kb, vb = stream.next()
         inp = {h: (synth.bf16_bits_to_f64(qb[i]), synth.bf16_bits_to_f64(kb[i]), synth.bf16_bits_to_f64(vb[i]))
                for i, h in enumerate(hs)}
         t0 = time.perf_counter()
-        orc.step(t, step_mask(w, t), inp)
-        t_step = time.perf_counter() - t0
+        orc.step(t, step_mask(w, tt), inp)
+        if t:
+            timed += time.perf_counter() - t0
+            n += 1
     dense = 4.0 * w.N * w.N * w.d * heads
-    return {"value": dense / t_step / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{w.name}: steady-state step t=1 (after an untimed anchor step) for {heads} of {w.H} "
-                      f"heads, all {w.N} rows; fp64 NumPy, {t_step:.2f} s; effective TFLOP/s counts "
-                      f"4*N^2*d per sampled head"}
+    return {"value": dense * n / timed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{w.name}: {n} steady-state steps (after an untimed anchor step) for {heads} of {w.H} "
+                      f"heads, all {w.N} rows; fp64 NumPy oracle, {timed:.1f} s timed; effective TFLOP/s "
+                      f"counts 4*N^2*d per sampled head and step"}
 
 
 def main():
@@ -164,6 +173,16 @@ def main():
             events[2].record()
         step_no[0] += 1
         return mask
+
+    if args.calibrate_copy:
+        # plain device copy of 1 GiB: 1 GiB read + 1 GiB written
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1.0)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
 
     steady = list(range(1, w.steps)) or [0]
     step(0)                                         # anchor: all fresh
@@ -234,8 +253,12 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        heads = args.cpu_heads or 1
-        out["cpu_baseline"] = cpu_baseline(w, heads)
+        # about 12 s of timed oracle work: the oracle sustains roughly 7e10
+        # fp64 FLOP/s on the fresh pairs of a step (measured on the image sample)
+        steps = args.cpu_steps or 3
+        per_head_step = fresh / w.H / 7e10
+        heads = args.cpu_heads or int(max(1, min(w.H, round(12.0 / (steps * per_head_step)))))
+        out["cpu_baseline"] = cpu_baseline(w, heads, steps)
     print(json.dumps(out), flush=True)
 
 

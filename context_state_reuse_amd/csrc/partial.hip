@@ -94,30 +94,31 @@ struct WaveState {
   float m_run[NQT], l_run[NQT], lr_run[NQT];
 };
 
-// S^T = K Q^T for the 64 keys of one LDS tile; each K operand read from LDS
-// feeds the NQT column tiles.
+// S^T = K Q^T for the 64 keys of one LDS tile into `sacc`; each K operand
+// read from LDS feeds the NQT column tiles.
 template <int D, int NQT>
-__device__ inline void tile_scores(WaveState<D, NQT>& w, const __bf16* kl, int l32, int hw) {
+__device__ inline void tile_scores(f32x16 (&sacc)[2][NQT], const WaveState<D, NQT>& w, const __bf16* kl, int l32,
+                                   int hw) {
   using G = Geometry<D>;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-    for (int c = 0; c < NQT; ++c) w.sacc[kb][c] = f32x16{};
+    for (int c = 0; c < NQT; ++c) sacc[kb][c] = f32x16{};
 #pragma unroll
     for (int s = 0; s < G::kSteps; ++s) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kl[(kb * 32 + l32) * G::KS + s * 16 + hw * 8]);
 #pragma unroll
       for (int c = 0; c < NQT; ++c)
-        w.sacc[kb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.qf[c][s], w.sacc[kb][c], 0, 0, 0);
+        sacc[kb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.qf[c][s], sacc[kb][c], 0, 0, 0);
     }
   }
 }
 
-// Online softmax of the tile held in sacc: lazily raised running max,
-// rescale of the accumulators when it moves, probabilities into pb.
+// Online softmax of the tile held in sacc, first half: tile max, lazily
+// raised running max, rescale of the accumulators when it moves.
 // MASK: keys at or past `lim` in this tile score -inf (ragged last tile).
 template <bool MASK, int D, int NQT>
-__device__ inline void tile_softmax(WaveState<D, NQT>& w, int lim, int hw, float sl2) {
+__device__ inline void tile_max(WaveState<D, NQT>& w, int lim, int hw, float sl2) {
   using G = Geometry<D>;
   if constexpr (MASK) {
 #pragma unroll
@@ -158,6 +159,12 @@ __device__ inline void tile_softmax(WaveState<D, NQT>& w, int lim, int hw, float
       for (int v = 0; v < G::vTiles; ++v) w.oacc[v][c] *= alpha;
     }
   }
+}
+
+// Second half: probabilities exp2(s * scale * log2e - m) into pb (rounded
+// to bf16 for the product) and the two row sums.
+template <int D, int NQT>
+__device__ inline void tile_exp(WaveState<D, NQT>& w, float sl2) {
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
   for (int c = 0; c < NQT; ++c)
@@ -179,6 +186,12 @@ __device__ inline void tile_softmax(WaveState<D, NQT>& w, int lim, int hw, float
         const u32x4 wv = {words[0], words[1], words[2], words[3]};
         w.pb[2 * kb + half][c] = __builtin_bit_cast(bf16x8, wv);
       }
+}
+
+template <bool MASK, int D, int NQT>
+__device__ inline void tile_softmax(WaveState<D, NQT>& w, int lim, int hw, float sl2) {
+  tile_max<MASK>(w, lim, hw, sl2);
+  tile_exp(w, sl2);
 }
 
 // O^T += V^T P^T for the tile whose V sits in `vl`; each V operand read from
@@ -205,7 +218,7 @@ __device__ inline void tile_pv(WaveState<D, NQT>& w, const __bf16* vl, int hw, i
 // operand traffic per MFMA and runs one wave per SIMD.  K/V tiles of 64 keys
 // are double-buffered in LDS: the next tile's global loads are in flight
 // while the current tile is multiplied; one barrier per tile.
-template <int D, int WAVES, int NQT>
+template <int D, int WAVES, int NQT, int SCHED>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
                           amdgpu_waves_per_eu(NQT == 1 ? 2 : 1, NQT == 1 ? 2 : 1)))
 void partial_kernel(const PartialParams p) {
@@ -276,26 +289,33 @@ void partial_kernel(const PartialParams p) {
   const int n_tiles = (len_k + kBc - 1) / kBc;
   u32x4 kreg[kLoads], vreg[kLoads];
 
-  auto gload = [&](int kt) {
+  // Global -> register staging of one K tile and one V tile (tile index -1:
+  // skip), and register -> LDS stores into the given buffers (-1: skip).
+  auto gload = [&](int kt_k, int kt_v) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int c = tid + i * kThreads;
       if (c < kBc * G::chunks) {
         const int key = c / G::chunks, ch = c % G::chunks;
-        const int krow = min(kt * kBc + key, len_k - 1);
-        kreg[i] = *reinterpret_cast<const u32x4*>(Kh + static_cast<size_t>(krow) * D + ch * 8);
-        vreg[i] = *reinterpret_cast<const u32x4*>(Vh + static_cast<size_t>(krow) * D + ch * 8);
+        if (kt_k >= 0) {
+          const int krow = min(kt_k * kBc + key, len_k - 1);
+          kreg[i] = *reinterpret_cast<const u32x4*>(Kh + static_cast<size_t>(krow) * D + ch * 8);
+        }
+        if (kt_v >= 0) {
+          const int vrow = min(kt_v * kBc + key, len_k - 1);
+          vreg[i] = *reinterpret_cast<const u32x4*>(Vh + static_cast<size_t>(vrow) * D + ch * 8);
+        }
       }
     }
   };
-  auto swrite = [&](int buf) {
+  auto swrite = [&](int kbuf, int vbuf) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int c = tid + i * kThreads;
       if (c < kBc * G::chunks) {
         const int key = c / G::chunks, ch = c % G::chunks;
-        *reinterpret_cast<u32x4*>(&k_lds[buf][key * G::KS + ch * 8]) = kreg[i];
-        *reinterpret_cast<u32x4*>(&v_lds[buf][key * G::VS + ch * 8]) = vreg[i];
+        if (kbuf >= 0) *reinterpret_cast<u32x4*>(&k_lds[kbuf][key * G::KS + ch * 8]) = kreg[i];
+        if (vbuf >= 0) *reinterpret_cast<u32x4*>(&v_lds[vbuf][key * G::VS + ch * 8]) = vreg[i];
       }
     }
   };
@@ -305,25 +325,89 @@ void partial_kernel(const PartialParams p) {
   // receives dim (lane % 16) of the four rows.
   const int tr_r = (lane & 15) >> 2;
   const int tr_dim = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+  auto softmax = [&](int kt) {
+    if (kt + 1 < n_tiles) {
+      tile_softmax<false>(w, kBc, hw, sl2);
+    } else {
+      tile_softmax<true>(w, len_k - kt * kBc, hw, sl2);
+    }
+  };
 
-  gload(0);
-  swrite(0);
-  __syncthreads();
-  // All tiles but the last are full (the last one may be ragged).
-  for (int kt = 0; kt + 1 < n_tiles; ++kt) {
-    const int buf = kt & 1;
-    gload(kt + 1);
-    tile_scores(w, k_lds[buf], l32, hw);
-    tile_softmax<false>(w, kBc, hw, sl2);
-    tile_pv(w, v_lds[buf], hw, tr_r, tr_dim);
-    swrite(buf ^ 1);
+  if constexpr (SCHED == 0) {
+    // Plain: per tile, scores -> softmax -> PV, one barrier.
+    gload(0, 0);
+    swrite(0, 0);
     __syncthreads();
-  }
-  {
+    for (int kt = 0; kt + 1 < n_tiles; ++kt) {
+      const int buf = kt & 1;
+      gload(kt + 1, kt + 1);
+      tile_scores(w.sacc, w, k_lds[buf], l32, hw);
+      tile_softmax<false>(w, kBc, hw, sl2);
+      tile_pv(w, v_lds[buf], hw, tr_r, tr_dim);
+      swrite(buf ^ 1, buf ^ 1);
+      __syncthreads();
+    }
     const int kt = n_tiles - 1;
-    tile_scores(w, k_lds[kt & 1], l32, hw);
+    tile_scores(w.sacc, w, k_lds[kt & 1], l32, hw);
     tile_softmax<true>(w, len_k - kt * kBc, hw, sl2);
     tile_pv(w, v_lds[kt & 1], hw, tr_r, tr_dim);
+  } else if constexpr (SCHED == 1) {
+    // Two groups of WAVES/2 waves offset by half a tile: phase ph runs, per
+    // group, either M(i) = {scores of tile i, PV of tile i-1} or X(i) =
+    // softmax of tile i; group 0 runs M(i) while group 1 runs X(i-1) and
+    // vice versa, a block barrier after every phase.  K runs one tile ahead
+    // of V: K(j+1), V(j) are fetched in phase 2j and stored in phase 2j+1.
+    const int group = wave / (WAVES / 2);
+    gload(0, -1);
+    swrite(0, -1);
+    __syncthreads();
+    const int last = 2 * n_tiles + 1;
+    for (int ph = 0; ph <= last; ++ph) {
+      const int j = ph >> 1;
+      if ((ph & 1) == 0) gload(j + 1 < n_tiles ? j + 1 : -1, j < n_tiles ? j : -1);
+      const int t = ph - group;
+      if (t >= 0 && t <= 2 * n_tiles) {
+        const int i = t >> 1;
+        if ((t & 1) == 0) {
+          if (i < n_tiles) tile_scores(w.sacc, w, k_lds[i & 1], l32, hw);
+          if (i >= 1) tile_pv(w, v_lds[(i - 1) & 1], hw, tr_r, tr_dim);
+        } else {
+          softmax(i);
+        }
+      }
+      if (ph & 1) swrite(j + 1 < n_tiles ? (j + 1) & 1 : -1, j < n_tiles ? j & 1 : -1);
+      __syncthreads();
+    }
+  } else {
+    // Software pipeline inside each wave: iteration j runs the softmax of
+    // tile j in the same instruction stream as the scores of tile j+1 (MFMA),
+    // then the PV product of tile j.  K runs one tile ahead of V: iteration
+    // j reads K(j+1) and V(j) and stages K(j+2) and V(j+1).
+    f32x16 nx[2][NQT];      // scores of the next tile
+    gload(0, 0);
+    swrite(0, 0);
+    __syncthreads();
+    gload(1 < n_tiles ? 1 : -1, -1);
+    tile_scores(w.sacc, w, k_lds[0], l32, hw);
+    swrite(1 < n_tiles ? 1 : -1, -1);
+    __syncthreads();
+    for (int j = 0; j + 1 < n_tiles; ++j) {
+      gload(j + 2 < n_tiles ? j + 2 : -1, j + 1);
+      tile_max<false>(w, kBc, hw, sl2);
+      tile_scores(nx, w, k_lds[(j + 1) & 1], l32, hw);
+      tile_exp(w, sl2);
+      tile_pv(w, v_lds[j & 1], hw, tr_r, tr_dim);
+      swrite(j + 2 < n_tiles ? j & 1 : -1, (j + 1) & 1);
+      __syncthreads();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int c = 0; c < NQT; ++c) w.sacc[kb][c] = nx[kb][c];
+    }
+    const int j = n_tiles - 1;
+    tile_max<true>(w, len_k - j * kBc, hw, sl2);
+    tile_exp(w, sl2);
+    tile_pv(w, v_lds[j & 1], hw, tr_r, tr_dim);
   }
 
   // Epilogue: OUT = O / l_rounded, LSE = ln2 * (m + log2 l), into the slot.
@@ -351,9 +435,19 @@ void partial_kernel(const PartialParams p) {
   }
 }
 
+// Loop schedule per head dim, from side-by-side measurement on MI355X: the
+// in-wave pipeline (2) wins at d = 64 and 72, the plain loop (0) at d = 128
+// (where the pipeline's second score buffer leaves fewer registers for LDS
+// prefetch).  The two-group ping-pong (1) measured slower everywhere.
+#ifndef DITANGO_SCHED
+#define DITANGO_SCHED -1
+#endif
+
 template <int D, int WAVES, int NQT>
 hipError_t launch(PartialParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((partial_kernel<D, WAVES, NQT>), dim3(p.n_blocks), dim3(64 * WAVES), 0, stream, p);
+  constexpr int chosen = DITANGO_SCHED >= 0 ? DITANGO_SCHED : (D == 128 ? 0 : 2);
+  constexpr int sched = (chosen == 1 && WAVES != 8) ? 0 : chosen;
+  hipLaunchKernelGGL((partial_kernel<D, WAVES, NQT, sched>), dim3(p.n_blocks), dim3(64 * WAVES), 0, stream, p);
   return hipGetLastError();
 }
 
