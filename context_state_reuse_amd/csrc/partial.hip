@@ -33,6 +33,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace ditango {
@@ -56,17 +58,30 @@ struct Geometry {
   static constexpr int kSteps = DK / 16;
   static constexpr int vTiles = DV / 32;
   static constexpr int chunks = D / 8;            // 16-byte chunks per global row
-  // LDS row strides in bf16, chosen with a bank-conflict counter sweep on
-  // gfx950 (64 banks of 4 bytes).  K rows are read 16 B per lane, 16 keys
-  // per pass: a stride of an odd multiple of 4 dwords spreads them over all
-  // banks.  V rows are read by ds_read_b64_tr_b16, 32 lanes per pass = 8 key
-  // rows x 32 B: a stride of 16 or 48 (mod 64) dwords puts those rows on
-  // disjoint banks (d=128: 80 dwords; d=72 and d=64: 48 dwords).
-  static constexpr int KS = DK + 8;
-  static constexpr int VS = DV == 128 ? 160 : 96;
+  // Staged layout (d = 72): rows padded, strides chosen with a bank-conflict
+  // counter sweep on gfx950 (64 banks of 4 bytes).  K rows are read 16 B per
+  // lane, 16 keys per pass: a stride of an odd multiple of 4 dwords spreads
+  // them over all banks.  V rows are read by ds_read_b64_tr_b16, 32 lanes
+  // per pass = 4 key rows x 64 B: a stride of 16 or 48 (mod 64) dwords puts
+  // those rows on disjoint banks.
+  //
+  // Direct layout (d = 64, 128): rows unpadded, filled by
+  // global_load_lds_dwordx4 (a wave writes 64 consecutive 16-byte chunks,
+  // so rows cannot be padded); the 16-byte chunk c of row r sits at position
+  // c ^ f(r), and the global load of position p fetches chunk p ^ f(r).
+  //   K: f = r mod 16 (d=128) or (r/2) mod 8 (d=64): the 16 rows of a
+  //      16-lane pass land on distinct banks.
+  //   V: f = 4 (r mod 4) (d=128) or 4 ((r/2) mod 2) (d=64): the 4 rows x 4
+  //      chunks of a 32-lane transpose-read pass land on distinct banks.
+  static constexpr bool direct = D == 64 || D == 128;
+  static constexpr int cpr = D / 8;               // 16-byte chunks per row (direct layout)
+  static constexpr int KS = direct ? D : DK + 8;
+  static constexpr int VS = direct ? D : (DV == 128 ? 160 : 96);
   static_assert(DV <= VS, "V row must fit its stride");
-  static_assert((KS / 2) % 8 == 4, "K stride must be an odd multiple of 4 dwords");
-  static_assert((VS / 2) % 64 == 16 || (VS / 2) % 64 == 48, "V stride must be 16 or 48 mod 64 dwords");
+  static_assert(direct || (KS / 2) % 8 == 4, "K stride must be an odd multiple of 4 dwords");
+  static_assert(direct || (VS / 2) % 64 == 16 || (VS / 2) % 64 == 48, "V stride must be 16 or 48 mod 64 dwords");
+  __device__ static int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  __device__ static int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
 typedef __attribute__((address_space(3))) bf16x4_v lds_bf16x4;
@@ -82,6 +97,29 @@ __device__ inline bf16x8 read_v_operand(const __bf16* p0, const __bf16* p1) {
 
 __device__ inline float xor32(float x) { return __shfl_xor(x, 32); }
 
+// Element offset of 16-byte chunk `c` of K row `r` in an LDS tile.  The K
+// swizzle depends on r mod 16, so rows 32 apart share it.
+template <int D>
+__device__ inline int k_operand_offset(int r, int c) {
+  using G = Geometry<D>;
+  if constexpr (G::direct) {
+    return r * G::KS + ((c ^ G::kswz(r)) << 3);
+  } else {
+    return r * G::KS + c * 8;
+  }
+}
+
+// Element offset of the 4 bf16 at dims [dim, dim+4) of V row `r` (dim % 4 == 0).
+template <int D>
+__device__ inline int v_operand_offset(int r, int dim) {
+  using G = Geometry<D>;
+  if constexpr (G::direct) {
+    return r * G::VS + (((dim >> 3) ^ G::vswz(r)) << 3) + (dim & 7);
+  } else {
+    return r * G::VS + dim;
+  }
+}
+
 // Per-wave pieces of the key-tile loop.  A wave owns 32 queries (one MFMA
 // column tile); see the file comment for the operand layouts.
 template <int D, int NQT>
@@ -94,11 +132,28 @@ struct WaveState {
   float m_run[NQT], l_run[NQT], lr_run[NQT];
 };
 
+// Per-lane LDS element offsets of the MFMA operands, fixed for the whole
+// kernel: koff[s] = K operand of k-step s (32-key block 0; block 1 is +32
+// rows), voff[v] = first transpose read of 32-dim tile v (key step u adds
+// 16 rows, the second read of a step 8 rows).
+template <int D>
+struct OperandOffsets {
+  using G = Geometry<D>;
+  int koff[G::kSteps];
+  int voff[G::vTiles];
+  __device__ OperandOffsets(int l32, int hw, int tr_r, int tr_dim) {
+#pragma unroll
+    for (int s = 0; s < G::kSteps; ++s) koff[s] = k_operand_offset<D>(l32, 2 * s + hw);
+#pragma unroll
+    for (int v = 0; v < G::vTiles; ++v) voff[v] = v_operand_offset<D>(4 * hw + tr_r, v * 32 + tr_dim);
+  }
+};
+
 // S^T = K Q^T for the 64 keys of one LDS tile into `sacc`; each K operand
 // read from LDS feeds the NQT column tiles.
 template <int D, int NQT>
-__device__ inline void tile_scores(f32x16 (&sacc)[2][NQT], const WaveState<D, NQT>& w, const __bf16* kl, int l32,
-                                   int hw) {
+__device__ inline void tile_scores(f32x16 (&sacc)[2][NQT], const WaveState<D, NQT>& w, const __bf16* kl,
+                                   const OperandOffsets<D>& off) {
   using G = Geometry<D>;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -106,7 +161,7 @@ __device__ inline void tile_scores(f32x16 (&sacc)[2][NQT], const WaveState<D, NQ
     for (int c = 0; c < NQT; ++c) sacc[kb][c] = f32x16{};
 #pragma unroll
     for (int s = 0; s < G::kSteps; ++s) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kl[(kb * 32 + l32) * G::KS + s * 16 + hw * 8]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kl[kb * 32 * G::KS + off.koff[s]]);
 #pragma unroll
       for (int c = 0; c < NQT; ++c)
         sacc[kb][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.qf[c][s], sacc[kb][c], 0, 0, 0);
@@ -195,16 +250,18 @@ __device__ inline void tile_softmax(WaveState<D, NQT>& w, int lim, int hw, float
 }
 
 // O^T += V^T P^T for the tile whose V sits in `vl`; each V operand read from
-// LDS feeds the NQT column tiles.
+// LDS feeds the NQT column tiles.  Rows u*16 (+8) added to the base offsets
+// keep the swizzle: it depends on the row only modulo 4 (d=128) or through
+// (row/2) mod 2 (d=64), which adding a multiple of 8 rows leaves unchanged.
 template <int D, int NQT>
-__device__ inline void tile_pv(WaveState<D, NQT>& w, const __bf16* vl, int hw, int tr_r, int tr_dim) {
+__device__ inline void tile_pv(WaveState<D, NQT>& w, const __bf16* vl, const OperandOffsets<D>& off) {
   using G = Geometry<D>;
 #pragma unroll
   for (int v = 0; v < G::vTiles; ++v) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const __bf16* p0 = &vl[(u * 16 + 4 * hw + tr_r) * G::VS + v * 32 + tr_dim];
-      const __bf16* p1 = &vl[(u * 16 + 8 + 4 * hw + tr_r) * G::VS + v * 32 + tr_dim];
+      const __bf16* p0 = &vl[u * 16 * G::VS + off.voff[v]];
+      const __bf16* p1 = &vl[(u * 16 + 8) * G::VS + off.voff[v]];
       const bf16x8 a = read_v_operand(p0, p1);
 #pragma unroll
       for (int c = 0; c < NQT; ++c)
@@ -227,8 +284,15 @@ void partial_kernel(const PartialParams p) {
   constexpr int QPW = 32 * NQT;                    // query rows per wave
   constexpr int BR = QPW * WAVES;                  // query rows per block
   constexpr int kLoads = (kBc * G::chunks + kThreads - 1) / kThreads;
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][kBc * G::KS];
-  __shared__ __attribute__((aligned(16))) __bf16 v_lds[2][kBc * G::VS];
+  // Four separate LDS buffers (not one array indexed at run time): distinct
+  // variables get distinct alias scopes, so the compiler can see that reads
+  // of one buffer never alias the direct loads filling the other and does not
+  // make them wait for the prefetch.  The tile loop is unrolled by two so the
+  // buffer of every access is a compile-time choice.
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds0[kBc * G::KS];
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds1[kBc * G::KS];
+  __shared__ __attribute__((aligned(16))) __bf16 v_lds0[kBc * G::VS];
+  __shared__ __attribute__((aligned(16))) __bf16 v_lds1[kBc * G::VS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -283,48 +347,115 @@ void partial_kernel(const PartialParams p) {
   // K columns beyond d (d = 72 pads the contraction to 80) must read as zero.
   if constexpr (G::DK > D) {
     for (int i = tid; i < 2 * kBc; i += kThreads)
-      *reinterpret_cast<u32x4*>(&k_lds[i / kBc][(i % kBc) * G::KS + D]) = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(&(i < kBc ? k_lds0 : k_lds1)[(i % kBc) * G::KS + D]) = u32x4{0u, 0u, 0u, 0u};
   }
 
   const int n_tiles = (len_k + kBc - 1) / kBc;
-  u32x4 kreg[kLoads], vreg[kLoads];
+  u32x4 kreg[G::direct ? 1 : kLoads], vreg[G::direct ? 1 : kLoads];
 
-  // Global -> register staging of one K tile and one V tile (tile index -1:
-  // skip), and register -> LDS stores into the given buffers (-1: skip).
+  // Tile transfers.  gload(kt_k, kt_v) starts fetching K tile kt_k and V
+  // tile kt_v (-1: none); swrite(kbuf, vbuf) completes them into those LDS
+  // buffers.  Direct layout: gload itself streams global memory into the
+  // buffers (global_load_lds_dwordx4) and swrite only waits for it; the
+  // buffers passed to swrite must be the ones given to the matching gload.
+  // Staged layout: gload fills registers and swrite stores them.
+
+  // Direct-load geometry: round i of a tile covers chunk positions
+  // [(i*WAVES + wave)*64, +64); per-lane element offsets of the global
+  // source (swizzled) are fixed for the kernel.
+  constexpr int kRounds = G::direct ? kBc * G::cpr / kThreads : 1;
+  static_assert(!G::direct || kBc * G::cpr % kThreads == 0, "tile must split evenly over the block");
+  const int swave = __builtin_amdgcn_readfirstlane(wave);
+  int krow_of[kRounds], kgoff[kRounds], vgoff[kRounds];
+#pragma unroll
+  for (int i = 0; i < kRounds; ++i) {
+    const int idx = (i * WAVES + wave) * 64 + lane;
+    const int r = G::direct ? idx / G::cpr : 0, pos = G::direct ? idx % G::cpr : 0;
+    krow_of[i] = r;
+    kgoff[i] = r * D + ((pos ^ G::kswz(r)) << 3);
+    vgoff[i] = r * D + ((pos ^ G::vswz(r)) << 3);
+  }
+  auto gload_direct = [&](int kt_k, __bf16* kdst, int kt_v, __bf16* vdst) {
+#pragma unroll
+    for (int i = 0; i < (G::direct ? kRounds : 0); ++i) {
+      const int lds_elem0 = (i * WAVES + swave) * 64 * 8;   // first element this wave writes
+      if (kt_k >= 0) {
+        const __bf16* src = Kh + static_cast<size_t>(kt_k) * kBc * D + kgoff[i];
+        if (kt_k * kBc + kBc > len_k && kt_k * kBc + krow_of[i] >= len_k)   // past a ragged end: repeat the last row
+          src = Kh + static_cast<size_t>(len_k - 1 - krow_of[i]) * D + kgoff[i];
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                         (__attribute__((address_space(3))) void*)(kdst + lds_elem0), 16, 0, 0);
+      }
+      if (kt_v >= 0) {
+        const __bf16* src = Vh + static_cast<size_t>(kt_v) * kBc * D + vgoff[i];
+        if (kt_v * kBc + kBc > len_k && kt_v * kBc + krow_of[i] >= len_k)
+          src = Vh + static_cast<size_t>(len_k - 1 - krow_of[i]) * D + vgoff[i];
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                         (__attribute__((address_space(3))) void*)(vdst + lds_elem0), 16, 0, 0);
+      }
+    }
+  };
   auto gload = [&](int kt_k, int kt_v) {
+    if constexpr (G::direct) {
+      (void)kt_k;
+      (void)kt_v;
+    } else {
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int c = tid + i * kThreads;
-      if (c < kBc * G::chunks) {
-        const int key = c / G::chunks, ch = c % G::chunks;
-        if (kt_k >= 0) {
-          const int krow = min(kt_k * kBc + key, len_k - 1);
-          kreg[i] = *reinterpret_cast<const u32x4*>(Kh + static_cast<size_t>(krow) * D + ch * 8);
-        }
-        if (kt_v >= 0) {
-          const int vrow = min(kt_v * kBc + key, len_k - 1);
-          vreg[i] = *reinterpret_cast<const u32x4*>(Vh + static_cast<size_t>(vrow) * D + ch * 8);
+      for (int i = 0; i < kLoads; ++i) {
+        const int c = tid + i * kThreads;
+        if (c < kBc * G::chunks) {
+          const int key = c / G::chunks, ch = c % G::chunks;
+          if (kt_k >= 0) {
+            const int krow = min(kt_k * kBc + key, len_k - 1);
+            kreg[i] = *reinterpret_cast<const u32x4*>(Kh + static_cast<size_t>(krow) * D + ch * 8);
+          }
+          if (kt_v >= 0) {
+            const int vrow = min(kt_v * kBc + key, len_k - 1);
+            vreg[i] = *reinterpret_cast<const u32x4*>(Vh + static_cast<size_t>(vrow) * D + ch * 8);
+          }
         }
       }
     }
   };
-  auto swrite = [&](int kbuf, int vbuf) {
+  auto swrite = [&](__bf16* kdst, __bf16* vdst) {
+    if constexpr (G::direct) {
+      (void)kdst;
+      (void)vdst;
+      __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have landed
+    } else {
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int c = tid + i * kThreads;
-      if (c < kBc * G::chunks) {
-        const int key = c / G::chunks, ch = c % G::chunks;
-        if (kbuf >= 0) *reinterpret_cast<u32x4*>(&k_lds[kbuf][key * G::KS + ch * 8]) = kreg[i];
-        if (vbuf >= 0) *reinterpret_cast<u32x4*>(&v_lds[vbuf][key * G::VS + ch * 8]) = vreg[i];
+      for (int i = 0; i < kLoads; ++i) {
+        const int c = tid + i * kThreads;
+        if (c < kBc * G::chunks) {
+          const int key = c / G::chunks, ch = c % G::chunks;
+          if (kdst) *reinterpret_cast<u32x4*>(&kdst[key * G::KS + ch * 8]) = kreg[i];
+          if (vdst) *reinterpret_cast<u32x4*>(&vdst[key * G::VS + ch * 8]) = vreg[i];
+        }
       }
     }
   };
+  // Start fetching K tile kt_k into kdst and V tile kt_v into vdst (a tile
+  // index of -1 fetches nothing; its destination must then be nullptr).
+  __bf16* pend_k = nullptr;
+  __bf16* pend_v = nullptr;
+  auto fetch = [&](int kt_k, __bf16* kdst, int kt_v, __bf16* vdst) {
+    if constexpr (G::direct) {
+      gload_direct(kt_k, kdst, kt_v, vdst);
+    } else {
+      gload(kt_k, kt_v);
+    }
+    pend_k = kdst;
+    pend_v = vdst;
+  };
+  // Complete the transfers started by the last fetch.
+  auto land = [&]() { swrite(pend_k, pend_v); };
 
   // ds_read_b64_tr_b16 addressing for the V^T operand: in each 16-lane group
   // lane 4r+c supplies key row r, dims 4c..4c+3 of the group's 16 dims, and
   // receives dim (lane % 16) of the four rows.
   const int tr_r = (lane & 15) >> 2;
   const int tr_dim = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+  const OperandOffsets<D> off(l32, hw, tr_r, tr_dim);
   auto softmax = [&](int kt) {
     if (kt + 1 < n_tiles) {
       tile_softmax<false>(w, kBc, hw, sl2);
@@ -333,81 +464,90 @@ void partial_kernel(const PartialParams p) {
     }
   };
 
+  // Buffer pair B (0 or 1) as compile-time pointers.
+  auto kb_ = [&](auto B) -> __bf16* { if constexpr (decltype(B)::value == 0) return k_lds0; else return k_lds1; };
+  auto vb_ = [&](auto B) -> __bf16* { if constexpr (decltype(B)::value == 0) return v_lds0; else return v_lds1; };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+
   if constexpr (SCHED == 0) {
-    // Plain: per tile, scores -> softmax -> PV, one barrier.
-    gload(0, 0);
-    swrite(0, 0);
-    __syncthreads();
-    for (int kt = 0; kt + 1 < n_tiles; ++kt) {
-      const int buf = kt & 1;
-      gload(kt + 1, kt + 1);
-      tile_scores(w.sacc, w, k_lds[buf], l32, hw);
+    // Plain: per tile, scores -> softmax -> PV, one barrier.  Tile kt lives
+    // in buffer pair kt & 1; the next tile is fetched into the other pair.
+    auto full_tile = [&](auto B, int kt) {
+      constexpr int b = decltype(B)::value;
+      using NB = std::integral_constant<int, 1 - b>;
+      fetch(kt + 1, kb_(NB{}), kt + 1, vb_(NB{}));
+      tile_scores(w.sacc, w, kb_(B), off);
       tile_softmax<false>(w, kBc, hw, sl2);
-      tile_pv(w, v_lds[buf], hw, tr_r, tr_dim);
-      swrite(buf ^ 1, buf ^ 1);
+      tile_pv(w, vb_(B), off);
+      land();
       __syncthreads();
-    }
-    const int kt = n_tiles - 1;
-    tile_scores(w.sacc, w, k_lds[kt & 1], l32, hw);
-    tile_softmax<true>(w, len_k - kt * kBc, hw, sl2);
-    tile_pv(w, v_lds[kt & 1], hw, tr_r, tr_dim);
-  } else if constexpr (SCHED == 1) {
-    // Two groups of WAVES/2 waves offset by half a tile: phase ph runs, per
-    // group, either M(i) = {scores of tile i, PV of tile i-1} or X(i) =
-    // softmax of tile i; group 0 runs M(i) while group 1 runs X(i-1) and
-    // vice versa, a block barrier after every phase.  K runs one tile ahead
-    // of V: K(j+1), V(j) are fetched in phase 2j and stored in phase 2j+1.
-    const int group = wave / (WAVES / 2);
-    gload(0, -1);
-    swrite(0, -1);
+    };
+    auto last_tile = [&](auto B, int kt) {
+      tile_scores(w.sacc, w, kb_(B), off);
+      tile_softmax<true>(w, len_k - kt * kBc, hw, sl2);
+      tile_pv(w, vb_(B), off);
+    };
+    fetch(0, k_lds0, 0, v_lds0);
+    land();
     __syncthreads();
-    const int last = 2 * n_tiles + 1;
-    for (int ph = 0; ph <= last; ++ph) {
-      const int j = ph >> 1;
-      if ((ph & 1) == 0) gload(j + 1 < n_tiles ? j + 1 : -1, j < n_tiles ? j : -1);
-      const int t = ph - group;
-      if (t >= 0 && t <= 2 * n_tiles) {
-        const int i = t >> 1;
-        if ((t & 1) == 0) {
-          if (i < n_tiles) tile_scores(w.sacc, w, k_lds[i & 1], l32, hw);
-          if (i >= 1) tile_pv(w, v_lds[(i - 1) & 1], hw, tr_r, tr_dim);
-        } else {
-          softmax(i);
-        }
-      }
-      if (ph & 1) swrite(j + 1 < n_tiles ? (j + 1) & 1 : -1, j < n_tiles ? j & 1 : -1);
-      __syncthreads();
+    int kt = 0;
+    for (; kt + 2 < n_tiles; kt += 2) {
+      full_tile(B0{}, kt);
+      full_tile(B1{}, kt + 1);
+    }
+    if (kt + 1 < n_tiles) {
+      full_tile(B0{}, kt);
+      last_tile(B1{}, kt + 1);
+    } else {
+      last_tile(B0{}, kt);
     }
   } else {
     // Software pipeline inside each wave: iteration j runs the softmax of
     // tile j in the same instruction stream as the scores of tile j+1 (MFMA),
     // then the PV product of tile j.  K runs one tile ahead of V: iteration
-    // j reads K(j+1) and V(j) and stages K(j+2) and V(j+1).
+    // j reads K(j+1) from pair (j+1)&1 and V(j) from pair j&1, and fetches
+    // K(j+2) into pair j&1 and V(j+1) into pair (j+1)&1.
     f32x16 nx[2][NQT];      // scores of the next tile
-    gload(0, 0);
-    swrite(0, 0);
-    __syncthreads();
-    gload(1 < n_tiles ? 1 : -1, -1);
-    tile_scores(w.sacc, w, k_lds[0], l32, hw);
-    swrite(1 < n_tiles ? 1 : -1, -1);
-    __syncthreads();
-    for (int j = 0; j + 1 < n_tiles; ++j) {
-      gload(j + 2 < n_tiles ? j + 2 : -1, j + 1);
+    auto iter = [&](auto B, int j) {   // B = j & 1
+      constexpr int b = decltype(B)::value;
+      using NB = std::integral_constant<int, 1 - b>;
+      const bool k2 = j + 2 < n_tiles;
+      fetch(k2 ? j + 2 : -1, k2 ? kb_(B) : nullptr, j + 1, vb_(NB{}));
       tile_max<false>(w, kBc, hw, sl2);
-      tile_scores(nx, w, k_lds[(j + 1) & 1], l32, hw);
+      tile_scores(nx, w, kb_(NB{}), off);
       tile_exp(w, sl2);
-      tile_pv(w, v_lds[j & 1], hw, tr_r, tr_dim);
-      swrite(j + 2 < n_tiles ? j & 1 : -1, (j + 1) & 1);
+      tile_pv(w, vb_(B), off);
+      land();
       __syncthreads();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int c = 0; c < NQT; ++c) w.sacc[kb][c] = nx[kb][c];
+    };
+    auto last = [&](auto B, int j) {
+      tile_max<true>(w, len_k - j * kBc, hw, sl2);
+      tile_exp(w, sl2);
+      tile_pv(w, vb_(B), off);
+    };
+    fetch(0, k_lds0, 0, v_lds0);
+    land();
+    __syncthreads();
+    fetch(1 < n_tiles ? 1 : -1, 1 < n_tiles ? k_lds1 : nullptr, -1, nullptr);
+    tile_scores(w.sacc, w, k_lds0, off);
+    land();
+    __syncthreads();
+    int j = 0;
+    for (; j + 2 < n_tiles; j += 2) {
+      iter(B0{}, j);
+      iter(B1{}, j + 1);
     }
-    const int j = n_tiles - 1;
-    tile_max<true>(w, len_k - j * kBc, hw, sl2);
-    tile_exp(w, sl2);
-    tile_pv(w, v_lds[j & 1], hw, tr_r, tr_dim);
+    if (j + 1 < n_tiles) {
+      iter(B0{}, j);
+      last(B1{}, j + 1);
+    } else {
+      last(B0{}, j);
+    }
   }
 
   // Epilogue: OUT = O / l_rounded, LSE = ln2 * (m + log2 l), into the slot.
@@ -438,15 +578,16 @@ void partial_kernel(const PartialParams p) {
 // Loop schedule per head dim, from side-by-side measurement on MI355X: the
 // in-wave pipeline (2) wins at d = 64 and 72, the plain loop (0) at d = 128
 // (where the pipeline's second score buffer leaves fewer registers for LDS
-// prefetch).  The two-group ping-pong (1) measured slower everywhere.
+// prefetch).  A two-group ping-pong (FA3-style, two barriers per tile) was
+// measured slower everywhere and is not kept.
 #ifndef DITANGO_SCHED
 #define DITANGO_SCHED -1
 #endif
 
 template <int D, int WAVES, int NQT>
 hipError_t launch(PartialParams& p, hipStream_t stream) {
-  constexpr int chosen = DITANGO_SCHED >= 0 ? DITANGO_SCHED : (D == 128 ? 0 : 2);
-  constexpr int sched = (chosen == 1 && WAVES != 8) ? 0 : chosen;
+  constexpr int sched = DITANGO_SCHED >= 0 ? DITANGO_SCHED : (D == 128 ? 0 : 2);
+  static_assert(sched == 0 || sched == 2, "loop schedules: 0 (plain) or 2 (software-pipelined)");
   hipLaunchKernelGGL((partial_kernel<D, WAVES, NQT, sched>), dim3(p.n_blocks), dim3(64 * WAVES), 0, stream, p);
   return hipGetLastError();
 }
