@@ -27,6 +27,25 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 
+#ifndef DITANGO_MERGE_NT
+#define DITANGO_MERGE_NT 1
+#endif
+
+// Streaming access: every slot byte is read once and every output written
+// once per step, so the non-temporal variants keep them from evicting
+// reusable lines (selected by measurement).
+__device__ inline f32x4 load_stream(const float* p) {
+  if constexpr (DITANGO_MERGE_NT) return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return *reinterpret_cast<const f32x4*>(p);
+}
+__device__ inline void store_stream(float* p, f32x4 v) {
+  if constexpr (DITANGO_MERGE_NT) {
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+  } else {
+    *reinterpret_cast<f32x4*>(p) = v;
+  }
+}
+
 template <int D, int PMAX>
 __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p, int row_tiles) {
   constexpr int R = kThreads / PMAX;                  // rows per block
@@ -76,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p, in
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         const int c = tid + j * kThreads;
-        if (c < valid) o[k][j] = *reinterpret_cast<const f32x4*>(src + 4 * c);
+        if (c < valid) o[k][j] = load_stream(src + 4 * c);
       }
     }
   }
@@ -96,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p, in
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int c = tid + j * kThreads;
-    if (c < valid) *reinterpret_cast<f32x4*>(dst + 4 * c) = acc[j];
+    if (c < valid) store_stream(dst + 4 * c, acc[j]);
   }
 }
 

@@ -51,10 +51,18 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kBc = 64;             // keys per K/V tile
 constexpr float kRescaleSlack = 8.0f;  // base-2 headroom before the running max moves
 
+#ifndef DITANGO_ONES_ROW
+#define DITANGO_ONES_ROW 1
+#endif
+
 template <int D>
 struct Geometry {
   static constexpr int DK = (D + 15) / 16 * 16;   // Q.K contraction, 16 per MFMA
   static constexpr int DV = (D + 31) / 32 * 32;   // rows of O^T, 32 per MFMA tile
+  // When O^T has spare rows (d = 72 pads to 96), V column d holds 1.0 in
+  // LDS, so O^T row d accumulates the sum of the rounded probabilities for
+  // free and the per-element v_dot2c is skipped.
+  static constexpr bool ones_row = DITANGO_ONES_ROW && DV > D;
   static constexpr int kSteps = DK / 16;
   static constexpr int vTiles = DV / 32;
   static constexpr int chunks = D / 8;            // 16-byte chunks per global row
@@ -236,7 +244,8 @@ __device__ inline void tile_exp(WaveState<D, NQT>& w, float sl2) {
           const bf16x2 pr = {(__bf16)e0, (__bf16)e1};   // one v_cvt_pk_bf16_f32
           words[j / 2] = __builtin_bit_cast(uint32_t, pr);
           w.l_run[c] += e0 + e1;
-          w.lr_run[c] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, w.lr_run[c], false);
+          if constexpr (!Geometry<D>::ones_row)
+            w.lr_run[c] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, w.lr_run[c], false);
         }
         const u32x4 wv = {words[0], words[1], words[2], words[3]};
         w.pb[2 * kb + half][c] = __builtin_bit_cast(bf16x8, wv);
@@ -275,9 +284,12 @@ __device__ inline void tile_pv(WaveState<D, NQT>& w, const __bf16* vl, const Ope
 // operand traffic per MFMA and runs one wave per SIMD.  K/V tiles of 64 keys
 // are double-buffered in LDS: the next tile's global loads are in flight
 // while the current tile is multiplied; one barrier per tile.
+template <int D, int NQT>
+constexpr int waves_per_simd() { return NQT == 2 ? 1 : 2; }
+
 template <int D, int WAVES, int NQT, int SCHED>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
-                          amdgpu_waves_per_eu(NQT == 1 ? 2 : 1, NQT == 1 ? 2 : 1)))
+                          amdgpu_waves_per_eu(waves_per_simd<D, NQT>(), waves_per_simd<D, NQT>())))
 void partial_kernel(const PartialParams p) {
   using G = Geometry<D>;
   constexpr int kThreads = 64 * WAVES;
@@ -348,6 +360,10 @@ void partial_kernel(const PartialParams p) {
   if constexpr (G::DK > D) {
     for (int i = tid; i < 2 * kBc; i += kThreads)
       *reinterpret_cast<u32x4*>(&(i < kBc ? k_lds0 : k_lds1)[(i % kBc) * G::KS + D]) = u32x4{0u, 0u, 0u, 0u};
+  }
+  if constexpr (G::ones_row) {
+    static_assert(!G::direct, "the ones column lives in the staged layout's spare columns");
+    for (int i = tid; i < 2 * kBc; i += kThreads) (i < kBc ? v_lds0 : v_lds1)[(i % kBc) * G::VS + D] = (__bf16)1.0f;
   }
 
   const int n_tiles = (len_k + kBc - 1) / kBc;
@@ -456,14 +472,6 @@ void partial_kernel(const PartialParams p) {
   const int tr_r = (lane & 15) >> 2;
   const int tr_dim = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
   const OperandOffsets<D> off(l32, hw, tr_r, tr_dim);
-  auto softmax = [&](int kt) {
-    if (kt + 1 < n_tiles) {
-      tile_softmax<false>(w, kBc, hw, sl2);
-    } else {
-      tile_softmax<true>(w, len_k - kt * kBc, hw, sl2);
-    }
-  };
-
   // Buffer pair B (0 or 1) as compile-time pointers.
   auto kb_ = [&](auto B) -> __bf16* { if constexpr (decltype(B)::value == 0) return k_lds0; else return k_lds1; };
   auto vb_ = [&](auto B) -> __bf16* { if constexpr (decltype(B)::value == 0) return v_lds0; else return v_lds1; };
@@ -555,7 +563,16 @@ void partial_kernel(const PartialParams p) {
 #pragma unroll
   for (int c = 0; c < NQT; ++c) {
     const float l_tot = w.l_run[c] + xor32(w.l_run[c]);
-    const float inv = 1.0f / (w.lr_run[c] + xor32(w.lr_run[c]));
+    float lr_tot;
+    if constexpr (G::ones_row) {
+      // O^T row D sits in tile D/32, element 4*((D%32)/8) of the lanes of
+      // half-wave 0 (D % 8 == 0); broadcast it to the query's other half.
+      static_assert(D % 8 == 0, "ones row must start a 4-row group of half-wave 0");
+      lr_tot = __shfl(w.oacc[D / 32][c][4 * ((D % 32) / 8)], l32);
+    } else {
+      lr_tot = w.lr_run[c] + xor32(w.lr_run[c]);
+    }
+    const float inv = 1.0f / lr_tot;
     const int row = row0 + 32 * c;
     if (row < len_q) {
       float* orow = p.O + (slot * p.S + row) * D;
