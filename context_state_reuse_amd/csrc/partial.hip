@@ -19,10 +19,11 @@
 // probabilities gives LSE, and the sum of the rounded ones (v_dot2c_f32_bf16)
 // normalises OUT, so the weights applied to V sum to one as used.
 //
-// Softmax runs in base 2 with the scale folded into one FMA.  The running
-// max is only raised when a tile's max exceeds it by more than 8 (a factor of
-// 256), which keeps every probability <= 256 and skips most rescales of the
-// accumulator; the final division by the row sum makes the result exact.
+// Softmax runs in base 2 with the scale folded into one FMA.  A tile's
+// probabilities are taken against the running max without first computing
+// the tile max; only when a lane's tile sum leaves [0, 2^64] (first tile,
+// or a score far above the running max) is the max recomputed and the state
+// rescaled.  The final division by the row sum makes the result exact.
 //
 // Block = 4 or 8 waves of 32 query rows each (128 or 256 rows), two waves
 // per SIMD (<= 256 VGPRs each, no accumulator spills to AGPRs), so one wave's
@@ -49,7 +50,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBc = 64;             // keys per K/V tile
-constexpr float kRescaleSlack = 8.0f;  // base-2 headroom before the running max moves
 
 #ifndef DITANGO_ONES_ROW
 #define DITANGO_ONES_ROW 1
@@ -94,7 +94,7 @@ struct Geometry {
 
 typedef __attribute__((address_space(3))) bf16x4_v lds_bf16x4;
 
-__device__ inline bf16x8 read_v_operand(const __bf16* p0, const __bf16* p1) {
+__device__ __attribute__((always_inline)) inline bf16x8 read_v_operand(const __bf16* p0, const __bf16* p1) {
   bf16x4_v a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0));
   bf16x4_v b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p1));
   u32x2 ua = __builtin_bit_cast(u32x2, a);
@@ -103,12 +103,12 @@ __device__ inline bf16x8 read_v_operand(const __bf16* p0, const __bf16* p1) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-__device__ inline float xor32(float x) { return __shfl_xor(x, 32); }
+__device__ __attribute__((always_inline)) inline float xor32(float x) { return __shfl_xor(x, 32); }
 
 // Element offset of 16-byte chunk `c` of K row `r` in an LDS tile.  The K
 // swizzle depends on r mod 16, so rows 32 apart share it.
 template <int D>
-__device__ inline int k_operand_offset(int r, int c) {
+__device__ __attribute__((always_inline)) inline int k_operand_offset(int r, int c) {
   using G = Geometry<D>;
   if constexpr (G::direct) {
     return r * G::KS + ((c ^ G::kswz(r)) << 3);
@@ -119,7 +119,7 @@ __device__ inline int k_operand_offset(int r, int c) {
 
 // Element offset of the 4 bf16 at dims [dim, dim+4) of V row `r` (dim % 4 == 0).
 template <int D>
-__device__ inline int v_operand_offset(int r, int dim) {
+__device__ __attribute__((always_inline)) inline int v_operand_offset(int r, int dim) {
   using G = Geometry<D>;
   if constexpr (G::direct) {
     return r * G::VS + (((dim >> 3) ^ G::vswz(r)) << 3) + (dim & 7);
@@ -160,7 +160,7 @@ struct OperandOffsets {
 // S^T = K Q^T for the 64 keys of one LDS tile into `sacc`; each K operand
 // read from LDS feeds the NQT column tiles.
 template <int D, int NQT>
-__device__ inline void tile_scores(f32x16 (&sacc)[2][NQT], const WaveState<D, NQT>& w, const __bf16* kl,
+__device__ __attribute__((always_inline)) inline void tile_scores(f32x16 (&sacc)[2][NQT], const WaveState<D, NQT>& w, const __bf16* kl,
                                    const OperandOffsets<D>& off) {
   using G = Geometry<D>;
 #pragma unroll
@@ -177,60 +177,24 @@ __device__ inline void tile_scores(f32x16 (&sacc)[2][NQT], const WaveState<D, NQ
   }
 }
 
-// Online softmax of the tile held in sacc, first half: tile max, lazily
-// raised running max, rescale of the accumulators when it moves.
+// Online softmax of the tile held in sacc, into the P operand pb and the row
+// sums.  Probabilities are exp2(s * scale * log2e - m) against the running
+// max m WITHOUT first taking the tile's max: the fp32 sums and bf16
+// probabilities stay exact in relative terms up to huge magnitudes, so m
+// only has to keep every probability below 2^64.  Each lane checks the sum
+// of its probabilities in the tile; if any lane's sum is not <= 2^64 (this
+// includes inf and NaN, e.g. on the first tile where m = -inf) the tile
+// takes the slow path: exact tile max, m raised to it, accumulated state
+// rescaled, probabilities recomputed.  After the first tile this is rare.
 // MASK: keys at or past `lim` in this tile score -inf (ragged last tile).
-template <bool MASK, int D, int NQT>
-__device__ inline void tile_max(WaveState<D, NQT>& w, int lim, int hw, float sl2) {
-  using G = Geometry<D>;
-  if constexpr (MASK) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int c = 0; c < NQT; ++c)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kb * 32 + 8 * (i >> 2) + hw * 4 + (i & 3);
-          if (key >= lim) w.sacc[kb][c][i] = -__builtin_inff();
-        }
-  }
-  float m_new[NQT];
-  bool need_any = false;
-#pragma unroll
-  for (int c = 0; c < NQT; ++c) {
-    float mx = fmaxf(w.sacc[0][c][0], w.sacc[0][c][1]);
-#pragma unroll
-    for (int i = 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(w.sacc[0][c][i], w.sacc[0][c][i + 1]));
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(w.sacc[1][c][i], w.sacc[1][c][i + 1]));
-    mx = fmaxf(mx, xor32(mx));
-    m_new[c] = mx * sl2;
-    need_any |= m_new[c] > w.m_run[c] + kRescaleSlack;
-  }
-  if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
-    // Rare after the first tile.  The empty volatile asm keeps the compiler
-    // from if-converting this block into unconditional multiplies.
-    asm volatile("; rescale" ::);
-#pragma unroll
-    for (int c = 0; c < NQT; ++c) {
-      const bool need = m_new[c] > w.m_run[c] + kRescaleSlack;
-      const float alpha = need ? __builtin_amdgcn_exp2f(w.m_run[c] - m_new[c]) : 1.0f;
-      w.m_run[c] = need ? m_new[c] : w.m_run[c];
-      w.l_run[c] *= alpha;
-      w.lr_run[c] *= alpha;
-#pragma unroll
-      for (int v = 0; v < G::vTiles; ++v) w.oacc[v][c] *= alpha;
-    }
-  }
-}
-
-// Second half: probabilities exp2(s * scale * log2e - m) into pb (rounded
-// to bf16 for the product) and the two row sums.
 template <int D, int NQT>
-__device__ inline void tile_exp(WaveState<D, NQT>& w, float sl2) {
+__device__ __attribute__((always_inline)) inline void tile_probs(WaveState<D, NQT>& w, float sl2, float (&tl)[NQT],
+                                                                 float (&tlr)[NQT]) {
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-  for (int c = 0; c < NQT; ++c)
+  for (int c = 0; c < NQT; ++c) {
+    tl[c] = 0.0f;
+    tlr[c] = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -243,19 +207,62 @@ __device__ inline void tile_exp(WaveState<D, NQT>& w, float sl2) {
               __builtin_amdgcn_exp2f(__builtin_fmaf(w.sacc[kb][c][8 * half + j + 1], sl2, -w.m_run[c]));
           const bf16x2 pr = {(__bf16)e0, (__bf16)e1};   // one v_cvt_pk_bf16_f32
           words[j / 2] = __builtin_bit_cast(uint32_t, pr);
-          w.l_run[c] += e0 + e1;
-          if constexpr (!Geometry<D>::ones_row)
-            w.lr_run[c] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, w.lr_run[c], false);
+          tl[c] += e0 + e1;
+          if constexpr (!Geometry<D>::ones_row) tlr[c] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, tlr[c], false);
         }
         const u32x4 wv = {words[0], words[1], words[2], words[3]};
         w.pb[2 * kb + half][c] = __builtin_bit_cast(bf16x8, wv);
       }
+  }
 }
 
 template <bool MASK, int D, int NQT>
-__device__ inline void tile_softmax(WaveState<D, NQT>& w, int lim, int hw, float sl2) {
-  tile_max<MASK>(w, lim, hw, sl2);
-  tile_exp(w, sl2);
+__device__ __attribute__((always_inline)) inline void tile_softmax(WaveState<D, NQT>& w, int lim, int hw, float sl2) {
+  using G = Geometry<D>;
+  constexpr uint32_t kSumLimitBits = 0x5f800000u;   // 2^64 as fp32 bits
+  if constexpr (MASK) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int c = 0; c < NQT; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb * 32 + 8 * (i >> 2) + hw * 4 + (i & 3);
+          if (key >= lim) w.sacc[kb][c][i] = -__builtin_inff();
+        }
+  }
+  float tl[NQT], tlr[NQT];
+  tile_probs(w, sl2, tl, tlr);
+  // Integer test on the magnitude bits: true for sums above 2^64, inf and
+  // NaN alike, independent of how the compiler treats NaN comparisons.
+  bool bad = false;
+#pragma unroll
+  for (int c = 0; c < NQT; ++c) bad |= (__builtin_bit_cast(uint32_t, tl[c]) & 0x7fffffffu) > kSumLimitBits;
+  if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+    asm volatile("; raise running max" ::);
+#pragma unroll
+    for (int c = 0; c < NQT; ++c) {
+      float mx = w.sacc[0][c][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, w.sacc[kb][c][i]);
+      mx = fmaxf(mx, xor32(mx));
+      const float m_new = fmaxf(mx * sl2, w.m_run[c]);
+      const float alpha = __builtin_amdgcn_exp2f(w.m_run[c] - m_new);   // 0 when m was -inf
+      w.m_run[c] = m_new;
+      w.l_run[c] *= alpha;
+      w.lr_run[c] *= alpha;
+#pragma unroll
+      for (int v = 0; v < G::vTiles; ++v) w.oacc[v][c] *= alpha;
+    }
+    tile_probs(w, sl2, tl, tlr);
+  }
+#pragma unroll
+  for (int c = 0; c < NQT; ++c) {
+    w.l_run[c] += tl[c];
+    w.lr_run[c] += tlr[c];
+  }
 }
 
 // O^T += V^T P^T for the tile whose V sits in `vl`; each V operand read from
@@ -263,7 +270,7 @@ __device__ inline void tile_softmax(WaveState<D, NQT>& w, int lim, int hw, float
 // keep the swizzle: it depends on the row only modulo 4 (d=128) or through
 // (row/2) mod 2 (d=64), which adding a multiple of 8 rows leaves unchanged.
 template <int D, int NQT>
-__device__ inline void tile_pv(WaveState<D, NQT>& w, const __bf16* vl, const OperandOffsets<D>& off) {
+__device__ __attribute__((always_inline)) inline void tile_pv(WaveState<D, NQT>& w, const __bf16* vl, const OperandOffsets<D>& off) {
   using G = Geometry<D>;
 #pragma unroll
   for (int v = 0; v < G::vTiles; ++v) {
@@ -522,9 +529,8 @@ void partial_kernel(const PartialParams p) {
       using NB = std::integral_constant<int, 1 - b>;
       const bool k2 = j + 2 < n_tiles;
       fetch(k2 ? j + 2 : -1, k2 ? kb_(B) : nullptr, j + 1, vb_(NB{}));
-      tile_max<false>(w, kBc, hw, sl2);
       tile_scores(nx, w, kb_(NB{}), off);
-      tile_exp(w, sl2);
+      tile_softmax<false>(w, kBc, hw, sl2);
       tile_pv(w, vb_(B), off);
       land();
       __syncthreads();
@@ -534,8 +540,7 @@ void partial_kernel(const PartialParams p) {
         for (int c = 0; c < NQT; ++c) w.sacc[kb][c] = nx[kb][c];
     };
     auto last = [&](auto B, int j) {
-      tile_max<true>(w, len_k - j * kBc, hw, sl2);
-      tile_exp(w, sl2);
+      tile_softmax<true>(w, len_k - j * kBc, hw, sl2);
       tile_pv(w, vb_(B), off);
     };
     fetch(0, k_lds0, 0, v_lds0);
