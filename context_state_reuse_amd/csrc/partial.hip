@@ -49,7 +49,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBc = 64;             // keys per K/V tile
 
 #ifndef DITANGO_ONES_ROW
 #define DITANGO_ONES_ROW 1
@@ -130,13 +129,14 @@ __device__ __attribute__((always_inline)) inline int v_operand_offset(int r, int
 
 // Per-wave pieces of the key-tile loop.  A wave owns 32 queries (one MFMA
 // column tile); see the file comment for the operand layouts.
-template <int D, int NQT>
+template <int D, int NQT, int NKB>
 struct WaveState {
   using G = Geometry<D>;
+  static constexpr int nkb = NKB;  // 32-key blocks per tile
   bf16x8 qf[NQT][G::kSteps];      // Q^T operand, per 32-query column tile
   f32x16 oacc[G::vTiles][NQT];    // O^T accumulator
-  f32x16 sacc[2][NQT];            // S^T of the current tile (two 32-key blocks)
-  bf16x8 pb[4][NQT];              // P^T operand of the tile's four 16-key steps
+  f32x16 sacc[NKB][NQT];          // S^T of the current tile
+  bf16x8 pb[2 * NKB][NQT];        // P^T operand of the tile's 16-key steps
   float m_run[NQT], l_run[NQT], lr_run[NQT];
 };
 
@@ -159,12 +159,12 @@ struct OperandOffsets {
 
 // S^T = K Q^T for the 64 keys of one LDS tile into `sacc`; each K operand
 // read from LDS feeds the NQT column tiles.
-template <int D, int NQT>
-__device__ __attribute__((always_inline)) inline void tile_scores(f32x16 (&sacc)[2][NQT], const WaveState<D, NQT>& w, const __bf16* kl,
-                                   const OperandOffsets<D>& off) {
+template <int D, int NQT, int NKB>
+__device__ __attribute__((always_inline)) inline void tile_scores(f32x16 (&sacc)[NKB][NQT], const WaveState<D, NQT, NKB>& w,
+                                                                  const __bf16* kl, const OperandOffsets<D>& off) {
   using G = Geometry<D>;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
     for (int c = 0; c < NQT; ++c) sacc[kb][c] = f32x16{};
 #pragma unroll
@@ -187,8 +187,12 @@ __device__ __attribute__((always_inline)) inline void tile_scores(f32x16 (&sacc)
 // takes the slow path: exact tile max, m raised to it, accumulated state
 // rescaled, probabilities recomputed.  After the first tile this is rare.
 // MASK: keys at or past `lim` in this tile score -inf (ragged last tile).
-template <int D, int NQT>
-__device__ __attribute__((always_inline)) inline void tile_probs(WaveState<D, NQT>& w, float sl2, float (&tl)[NQT],
+#ifndef DITANGO_INTERLEAVE_VALU
+#define DITANGO_INTERLEAVE_VALU 9
+#endif
+
+template <int D, int NQT, int NKB>
+__device__ __attribute__((always_inline)) inline void tile_probs(WaveState<D, NQT, NKB>& w, float sl2, float (&tl)[NQT],
                                                                  float (&tlr)[NQT]) {
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
@@ -196,7 +200,7 @@ __device__ __attribute__((always_inline)) inline void tile_probs(WaveState<D, NQ
     tl[c] = 0.0f;
     tlr[c] = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         uint32_t words[4];
@@ -216,13 +220,27 @@ __device__ __attribute__((always_inline)) inline void tile_probs(WaveState<D, NQ
   }
 }
 
-template <bool MASK, int D, int NQT>
-__device__ __attribute__((always_inline)) inline void tile_softmax(WaveState<D, NQT>& w, int lim, int hw, float sl2) {
+// Interleave the MFMAs and VALU instructions of the current scheduling
+// region: n_mfma groups of (1 MFMA, per VALU).  Used where the next tile's
+// score MFMAs and this tile's probabilities are independent, so one wave
+// keeps the matrix core busy while it issues the softmax arithmetic.
+template <int n_mfma, int per>
+__device__ __attribute__((always_inline)) inline void interleave_mfma_valu() {
+#pragma unroll
+  for (int i = 0; i < n_mfma; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, per, 0);  // then `per` VALU
+  }
+}
+
+template <bool MASK, bool INTERLEAVE = false, int D, int NQT, int NKB>
+__device__ __attribute__((always_inline)) inline void tile_softmax(WaveState<D, NQT, NKB>& w, int lim, int hw,
+                                                                   float sl2) {
   using G = Geometry<D>;
   constexpr uint32_t kSumLimitBits = 0x5f800000u;   // 2^64 as fp32 bits
   if constexpr (MASK) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int c = 0; c < NQT; ++c)
 #pragma unroll
@@ -233,6 +251,7 @@ __device__ __attribute__((always_inline)) inline void tile_softmax(WaveState<D, 
   }
   float tl[NQT], tlr[NQT];
   tile_probs(w, sl2, tl, tlr);
+  if constexpr (INTERLEAVE) interleave_mfma_valu<NKB * G::kSteps * NQT, DITANGO_INTERLEAVE_VALU>();
   // Integer test on the magnitude bits: true for sums above 2^64, inf and
   // NaN alike, independent of how the compiler treats NaN comparisons.
   bool bad = false;
@@ -244,7 +263,7 @@ __device__ __attribute__((always_inline)) inline void tile_softmax(WaveState<D, 
     for (int c = 0; c < NQT; ++c) {
       float mx = w.sacc[0][c][0];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, w.sacc[kb][c][i]);
       mx = fmaxf(mx, xor32(mx));
@@ -269,13 +288,14 @@ __device__ __attribute__((always_inline)) inline void tile_softmax(WaveState<D, 
 // LDS feeds the NQT column tiles.  Rows u*16 (+8) added to the base offsets
 // keep the swizzle: it depends on the row only modulo 4 (d=128) or through
 // (row/2) mod 2 (d=64), which adding a multiple of 8 rows leaves unchanged.
-template <int D, int NQT>
-__device__ __attribute__((always_inline)) inline void tile_pv(WaveState<D, NQT>& w, const __bf16* vl, const OperandOffsets<D>& off) {
+template <int D, int NQT, int NKB>
+__device__ __attribute__((always_inline)) inline void tile_pv(WaveState<D, NQT, NKB>& w, const __bf16* vl,
+                                                              const OperandOffsets<D>& off) {
   using G = Geometry<D>;
 #pragma unroll
   for (int v = 0; v < G::vTiles; ++v) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 2 * NKB; ++u) {
       const __bf16* p0 = &vl[u * 16 * G::VS + off.voff[v]];
       const __bf16* p1 = &vl[(u * 16 + 8) * G::VS + off.voff[v]];
       const bf16x8 a = read_v_operand(p0, p1);
@@ -294,11 +314,13 @@ __device__ __attribute__((always_inline)) inline void tile_pv(WaveState<D, NQT>&
 template <int D, int NQT>
 constexpr int waves_per_simd() { return NQT == 2 ? 1 : 2; }
 
-template <int D, int WAVES, int NQT, int SCHED>
+template <int D, int WAVES, int NQT, int SCHED, int BC>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
                           amdgpu_waves_per_eu(waves_per_simd<D, NQT>(), waves_per_simd<D, NQT>())))
 void partial_kernel(const PartialParams p) {
   using G = Geometry<D>;
+  constexpr int kBc = BC;                          // keys per K/V tile (32 or 64)
+  static_assert(BC == 32 || BC == 64, "key tile of 32 or 64");
   constexpr int kThreads = 64 * WAVES;
   constexpr int QPW = 32 * NQT;                    // query rows per wave
   constexpr int BR = QPW * WAVES;                  // query rows per block
@@ -343,7 +365,7 @@ void partial_kernel(const PartialParams p) {
   const float sl2 = p.scale_log2;
   const int row0 = qt * BR + wave * QPW + l32;    // this lane's query row of column tile 0
 
-  WaveState<D, NQT> w;
+  WaveState<D, NQT, BC / 32> w;
 #pragma unroll
   for (int c = 0; c < NQT; ++c) {
     const __bf16* qrow = Qh + static_cast<size_t>(min(row0 + 32 * c, len_q - 1)) * D;
@@ -386,21 +408,23 @@ void partial_kernel(const PartialParams p) {
   // Direct-load geometry: round i of a tile covers chunk positions
   // [(i*WAVES + wave)*64, +64); per-lane element offsets of the global
   // source (swizzled) are fixed for the kernel.
-  constexpr int kRounds = G::direct ? kBc * G::cpr / kThreads : 1;
-  static_assert(!G::direct || kBc * G::cpr % kThreads == 0, "tile must split evenly over the block");
+  constexpr int kGroups = G::direct ? kBc * G::cpr / 64 : 1;          // 64-chunk groups per tile
+  constexpr int kRounds = (kGroups + WAVES - 1) / WAVES;                 // groups per wave (last may idle)
+  static_assert(!G::direct || kBc * G::cpr % 64 == 0, "tile must split into 64-chunk groups");
   const int swave = __builtin_amdgcn_readfirstlane(wave);
   int krow_of[kRounds], kgoff[kRounds], vgoff[kRounds];
 #pragma unroll
   for (int i = 0; i < kRounds; ++i) {
-    const int idx = (i * WAVES + wave) * 64 + lane;
+    const int idx = min((i * WAVES + wave) * 64 + lane, kBc * G::cpr - 1);
     const int r = G::direct ? idx / G::cpr : 0, pos = G::direct ? idx % G::cpr : 0;
     krow_of[i] = r;
     kgoff[i] = r * D + ((pos ^ G::kswz(r)) << 3);
     vgoff[i] = r * D + ((pos ^ G::vswz(r)) << 3);
   }
-  auto gload_direct = [&](int kt_k, __bf16* kdst, int kt_v, __bf16* vdst) {
+  auto gload_direct = [&](int kt_k, __bf16* kdst, int kt_v, __bf16* vdst) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < (G::direct ? kRounds : 0); ++i) {
+      if (kGroups % WAVES != 0 && i * WAVES + swave >= kGroups) break;   // wave-uniform
       const int lds_elem0 = (i * WAVES + swave) * 64 * 8;   // first element this wave writes
       if (kt_k >= 0) {
         const __bf16* src = Kh + static_cast<size_t>(kt_k) * kBc * D + kgoff[i];
@@ -418,7 +442,7 @@ void partial_kernel(const PartialParams p) {
       }
     }
   };
-  auto gload = [&](int kt_k, int kt_v) {
+  auto gload = [&](int kt_k, int kt_v) __attribute__((always_inline)) {
     if constexpr (G::direct) {
       (void)kt_k;
       (void)kt_v;
@@ -440,7 +464,7 @@ void partial_kernel(const PartialParams p) {
       }
     }
   };
-  auto swrite = [&](__bf16* kdst, __bf16* vdst) {
+  auto swrite = [&](__bf16* kdst, __bf16* vdst) __attribute__((always_inline)) {
     if constexpr (G::direct) {
       (void)kdst;
       (void)vdst;
@@ -461,7 +485,7 @@ void partial_kernel(const PartialParams p) {
   // index of -1 fetches nothing; its destination must then be nullptr).
   __bf16* pend_k = nullptr;
   __bf16* pend_v = nullptr;
-  auto fetch = [&](int kt_k, __bf16* kdst, int kt_v, __bf16* vdst) {
+  auto fetch = [&](int kt_k, __bf16* kdst, int kt_v, __bf16* vdst) __attribute__((always_inline)) {
     if constexpr (G::direct) {
       gload_direct(kt_k, kdst, kt_v, vdst);
     } else {
@@ -471,7 +495,7 @@ void partial_kernel(const PartialParams p) {
     pend_v = vdst;
   };
   // Complete the transfers started by the last fetch.
-  auto land = [&]() { swrite(pend_k, pend_v); };
+  auto land = [&]() __attribute__((always_inline)) { swrite(pend_k, pend_v); };
 
   // ds_read_b64_tr_b16 addressing for the V^T operand: in each 16-lane group
   // lane 4r+c supplies key row r, dims 4c..4c+3 of the group's 16 dims, and
@@ -480,15 +504,15 @@ void partial_kernel(const PartialParams p) {
   const int tr_dim = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
   const OperandOffsets<D> off(l32, hw, tr_r, tr_dim);
   // Buffer pair B (0 or 1) as compile-time pointers.
-  auto kb_ = [&](auto B) -> __bf16* { if constexpr (decltype(B)::value == 0) return k_lds0; else return k_lds1; };
-  auto vb_ = [&](auto B) -> __bf16* { if constexpr (decltype(B)::value == 0) return v_lds0; else return v_lds1; };
+  auto kb_ = [&](auto B) __attribute__((always_inline)) -> __bf16* { if constexpr (decltype(B)::value == 0) return k_lds0; else return k_lds1; };
+  auto vb_ = [&](auto B) __attribute__((always_inline)) -> __bf16* { if constexpr (decltype(B)::value == 0) return v_lds0; else return v_lds1; };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
 
   if constexpr (SCHED == 0) {
     // Plain: per tile, scores -> softmax -> PV, one barrier.  Tile kt lives
     // in buffer pair kt & 1; the next tile is fetched into the other pair.
-    auto full_tile = [&](auto B, int kt) {
+    auto full_tile = [&](auto B, int kt) __attribute__((always_inline)) {
       constexpr int b = decltype(B)::value;
       using NB = std::integral_constant<int, 1 - b>;
       fetch(kt + 1, kb_(NB{}), kt + 1, vb_(NB{}));
@@ -498,7 +522,7 @@ void partial_kernel(const PartialParams p) {
       land();
       __syncthreads();
     };
-    auto last_tile = [&](auto B, int kt) {
+    auto last_tile = [&](auto B, int kt) __attribute__((always_inline)) {
       tile_scores(w.sacc, w, kb_(B), off);
       tile_softmax<true>(w, len_k - kt * kBc, hw, sl2);
       tile_pv(w, vb_(B), off);
@@ -523,23 +547,23 @@ void partial_kernel(const PartialParams p) {
     // then the PV product of tile j.  K runs one tile ahead of V: iteration
     // j reads K(j+1) from pair (j+1)&1 and V(j) from pair j&1, and fetches
     // K(j+2) into pair j&1 and V(j+1) into pair (j+1)&1.
-    f32x16 nx[2][NQT];      // scores of the next tile
-    auto iter = [&](auto B, int j) {   // B = j & 1
+    f32x16 nx[BC / 32][NQT];   // scores of the next tile
+    auto iter = [&](auto B, int j) __attribute__((always_inline)) {   // B = j & 1
       constexpr int b = decltype(B)::value;
       using NB = std::integral_constant<int, 1 - b>;
       const bool k2 = j + 2 < n_tiles;
       fetch(k2 ? j + 2 : -1, k2 ? kb_(B) : nullptr, j + 1, vb_(NB{}));
       tile_scores(nx, w, kb_(NB{}), off);
-      tile_softmax<false>(w, kBc, hw, sl2);
+      tile_softmax<false, true>(w, kBc, hw, sl2);
       tile_pv(w, vb_(B), off);
       land();
       __syncthreads();
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
         for (int c = 0; c < NQT; ++c) w.sacc[kb][c] = nx[kb][c];
     };
-    auto last = [&](auto B, int j) {
+    auto last = [&](auto B, int j) __attribute__((always_inline)) {
       tile_softmax<true>(w, len_k - j * kBc, hw, sl2);
       tile_pv(w, vb_(B), off);
     };
@@ -600,17 +624,24 @@ void partial_kernel(const PartialParams p) {
 // Loop schedule per head dim, from side-by-side measurement on MI355X: the
 // in-wave pipeline (2) wins at d = 64 and 72, the plain loop (0) at d = 128
 // (where the pipeline's second score buffer leaves fewer registers for LDS
-// prefetch).  A two-group ping-pong (FA3-style, two barriers per tile) was
-// measured slower everywhere and is not kept.
+// prefetch).  A two-group ping-pong (FA3-style, one group on MFMA while the
+// other runs the softmax, two barriers per tile) was measured slower on
+// every head dim and is not kept.
 #ifndef DITANGO_SCHED
 #define DITANGO_SCHED -1
+#endif
+
+// Keys per tile: 64, or 32 to leave registers for scheduling.
+#ifndef DITANGO_BC
+#define DITANGO_BC 64
 #endif
 
 template <int D, int WAVES, int NQT>
 hipError_t launch(PartialParams& p, hipStream_t stream) {
   constexpr int sched = DITANGO_SCHED >= 0 ? DITANGO_SCHED : (D == 128 ? 0 : 2);
   static_assert(sched == 0 || sched == 2, "loop schedules: 0 (plain) or 2 (software-pipelined)");
-  hipLaunchKernelGGL((partial_kernel<D, WAVES, NQT, sched>), dim3(p.n_blocks), dim3(64 * WAVES), 0, stream, p);
+  hipLaunchKernelGGL((partial_kernel<D, WAVES, NQT, sched, DITANGO_BC>), dim3(p.n_blocks), dim3(64 * WAVES), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
