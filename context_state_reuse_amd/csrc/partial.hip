@@ -319,8 +319,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
                           amdgpu_waves_per_eu(waves_per_simd<D, NQT>(), waves_per_simd<D, NQT>())))
 void partial_kernel(const PartialParams p) {
   using G = Geometry<D>;
-  constexpr int kBc = BC;                          // keys per K/V tile (32 or 64)
-  static_assert(BC == 32 || BC == 64, "key tile of 32 or 64");
+  constexpr int kBc = BC;                          // keys per K/V tile (32, 64 or 128)
+  static_assert(BC == 32 || BC == 64 || BC == 128, "key tile of 32, 64 or 128");
   constexpr int kThreads = 64 * WAVES;
   constexpr int QPW = 32 * NQT;                    // query rows per wave
   constexpr int BR = QPW * WAVES;                  // query rows per block
@@ -622,25 +622,27 @@ void partial_kernel(const PartialParams p) {
 }
 
 // Loop schedule per head dim, from side-by-side measurement on MI355X: the
-// in-wave pipeline (2) wins at d = 64 and 72, the plain loop (0) at d = 128
-// (where the pipeline's second score buffer leaves fewer registers for LDS
-// prefetch).  A two-group ping-pong (FA3-style, one group on MFMA while the
-// other runs the softmax, two barriers per tile) was measured slower on
-// every head dim and is not kept.
+// in-wave pipeline (2) wins at d = 72 (about 3%), the plain loop (0) at
+// d = 64 (about 4%) and d = 128 (where the pipeline's second score buffer
+// leaves fewer registers for LDS prefetch).  A two-group ping-pong
+// (FA3-style, one group on MFMA while the other runs the softmax, two
+// barriers per tile) was measured slower on every head dim and is not kept.
 #ifndef DITANGO_SCHED
 #define DITANGO_SCHED -1
 #endif
 
-// Keys per tile: 64, or 32 to leave registers for scheduling.
+// Keys per tile: 64 (32 leaves registers for scheduling; 128 was measured
+// slower at d = 64 and spills at d = 72).
 #ifndef DITANGO_BC
 #define DITANGO_BC 64
 #endif
 
 template <int D, int WAVES, int NQT>
 hipError_t launch(PartialParams& p, hipStream_t stream) {
-  constexpr int sched = DITANGO_SCHED >= 0 ? DITANGO_SCHED : (D == 128 ? 0 : 2);
+  constexpr int sched = DITANGO_SCHED >= 0 ? DITANGO_SCHED : (D == 72 ? 2 : 0);
+  constexpr int bc = DITANGO_BC;
   static_assert(sched == 0 || sched == 2, "loop schedules: 0 (plain) or 2 (software-pipelined)");
-  hipLaunchKernelGGL((partial_kernel<D, WAVES, NQT, sched, DITANGO_BC>), dim3(p.n_blocks), dim3(64 * WAVES), 0,
+  hipLaunchKernelGGL((partial_kernel<D, WAVES, NQT, sched, bc>), dim3(p.n_blocks), dim3(64 * WAVES), 0,
                      stream, p);
   return hipGetLastError();
 }
