@@ -53,6 +53,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #ifndef DITANGO_ONES_ROW
 #define DITANGO_ONES_ROW 1
 #endif
+#ifndef DITANGO_D72_DIRECT
+#define DITANGO_D72_DIRECT 1
+#endif
 
 template <int D>
 struct Geometry {
@@ -65,30 +68,40 @@ struct Geometry {
   static constexpr int kSteps = DK / 16;
   static constexpr int vTiles = DV / 32;
   static constexpr int chunks = D / 8;            // 16-byte chunks per global row
-  // Staged layout (d = 72): rows padded, strides chosen with a bank-conflict
-  // counter sweep on gfx950 (64 banks of 4 bytes).  K rows are read 16 B per
-  // lane, 16 keys per pass: a stride of an odd multiple of 4 dwords spreads
-  // them over all banks.  V rows are read by ds_read_b64_tr_b16, 32 lanes
-  // per pass = 4 key rows x 64 B: a stride of 16 or 48 (mod 64) dwords puts
-  // those rows on disjoint banks.
+  // Staged layout (global -> registers -> LDS; kept as an alternative for
+  // d = 72): rows padded, strides chosen with a bank-conflict counter sweep
+  // on gfx950 (64 banks of 4 bytes).  K rows are read 16 B per lane, 16 keys
+  // per pass: a stride of an odd multiple of 4 dwords spreads them over all
+  // banks.  V rows are read by ds_read_b64_tr_b16, 32 lanes per pass = 4 key
+  // rows x 64 B: a stride of 16 or 48 (mod 64) dwords puts those rows on
+  // disjoint banks.
   //
-  // Direct layout (d = 64, 128): rows unpadded, filled by
-  // global_load_lds_dwordx4 (a wave writes 64 consecutive 16-byte chunks,
-  // so rows cannot be padded); the 16-byte chunk c of row r sits at position
-  // c ^ f(r), and the global load of position p fetches chunk p ^ f(r).
+  // Direct layout: filled by global_load_lds_dwordx4 (a wave writes 64
+  // consecutive 16-byte chunks, so a row's stride is a whole number of
+  // chunks).  For d = 64 and 128 rows are unpadded and the 16-byte chunk c
+  // of row r sits at position c ^ f(r); the global load of position p
+  // fetches chunk p ^ f(r).
   //   K: f = r mod 16 (d=128) or (r/2) mod 8 (d=64): the 16 rows of a
   //      16-lane pass land on distinct banks.
   //   V: f = 4 (r mod 4) (d=128) or 4 ((r/2) mod 2) (d=64): the 4 rows x 4
   //      chunks of a 32-lane transpose-read pass land on distinct banks.
-  static constexpr bool direct = D == 64 || D == 128;
-  static constexpr int cpr = D / 8;               // 16-byte chunks per row (direct layout)
+  //   d = 72: no swizzle.  K rows of 72 (36 dwords, an odd multiple of 4);
+  //      the contraction pad 72..79 reads the next row's first chunk, which
+  //      is finite and meets Q's zero pad.  V rows of 96 (48 dwords) whose
+  //      chunks 9..11 -- the ones column and zeros -- are written once and
+  //      skipped by the loads.
+  static constexpr bool direct = D == 64 || D == 128 || (D == 72 && DITANGO_D72_DIRECT);
   static constexpr int KS = direct ? D : DK + 8;
-  static constexpr int VS = direct ? D : (DV == 128 ? 160 : 96);
+  static constexpr int VS = direct ? DV : (DV == 128 ? 160 : 96);
+  static constexpr int kcpr = KS / 8;             // 16-byte chunks per LDS row (direct layout)
+  static constexpr int vcpr = VS / 8;
+  static constexpr int kpad = direct && DK > D ? 8 : 0;   // elements past a K tile read by the last row
   static_assert(DV <= VS, "V row must fit its stride");
-  static_assert(direct || (KS / 2) % 8 == 4, "K stride must be an odd multiple of 4 dwords");
-  static_assert(direct || (VS / 2) % 64 == 16 || (VS / 2) % 64 == 48, "V stride must be 16 or 48 mod 64 dwords");
-  __device__ static int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
-  __device__ static int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+  static_assert((direct && D != 72) || (KS / 2) % 8 == 4, "K stride must be an odd multiple of 4 dwords");
+  static_assert((direct && D != 72) || (VS / 2) % 64 == 16 || (VS / 2) % 64 == 48,
+                "V stride must be 16 or 48 mod 64 dwords");
+  __device__ static int kswz(int r) { return D == 128 ? (r & 15) : D == 64 ? ((r >> 1) & 7) : 0; }
+  __device__ static int vswz(int r) { return D == 128 ? 4 * (r & 3) : D == 64 ? 4 * ((r >> 1) & 1) : 0; }
 };
 
 typedef __attribute__((address_space(3))) bf16x4_v lds_bf16x4;
@@ -330,8 +343,8 @@ void partial_kernel(const PartialParams p) {
   // of one buffer never alias the direct loads filling the other and does not
   // make them wait for the prefetch.  The tile loop is unrolled by two so the
   // buffer of every access is a compile-time choice.
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds0[kBc * G::KS];
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds1[kBc * G::KS];
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds0[kBc * G::KS + G::kpad];
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds1[kBc * G::KS + G::kpad];
   __shared__ __attribute__((aligned(16))) __bf16 v_lds0[kBc * G::VS];
   __shared__ __attribute__((aligned(16))) __bf16 v_lds1[kBc * G::VS];
 
@@ -385,14 +398,31 @@ void partial_kernel(const PartialParams p) {
     w.lr_run[c] = 0.0f;
   }
 
-  // K columns beyond d (d = 72 pads the contraction to 80) must read as zero.
+  // K columns beyond d (d = 72 pads the contraction to 80) must read as
+  // zero (staged layout), or as finite values (direct layout: the next row,
+  // and past the last row this zeroed pad).
   if constexpr (G::DK > D) {
-    for (int i = tid; i < 2 * kBc; i += kThreads)
-      *reinterpret_cast<u32x4*>(&(i < kBc ? k_lds0 : k_lds1)[(i % kBc) * G::KS + D]) = u32x4{0u, 0u, 0u, 0u};
+    if constexpr (G::direct) {
+      if (tid < 2) *reinterpret_cast<u32x4*>(&(tid == 0 ? k_lds0 : k_lds1)[kBc * G::KS]) = u32x4{0u, 0u, 0u, 0u};
+    } else {
+      for (int i = tid; i < 2 * kBc; i += kThreads)
+        *reinterpret_cast<u32x4*>(&(i < kBc ? k_lds0 : k_lds1)[(i % kBc) * G::KS + D]) = u32x4{0u, 0u, 0u, 0u};
+    }
   }
   if constexpr (G::ones_row) {
-    static_assert(!G::direct, "the ones column lives in the staged layout's spare columns");
-    for (int i = tid; i < 2 * kBc; i += kThreads) (i < kBc ? v_lds0 : v_lds1)[(i % kBc) * G::VS + D] = (__bf16)1.0f;
+    if constexpr (G::direct) {
+      // Chunks D/8 .. vcpr-1 of every V row: 1.0 at column D, zeros after.
+      constexpr int padc = G::vcpr - D / 8;
+      static_assert(D % 8 == 0 && padc >= 1, "ones column starts a spare chunk");
+      for (int i = tid; i < 2 * kBc * padc; i += kThreads) {
+        const int j = i % (kBc * padc);
+        const int r = j / padc, c = D / 8 + j % padc;
+        const u32x4 val = {c == D / 8 ? 0x3f80u : 0u, 0u, 0u, 0u};   // bf16 1.0 in element 0
+        *reinterpret_cast<u32x4*>(&(i < kBc * padc ? v_lds0 : v_lds1)[r * G::VS + c * 8]) = val;
+      }
+    } else {
+      for (int i = tid; i < 2 * kBc; i += kThreads) (i < kBc ? v_lds0 : v_lds1)[(i % kBc) * G::VS + D] = (__bf16)1.0f;
+    }
   }
 
   const int n_tiles = (len_k + kBc - 1) / kBc;
@@ -405,26 +435,36 @@ void partial_kernel(const PartialParams p) {
   // buffers passed to swrite must be the ones given to the matching gload.
   // Staged layout: gload fills registers and swrite stores them.
 
-  // Direct-load geometry: round i of a tile covers chunk positions
-  // [(i*WAVES + wave)*64, +64); per-lane element offsets of the global
-  // source (swizzled) are fixed for the kernel.
-  constexpr int kGroups = G::direct ? kBc * G::cpr / 64 : 1;          // 64-chunk groups per tile
-  constexpr int kRounds = (kGroups + WAVES - 1) / WAVES;                 // groups per wave (last may idle)
-  static_assert(!G::direct || kBc * G::cpr % 64 == 0, "tile must split into 64-chunk groups");
+  // Direct-load geometry: round i of a tile covers LDS chunk positions
+  // [(i*WAVES + wave)*64, +64) (lane L writes position +L); per-lane element
+  // offsets of the global source (swizzled) are fixed for the kernel.  V
+  // positions past column d (the d = 72 ones/zero chunks) are not loaded.
+  constexpr int kGroupsK = G::direct ? kBc * G::kcpr / 64 : 1;          // 64-chunk groups per K tile
+  constexpr int kGroupsV = G::direct ? kBc * G::vcpr / 64 : 1;
+  constexpr int kRoundsK = (kGroupsK + WAVES - 1) / WAVES;               // groups per wave (last may idle)
+  constexpr int kRoundsV = (kGroupsV + WAVES - 1) / WAVES;
+  static_assert(!G::direct || (kBc * G::kcpr % 64 == 0 && kBc * G::vcpr % 64 == 0),
+                "tiles must split into 64-chunk groups");
   const int swave = __builtin_amdgcn_readfirstlane(wave);
-  int krow_of[kRounds], kgoff[kRounds], vgoff[kRounds];
+  int krow_of[kRoundsK], kgoff[kRoundsK], vrow_of[kRoundsV], vgoff[kRoundsV];
 #pragma unroll
-  for (int i = 0; i < kRounds; ++i) {
-    const int idx = min((i * WAVES + wave) * 64 + lane, kBc * G::cpr - 1);
-    const int r = G::direct ? idx / G::cpr : 0, pos = G::direct ? idx % G::cpr : 0;
+  for (int i = 0; i < kRoundsK; ++i) {
+    const int idx = min((i * WAVES + wave) * 64 + lane, kBc * G::kcpr - 1);
+    const int r = G::direct ? idx / G::kcpr : 0, pos = G::direct ? idx % G::kcpr : 0;
     krow_of[i] = r;
     kgoff[i] = r * D + ((pos ^ G::kswz(r)) << 3);
-    vgoff[i] = r * D + ((pos ^ G::vswz(r)) << 3);
+  }
+#pragma unroll
+  for (int i = 0; i < kRoundsV; ++i) {
+    const int idx = min((i * WAVES + wave) * 64 + lane, kBc * G::vcpr - 1);
+    const int r = G::direct ? idx / G::vcpr : 0, pos = G::direct ? idx % G::vcpr : 0;
+    vrow_of[i] = r;
+    vgoff[i] = pos < D / 8 ? r * D + ((pos ^ G::vswz(r)) << 3) : -1;   // -1: spare chunk, not loaded
   }
   auto gload_direct = [&](int kt_k, __bf16* kdst, int kt_v, __bf16* vdst) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < (G::direct ? kRounds : 0); ++i) {
-      if (kGroups % WAVES != 0 && i * WAVES + swave >= kGroups) break;   // wave-uniform
+    for (int i = 0; i < (G::direct ? kRoundsK : 0); ++i) {
+      if (kGroupsK % WAVES != 0 && i * WAVES + swave >= kGroupsK) break;   // wave-uniform
       const int lds_elem0 = (i * WAVES + swave) * 64 * 8;   // first element this wave writes
       if (kt_k >= 0) {
         const __bf16* src = Kh + static_cast<size_t>(kt_k) * kBc * D + kgoff[i];
@@ -433,10 +473,15 @@ void partial_kernel(const PartialParams p) {
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                          (__attribute__((address_space(3))) void*)(kdst + lds_elem0), 16, 0, 0);
       }
-      if (kt_v >= 0) {
+    }
+#pragma unroll
+    for (int i = 0; i < (G::direct ? kRoundsV : 0); ++i) {
+      if (kGroupsV % WAVES != 0 && i * WAVES + swave >= kGroupsV) break;   // wave-uniform
+      const int lds_elem0 = (i * WAVES + swave) * 64 * 8;
+      if (kt_v >= 0 && (G::vcpr == D / 8 || vgoff[i] >= 0)) {
         const __bf16* src = Vh + static_cast<size_t>(kt_v) * kBc * D + vgoff[i];
-        if (kt_v * kBc + kBc > len_k && kt_v * kBc + krow_of[i] >= len_k)
-          src = Vh + static_cast<size_t>(len_k - 1 - krow_of[i]) * D + vgoff[i];
+        if (kt_v * kBc + kBc > len_k && kt_v * kBc + vrow_of[i] >= len_k)
+          src = Vh + static_cast<size_t>(len_k - 1 - vrow_of[i]) * D + vgoff[i];
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                          (__attribute__((address_space(3))) void*)(vdst + lds_elem0), 16, 0, 0);
       }
