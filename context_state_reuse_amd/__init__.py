@@ -7,6 +7,8 @@ tensors, host masks and streams into the C calls.
 from .binding import (DITANGO_EHIP, DITANGO_EINVAL, DITANGO_ENOCACHE,  # noqa: F401
                       DITANGO_MASK_ALL, DITANGO_MASK_NEAREST, DITANGO_MASK_NONE,
                       DITANGO_MASK_RADIUS, DITANGO_MASK_RANDOM, DITANGO_OK, EXPORTED,
-                      DitangoError, StateCache, ditango_attn_partial, ditango_mask_build,
-                      ditango_state_cache_update, ditango_state_merge, ditango_states_bytes,
-                      ditango_version, make_shape, workload_mask)
+                      DITANGO_MAX_SLOTS, DitangoError, GroupedStateCache, StateCache,
+                      ditango_attn_partial, ditango_group_attn_partial, ditango_group_cache_update,
+                      ditango_group_compose, ditango_group_merge, ditango_group_slots,
+                      ditango_mask_build, ditango_state_cache_update, ditango_state_merge,
+                      ditango_states_bytes, ditango_version, make_shape, workload_mask)

@@ -28,6 +28,7 @@ DITANGO_EINVAL = -1
 DITANGO_ENOCACHE = -2
 DITANGO_EHIP = -3
 DITANGO_MAX_P = 32
+DITANGO_MAX_SLOTS = 32
 
 DITANGO_MASK_ALL = 0
 DITANGO_MASK_NONE = 1
@@ -40,7 +41,10 @@ MASK_POLICIES = {"all": DITANGO_MASK_ALL, "none": DITANGO_MASK_NONE, "radius": D
 
 EXPORTED = ("ditango_states_bytes", "ditango_states_init", "ditango_attn_partial",
             "ditango_state_cache_update", "ditango_state_merge", "ditango_mask_build",
-            "ditango_last_error", "ditango_version")
+            "ditango_last_error", "ditango_version",
+            "ditango_group_slots", "ditango_gstates_slot_bytes", "ditango_gstates_init",
+            "ditango_group_attn_partial", "ditango_group_cache_update", "ditango_group_merge",
+            "ditango_group_compose", "ditango_group_reset")
 
 
 class DitangoError(RuntimeError):
@@ -57,6 +61,12 @@ class ditango_shape_t(ctypes.Structure):
 class ditango_states_t(ctypes.Structure):
     _fields_ = [("shape", ditango_shape_t), ("S", ctypes.c_int32), ("O", ctypes.c_void_p),
                 ("LSE", ctypes.c_void_p), ("tc", ctypes.c_void_p)]
+
+
+class ditango_gstates_t(ctypes.Structure):
+    _fields_ = [("shape", ditango_shape_t), ("S", ctypes.c_int32), ("g0", ctypes.c_int32), ("g", ctypes.c_int32),
+                ("O", ctypes.c_void_p * DITANGO_MAX_SLOTS), ("LSE", ctypes.c_void_p * DITANGO_MAX_SLOTS),
+                ("tc", ctypes.c_void_p)]
 
 
 def _load():
@@ -82,6 +92,25 @@ def _load():
     lib.ditango_last_error.argtypes = []
     lib.ditango_version.restype = ctypes.c_int32
     lib.ditango_version.argtypes = []
+    gst = ctypes.POINTER(ditango_gstates_t)
+    ptab = ctypes.POINTER(ctypes.c_void_p)
+    lib.ditango_group_slots.restype = ctypes.c_int32
+    lib.ditango_group_slots.argtypes = [i32, i32]
+    lib.ditango_gstates_slot_bytes.restype = ctypes.c_size_t
+    lib.ditango_gstates_slot_bytes.argtypes = [ctypes.POINTER(ditango_shape_t), ctypes.POINTER(ctypes.c_size_t),
+                                               ctypes.POINTER(ctypes.c_size_t)]
+    lib.ditango_gstates_init.restype = ctypes.c_int
+    lib.ditango_gstates_init.argtypes = [gst, ctypes.POINTER(ditango_shape_t), i32, ptab, ptab, vp]
+    lib.ditango_group_attn_partial.restype = ctypes.c_int
+    lib.ditango_group_attn_partial.argtypes = [vp, vp, vp, u8p, gst, vp]
+    lib.ditango_group_cache_update.restype = ctypes.c_int
+    lib.ditango_group_cache_update.argtypes = [gst, u8p, i32, u8p]
+    lib.ditango_group_merge.restype = ctypes.c_int
+    lib.ditango_group_merge.argtypes = [gst, vp, vp, vp]
+    lib.ditango_group_compose.restype = ctypes.c_int
+    lib.ditango_group_compose.argtypes = [gst, i32, vp]
+    lib.ditango_group_reset.restype = ctypes.c_int
+    lib.ditango_group_reset.argtypes = [gst, ptab, ptab]
     return lib
 
 
@@ -199,3 +228,118 @@ def workload_mask(w, t: int) -> np.ndarray:
     if t == 0:
         return ditango_mask_build("all", w.P)
     return ditango_mask_build(w.policy, w.P, w.n_fresh, 1000 * w.cfg_id + t)
+
+
+# ------------------------------------------------------------ grouped cache
+
+def ditango_group_slots(P: int, g: int) -> int:
+    return int(lib.ditango_group_slots(int(P), int(g)))
+
+
+def _ptab(ptrs):
+    arr = (ctypes.c_void_p * DITANGO_MAX_SLOTS)()
+    for i, x in enumerate(ptrs):
+        arr[i] = x
+    return arr
+
+
+class GroupedStateCache:
+    """Grouped, composed state cache: one device tensor pair per slot.
+
+    Slot s of query partition q (0 = the local pair, 1 + j = group j of g
+    adjacent partitions without q) holds rows [h][q][S][d].  A group merge
+    (``compose``) releases the slots it no longer needs, so their memory
+    returns to the allocator; ``reset`` re-creates them for an anchor step.
+    """
+
+    def __init__(self, H: int, N: int, d: int, P: int, g: int, scale: float | None = None, device="cuda"):
+        self.shape = make_shape(H, N, d, P, scale)
+        self.H, self.N, self.d, self.P = H, N, d, P
+        self.S = -(-N // P)
+        self.device = device
+        n = ditango_group_slots(P, g)
+        if n == 0:
+            raise DitangoError(DITANGO_EINVAL, f"group size {g} is invalid for P={P}")
+        self.O = [self._slot_o() for _ in range(n)]
+        self.LSE = [self._slot_l() for _ in range(n)]
+        self.tc = np.full((P, DITANGO_MAX_SLOTS), -1, dtype=np.int32)
+        self.st = ditango_gstates_t()
+        _check(lib.ditango_gstates_init(ctypes.byref(self.st), ctypes.byref(self.shape), int(g),
+                                        _ptab([t.data_ptr() for t in self.O]),
+                                        _ptab([t.data_ptr() for t in self.LSE]),
+                                        ctypes.c_void_p(self.tc.ctypes.data)))
+
+    def _slot_o(self):
+        import torch
+        return torch.empty((self.H, self.P, self.S, self.d), dtype=torch.float32, device=self.device)
+
+    def _slot_l(self):
+        import torch
+        return torch.empty((self.H, self.P, self.S), dtype=torch.float32, device=self.device)
+
+    @property
+    def g(self) -> int:
+        return int(self.st.g)
+
+    @property
+    def n_slots(self) -> int:
+        return ditango_group_slots(self.P, self.g)
+
+    @property
+    def tc_matrix(self) -> np.ndarray:
+        return self.tc[:, :self.n_slots].copy()
+
+    @property
+    def device_bytes(self) -> int:
+        return sum(t.numel() * 4 for t in self.O + self.LSE)
+
+    def compose(self, k: int = 2, stream=None) -> None:
+        """Dynamic Group State Compose: group size g -> k g; frees released slots."""
+        import torch
+        _check(lib.ditango_group_compose(ctypes.byref(self.st), int(k), _stream(stream)))
+        n = self.n_slots
+        if len(self.O) > n:
+            # the released buffers are read by the queued group merges
+            torch.cuda.synchronize()
+            del self.O[n:], self.LSE[n:]
+
+    def reset(self) -> None:
+        """Back to the original group size with every slot empty (before an anchor step)."""
+        n = ditango_group_slots(self.P, int(self.st.g0))
+        while len(self.O) < n:
+            self.O.append(self._slot_o())
+            self.LSE.append(self._slot_l())
+        _check(lib.ditango_group_reset(ctypes.byref(self.st), _ptab([t.data_ptr() for t in self.O]),
+                                       _ptab([t.data_ptr() for t in self.LSE])))
+
+
+def ditango_group_attn_partial(Q, K, V, mask, cache: GroupedStateCache, stream=None) -> None:
+    m = _mask(mask, cache.P)
+    _check(lib.ditango_group_attn_partial(_qkv(Q, cache, "Q"), _qkv(K, cache, "K"), _qkv(V, cache, "V"),
+                                          _u8(m), ctypes.byref(cache.st), _stream(stream)))
+
+
+def ditango_group_cache_update(cache: GroupedStateCache, mask, step: int) -> np.ndarray:
+    m = _mask(mask, cache.P)
+    computed = np.zeros((cache.P, cache.n_slots), dtype=np.uint8)
+    _check(lib.ditango_group_cache_update(ctypes.byref(cache.st), _u8(m), int(step), _u8(computed)))
+    return computed
+
+
+def ditango_group_merge(cache: GroupedStateCache, O=None, LSE=None, stream=None):
+    import torch
+    dev = cache.O[0].device
+    if O is None:
+        O = torch.empty((cache.H, cache.N, cache.d), dtype=torch.float32, device=dev)
+    if LSE is None:
+        LSE = torch.empty((cache.H, cache.N), dtype=torch.float32, device=dev)
+    for t, shp, nm in ((O, (cache.H, cache.N, cache.d), "O"), (LSE, (cache.H, cache.N), "LSE")):
+        if not (t.is_cuda and t.dtype == torch.float32 and t.is_contiguous() and tuple(t.shape) == shp):
+            raise ValueError(f"{nm} must be a contiguous float32 device tensor of shape {shp}")
+    _check(lib.ditango_group_merge(ctypes.byref(cache.st), ctypes.c_void_p(O.data_ptr()),
+                                   ctypes.c_void_p(LSE.data_ptr()), _stream(stream)))
+    return O, LSE
+
+
+def ditango_group_compose(cache: GroupedStateCache, k: int = 2, stream=None) -> None:
+    cache.compose(k, stream)

@@ -4,16 +4,20 @@
 // Method: "DiTango: Cost-Effective Parallel Diffusion Generation with
 // Selective Attention State Reuse" -- state selection (COMPUTE/REUSE per
 // unit, t_c = last computation step), anchor steps (all compute, t_c <- t),
-// selective compute and reuse (Fig. 6).  The unit here is one
-// (query partition, KV partition) pair.
+// selective compute and reuse (Fig. 6).  The unit is one (query partition,
+// KV partition) pair in the per-pair cache, one slot (the local pair or a
+// group of adjacent partitions) in the grouped cache, whose groups can be
+// merged k at a time (Dynamic Group State Compose).
 
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "ditango.h"
@@ -86,13 +90,98 @@ struct SplitMix64 {
   }
 };
 
+// ---- grouped cache: slot s of query partition q (0 = local pair,
+// 1 + j = group j = partitions [j g, min((j+1) g, P)) without q)
+
+int group_slots(int P, int g) {
+  if (P < 1 || P > DITANGO_MAX_P || g < 1) return 0;
+  const int n = 1 + (P + g - 1) / g;
+  return n > DITANGO_MAX_SLOTS ? 0 : n;
+}
+
+void group_range(int P, int g, int s, int q, int* a, int* b) {
+  if (s == 0) {
+    *a = q;
+    *b = q + 1;
+  } else {
+    *a = (s - 1) * g;
+    *b = std::min(*a + g, P);
+  }
+}
+
+// The slot holds a state of at least one partition (group {q} alone does not).
+bool slot_live(int P, int g, int q, int s) {
+  int a, b;
+  group_range(P, g, s, q, &a, &b);
+  return s == 0 || b - a > 1 || a != q;
+}
+
+// COMPUTE when any member is fresh in the pair mask.
+bool slot_fresh(const uint8_t* mask, int P, int g, int q, int s) {
+  int a, b;
+  group_range(P, g, s, q, &a, &b);
+  for (int k = a; k < b; ++k)
+    if ((s == 0 || k != q) && mask[q * P + k]) return true;
+  return false;
+}
+
+// Key tokens of slot s of q (the state's reduction length).
+int64_t slot_keys(int N, int P, int S, int g, int q, int s) {
+  int a, b;
+  group_range(P, g, s, q, &a, &b);
+  int64_t n = std::min<int64_t>(static_cast<int64_t>(b) * S, N) - static_cast<int64_t>(a) * S;
+  if (s != 0 && a <= q && q < b) n -= std::min<int64_t>(S, N - static_cast<int64_t>(q) * S);
+  return n;
+}
+
+int& gtc(const ditango_gstates_t* st, int q, int s) { return st->tc[q * DITANGO_MAX_SLOTS + s]; }
+
+int check_slot_buffers(float* const* O, float* const* LSE, int n) {
+  if (!O || !LSE) return fail(DITANGO_EINVAL, "slot buffer tables are NULL");
+  for (int s = 0; s < n; ++s) {
+    if (!O[s] || !LSE[s]) return fail(DITANGO_EINVAL, "slot %d buffers are NULL", s);
+    if ((reinterpret_cast<uintptr_t>(O[s]) | reinterpret_cast<uintptr_t>(LSE[s])) & 15u)
+      return fail(DITANGO_EINVAL, "slot %d buffers must be 16-byte aligned", s);
+  }
+  return DITANGO_OK;
+}
+
+int check_gstates(const ditango_gstates_t* st, int* n_slots) {
+  if (!st) return fail(DITANGO_EINVAL, "states is NULL");
+  int32_t S = 0;
+  int rc = check_shape(&st->shape, &S);
+  if (rc) return rc;
+  if (S != st->S) return fail(DITANGO_EINVAL, "states.S=%d does not match ceil(N/P)=%d", st->S, S);
+  if (st->g0 < 1 || st->g < st->g0 || st->g % st->g0)
+    return fail(DITANGO_EINVAL, "group sizes g0=%d, g=%d are inconsistent", st->g0, st->g);
+  const int n = group_slots(st->shape.P, st->g);
+  if (!n) return fail(DITANGO_EINVAL, "group size %d gives too many slots for P=%d", st->g, st->shape.P);
+  if (!st->tc) return fail(DITANGO_EINVAL, "tc is NULL");
+  if ((rc = check_slot_buffers(st->O, st->LSE, n))) return rc;
+  *n_slots = n;
+  return DITANGO_OK;
+}
+
+hipError_t launch_group_merge(ditango::MergeParams& m, const ditango_gstates_t* st, int n_in,
+                              hipStream_t stream) {
+  m.in_hs = st->shape.P;
+  m.in_qs = 1;
+  m.n_in = n_in;
+  m.H = st->shape.H;
+  m.N = st->shape.N;
+  m.P = st->shape.P;
+  m.S = st->S;
+  m.d = st->shape.d;
+  return ditango::launch_merge(m, stream);
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* ditango_last_error(void) { return g_err.c_str(); }
 
-int32_t ditango_version(void) { return 1; }
+int32_t ditango_version(void) { return 2; }
 
 size_t ditango_states_bytes(const ditango_shape_t* shape, size_t* o_bytes, size_t* lse_bytes) {
   int32_t S = 0;
@@ -199,11 +288,22 @@ int ditango_state_merge(const ditango_states_t* st, float* O, float* LSE, void* 
   const int P = st->shape.P;
   for (int i = 0; i < P * P; ++i)
     if (st->tc[i] < 0) return fail(DITANGO_ENOCACHE, "pair (q=%d, k=%d) holds no state", i / P, i % P);
+  // State k of the rows of (h, q) is slot h*P*P + q*P + k.
   ditango::MergeParams m;
-  m.Os = st->O;
-  m.LSEs = st->LSE;
+  std::memset(&m, 0, sizeof m);
+  const size_t slot_o = static_cast<size_t>(st->S) * st->shape.d;
+  for (int k = 0; k < P; ++k) {
+    m.in_O[k] = st->O + k * slot_o;
+    m.in_L[k] = st->LSE + static_cast<size_t>(k) * st->S;
+  }
+  for (int q = 0; q < P; ++q) m.live[q] = P == 32 ? 0xffffffffu : (1u << P) - 1u;
+  m.in_hs = static_cast<int64_t>(P) * P;
+  m.in_qs = P;
+  m.out_hs = st->shape.N;
+  m.out_qs = st->S;
   m.O = O;
   m.LSE = LSE;
+  m.n_in = P;
   m.H = st->shape.H;
   m.N = st->shape.N;
   m.P = P;
@@ -211,6 +311,222 @@ int ditango_state_merge(const ditango_states_t* st, float* O, float* LSE, void* 
   m.d = st->shape.d;
   hipError_t e = ditango::launch_merge(m, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(DITANGO_EHIP, "merge kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int32_t ditango_group_slots(int32_t P, int32_t g) { return group_slots(P, g); }
+
+size_t ditango_gstates_slot_bytes(const ditango_shape_t* shape, size_t* o_bytes, size_t* lse_bytes) {
+  int32_t S = 0;
+  if (check_shape(shape, &S)) return 0;
+  const size_t rows = static_cast<size_t>(shape->H) * shape->P * S;
+  if (o_bytes) *o_bytes = rows * shape->d * sizeof(float);
+  if (lse_bytes) *lse_bytes = rows * sizeof(float);
+  ok();
+  return rows * (shape->d + 1) * sizeof(float);
+}
+
+int ditango_gstates_init(ditango_gstates_t* st, const ditango_shape_t* shape, int32_t g, float* const* O,
+                         float* const* LSE, int32_t* tc) {
+  if (!st) return fail(DITANGO_EINVAL, "states is NULL");
+  int32_t S = 0;
+  int rc = check_shape(shape, &S);
+  if (rc) return rc;
+  const int n = group_slots(shape->P, g);
+  if (!n) return fail(DITANGO_EINVAL, "group size g=%d invalid for P=%d (at most %d slots)", g, shape->P,
+                      DITANGO_MAX_SLOTS);
+  if (!tc) return fail(DITANGO_EINVAL, "tc is NULL");
+  if ((rc = check_slot_buffers(O, LSE, n))) return rc;
+  st->shape = *shape;
+  st->S = S;
+  st->g0 = st->g = g;
+  for (int s = 0; s < DITANGO_MAX_SLOTS; ++s) {
+    st->O[s] = s < n ? O[s] : nullptr;
+    st->LSE[s] = s < n ? LSE[s] : nullptr;
+  }
+  st->tc = tc;
+  for (int i = 0; i < shape->P * DITANGO_MAX_SLOTS; ++i) tc[i] = -1;
+  return ok();
+}
+
+int ditango_group_attn_partial(const void* Q, const void* K, const void* V, const uint8_t* mask,
+                               ditango_gstates_t* st, void* stream) {
+  int ns = 0;
+  int rc = check_gstates(st, &ns);
+  if (rc) return rc;
+  const int P = st->shape.P, g = st->g;
+  if ((rc = check_mask(mask, P))) return rc;
+  if (!Q || !K || !V) return fail(DITANGO_EINVAL, "Q, K and V must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(Q) | reinterpret_cast<uintptr_t>(K) | reinterpret_cast<uintptr_t>(V)) & 15u)
+    return fail(DITANGO_EINVAL, "Q, K and V must be 16-byte aligned");
+  for (int q = 0; q < P; ++q)
+    for (int s = 0; s < ns; ++s)
+      if (slot_live(P, g, q, s) && !slot_fresh(mask, P, g, q, s) && gtc(st, q, s) < 0)
+        return fail(DITANGO_ENOCACHE, "slot (q=%d, s=%d) is REUSE but was never computed", q, s);
+
+  ditango::PartialParams p;
+  std::memset(&p, 0, sizeof p);
+  // Items with the longest key ranges first (whole groups before the local
+  // pair and the group that lost q), so the longest blocks start first.
+  std::vector<std::pair<int64_t, int>> items;
+  for (int s = 0; s < ns; ++s)
+    for (int q = 0; q < P; ++q)
+      if (slot_live(P, g, q, s) && slot_fresh(mask, P, g, q, s))
+        items.push_back({-slot_keys(st->shape.N, P, st->S, g, q, s), (q << 6) | s});
+  if (items.empty()) return ok();
+  std::stable_sort(items.begin(), items.end(),
+                   [](const std::pair<int64_t, int>& x, const std::pair<int64_t, int>& y) { return x.first < y.first; });
+  for (size_t i = 0; i < items.size(); ++i) p.pairs[i] = static_cast<uint16_t>(items[i].second);
+  p.Q = static_cast<const __bf16*>(Q);
+  p.K = static_cast<const __bf16*>(K);
+  p.V = static_cast<const __bf16*>(V);
+  p.H = st->shape.H;
+  p.N = st->shape.N;
+  p.P = P;
+  p.S = st->S;
+  p.d = st->shape.d;
+  p.scale_log2 = st->shape.scale * 1.4426950408889634f;
+  p.n_pairs = static_cast<int32_t>(items.size());
+  p.grouped = 1;
+  p.g = g;
+  for (int s = 0; s < ns; ++s) {
+    p.gO[s] = st->O[s];
+    p.gLSE[s] = st->LSE[s];
+  }
+  const int rows = ditango::partial_rows_per_block(p.d, p.S);
+  p.q_tiles = (p.S + rows - 1) / rows;
+  const int64_t blocks = static_cast<int64_t>(p.H) * p.n_pairs * p.q_tiles;
+  if (blocks > 0x7fffffff) return fail(DITANGO_EINVAL, "grid of %lld blocks is too large", (long long)blocks);
+  p.n_blocks = static_cast<int32_t>(blocks);
+  hipError_t e = ditango::launch_partial(p, rows, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DITANGO_EHIP, "partial kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int ditango_group_cache_update(ditango_gstates_t* st, const uint8_t* mask, int32_t step, uint8_t* computed_out) {
+  int ns = 0;
+  int rc = check_gstates(st, &ns);
+  if (rc) return rc;
+  const int P = st->shape.P, g = st->g;
+  if ((rc = check_mask(mask, P))) return rc;
+  if (step < 0) return fail(DITANGO_EINVAL, "step=%d must be >= 0", step);
+  for (int q = 0; q < P; ++q)
+    for (int s = 0; s < ns; ++s) {
+      if (!slot_live(P, g, q, s)) continue;
+      if (gtc(st, q, s) > step)
+        return fail(DITANGO_EINVAL, "step=%d is earlier than slot (q=%d, s=%d)'s last computation step %d", step,
+                    q, s, gtc(st, q, s));
+      if (!slot_fresh(mask, P, g, q, s) && gtc(st, q, s) < 0)
+        return fail(DITANGO_EINVAL, "slot (q=%d, s=%d) reused but never computed", q, s);
+    }
+  for (int q = 0; q < P; ++q)
+    for (int s = 0; s < ns; ++s) {
+      const bool c = slot_live(P, g, q, s) && slot_fresh(mask, P, g, q, s);
+      if (c) gtc(st, q, s) = step;
+      if (computed_out) computed_out[q * ns + s] = c ? 1 : 0;
+    }
+  return ok();
+}
+
+int ditango_group_merge(const ditango_gstates_t* st, float* O, float* LSE, void* stream) {
+  int ns = 0;
+  int rc = check_gstates(st, &ns);
+  if (rc) return rc;
+  if (!O || !LSE) return fail(DITANGO_EINVAL, "O and LSE must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(O) | reinterpret_cast<uintptr_t>(LSE)) & 15u)
+    return fail(DITANGO_EINVAL, "O and LSE must be 16-byte aligned");
+  const int P = st->shape.P, g = st->g;
+  ditango::MergeParams m;
+  std::memset(&m, 0, sizeof m);
+  for (int q = 0; q < P; ++q)
+    for (int s = 0; s < ns; ++s)
+      if (slot_live(P, g, q, s)) {
+        if (gtc(st, q, s) < 0) return fail(DITANGO_ENOCACHE, "slot (q=%d, s=%d) holds no state", q, s);
+        m.live[q] |= 1u << s;
+      }
+  for (int s = 0; s < ns; ++s) {
+    m.in_O[s] = st->O[s];
+    m.in_L[s] = st->LSE[s];
+  }
+  m.out_hs = st->shape.N;
+  m.out_qs = st->S;
+  m.O = O;
+  m.LSE = LSE;
+  hipError_t e = launch_group_merge(m, st, ns, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DITANGO_EHIP, "merge kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int ditango_group_compose(ditango_gstates_t* st, int32_t k, void* stream) {
+  int ns = 0;
+  int rc = check_gstates(st, &ns);
+  if (rc) return rc;
+  if (k < 2) return fail(DITANGO_EINVAL, "merge factor k=%d must be >= 2", k);
+  const int P = st->shape.P, g = st->g;
+  if (static_cast<int64_t>(g) * k > DITANGO_MAX_P * 2)
+    return fail(DITANGO_EINVAL, "group size %d * %d is beyond any partition count", g, k);
+  const int g_new = g * k;
+  const int m_old = ns - 1, m_new = group_slots(P, g_new) - 1;
+  for (int q = 0; q < P; ++q)
+    for (int s = 0; s < ns; ++s)
+      if (slot_live(P, g, q, s) && gtc(st, q, s) < 0)
+        return fail(DITANGO_ENOCACHE, "slot (q=%d, s=%d) holds no state to merge", q, s);
+  std::vector<int> tc_new(static_cast<size_t>(P) * m_new, -1);
+  // New group i is written over slot 1 + i after every earlier launch has
+  // read that slot (stream order); group 0 reads and writes slot 1 element
+  // by element in the same thread.
+  for (int i = 0; i < m_new; ++i) {
+    const int j0 = k * i, j1 = std::min(k * i + k, m_old);
+    ditango::MergeParams m;
+    std::memset(&m, 0, sizeof m);
+    bool any = false;
+    for (int j = j0; j < j1; ++j) {
+      m.in_O[j - j0] = st->O[1 + j];
+      m.in_L[j - j0] = st->LSE[1 + j];
+    }
+    for (int q = 0; q < P; ++q) {
+      int t = -1;
+      for (int j = j0; j < j1; ++j)
+        if (slot_live(P, g, q, 1 + j)) {
+          m.live[q] |= 1u << (j - j0);
+          t = t < 0 ? gtc(st, q, 1 + j) : std::min(t, gtc(st, q, 1 + j));
+        }
+      tc_new[static_cast<size_t>(q) * m_new + i] = t;
+      any = any || m.live[q];
+    }
+    if (!any) continue;
+    m.out_hs = static_cast<int64_t>(P) * st->S;
+    m.out_qs = st->S;
+    m.O = st->O[1 + i];
+    m.LSE = st->LSE[1 + i];
+    hipError_t e = launch_group_merge(m, st, j1 - j0, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(DITANGO_EHIP, "group merge kernel launch: %s", hipGetErrorString(e));
+  }
+  for (int q = 0; q < P; ++q)
+    for (int s = 1; s < DITANGO_MAX_SLOTS; ++s)
+      gtc(st, q, s) = s <= m_new ? tc_new[static_cast<size_t>(q) * m_new + s - 1] : -1;
+  for (int s = 1 + m_new; s < DITANGO_MAX_SLOTS; ++s) {
+    st->O[s] = nullptr;
+    st->LSE[s] = nullptr;
+  }
+  st->g = g_new;
+  return ok();
+}
+
+int ditango_group_reset(ditango_gstates_t* st, float* const* O, float* const* LSE) {
+  if (!st) return fail(DITANGO_EINVAL, "states is NULL");
+  int32_t S = 0;
+  int rc = check_shape(&st->shape, &S);
+  if (rc) return rc;
+  const int n = group_slots(st->shape.P, st->g0);
+  if (!n || !st->tc) return fail(DITANGO_EINVAL, "states were not initialised");
+  if ((rc = check_slot_buffers(O, LSE, n))) return rc;
+  for (int s = 0; s < DITANGO_MAX_SLOTS; ++s) {
+    st->O[s] = s < n ? O[s] : nullptr;
+    st->LSE[s] = s < n ? LSE[s] : nullptr;
+  }
+  st->g = st->g0;
+  for (int i = 0; i < st->shape.P * DITANGO_MAX_SLOTS; ++i) st->tc[i] = -1;
   return ok();
 }
 

@@ -9,28 +9,51 @@
 
 namespace ditango {
 
-// Launch parameters of the fresh partial-attention kernel.  The fresh-pair
-// list travels in the kernel arguments (at most 32 x 32 pairs), so a launch
-// needs no device-side work list and no allocation.
+// Launch parameters of the fresh partial-attention kernel.  The work list
+// travels in the kernel arguments (at most 32 x 32 items), so a launch needs
+// no device-side work list and no allocation.
+//
+// Per-pair cache (grouped = 0): item = pair id q*P + k; the state goes to
+// slot h*P*P + item of O/LSE ([H][P*P][S][d]).
+// Grouped cache (grouped = 1): item = (q << 6) | s for slot s of query
+// partition q; the keys are those of the slot's members (slot 0: partition
+// q; slot 1 + j: group j of size g without q -- one contiguous range, or two
+// when q sits strictly inside the group); the state goes to gO[s] / gLSE[s]
+// at (h*P + q)*S.
 struct PartialParams {
   const __bf16* Q;          // [H][N][d]
   const __bf16* K;          // [H][N][d]
   const __bf16* V;          // [H][N][d]
-  float* O;                 // cache [H][P*P][S][d]
-  float* LSE;               // cache [H][P*P][S]
+  float* O;                 // per-pair cache [H][P*P][S][d]
+  float* LSE;               // per-pair cache [H][P*P][S]
   int32_t H, N, P, S, d;
   float scale_log2;         // scale * log2(e): scores in base-2 units
-  int32_t n_pairs;          // fresh pairs in `pairs`
+  int32_t n_pairs;          // work items in `pairs`
   int32_t q_tiles;          // query tiles per partition, ceil(S / rows per block)
   int32_t n_blocks;         // H * n_pairs * q_tiles
-  uint16_t pairs[DITANGO_MAX_P * DITANGO_MAX_P];  // pair ids q*P+k, grouped by k
+  int32_t grouped;          // 0: per-pair cache, 1: grouped cache
+  int32_t g;                // group size (grouped)
+  float* gO[DITANGO_MAX_SLOTS];    // grouped: slot buffers [H][P][S][d]
+  float* gLSE[DITANGO_MAX_SLOTS];  // grouped: [H][P][S]
+  uint16_t pairs[DITANGO_MAX_P * DITANGO_MAX_P];  // work items (see above)
 };
 
+// Composition (Eq. 4) of n_in states per row.  State k of the rows of
+// (head h, query partition q) starts at in_O[k] + (h*in_hs + q*in_qs)*S*d
+// (LSE: in_L[k] + (h*in_hs + q*in_qs)*S); it takes part when bit k of
+// live[q] is set.  Row r of (h, q) is written to O + (h*out_hs + q*out_qs
+// + r)*d and LSE + h*out_hs + q*out_qs + r.  A (h, q) with no live state is
+// skipped.  The row merge of both caches and the in-place group merge of
+// the grouped cache are instances.
 struct MergeParams {
-  const float* Os;          // cache [H][P*P][S][d]
-  const float* LSEs;        // cache [H][P*P][S]
-  float* O;                 // [H][N][d]
-  float* LSE;               // [H][N]
+  const float* in_O[DITANGO_MAX_SLOTS];
+  const float* in_L[DITANGO_MAX_SLOTS];
+  uint32_t live[DITANGO_MAX_P];
+  int64_t in_hs, in_qs;     // in units of S rows
+  int64_t out_hs, out_qs;   // in rows
+  float* O;
+  float* LSE;
+  int32_t n_in;             // <= DITANGO_MAX_SLOTS
   int32_t H, N, P, S, d;
 };
 

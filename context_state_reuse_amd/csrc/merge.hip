@@ -1,20 +1,27 @@
-// Composition of the P pair states of every row (DiTango page, Eq. 4, the
-// n-ary form of its associative and commutative state composition):
+// Composition of the states of every row (DiTango page, Eq. 4, the n-ary
+// form of its associative and commutative state composition):
 //   m = max_k LSE_k,  w_k = exp(LSE_k - m) / Z,  Z = sum_k exp(LSE_k - m)
 //   OUT = sum_k w_k OUT_k,  LSE = m + log Z
-// The P slots of a row mix states written this step (fresh) and states
-// written at earlier steps (reused); the merge does not distinguish them.
+// Instances: the row merge of the per-pair cache (the P pair states of a
+// row, fresh ones written this step and reused ones from earlier steps
+// alike), the row merge of the grouped cache (local slot plus group slots),
+// and the in-place merge of groups (Dynamic Group State Compose), whose
+// output is a group slot.  Where the states are and which take part come
+// from tables in the launch parameters.
 //
-// HBM-bound: per row and head it reads P*(d+1) floats and writes d+1.
+// HBM-bound: per row and head it reads n*(d+1) floats and writes d+1.
 // A block owns R consecutive rows of one query partition of one head.
-//   1. one lane per (row, slot) loads LSE_k, the row's lanes reduce max and
+//   1. one lane per (row, state) loads LSE_k, the row's lanes reduce max and
 //      sum with cross-lane shuffles, and the normalised weights go to LDS;
-//   2. for every slot k the block streams the R*d contiguous floats of rows
-//      [i0, i0+R) of slot (q, k) with 16-byte loads -- all P slots' loads are
-//      issued before the first is used, about 32 per thread -- and
-//      accumulates w_k * OUT_k in registers;
+//   2. for every state k the block streams the R*d contiguous floats of its
+//      rows with 16-byte loads -- all states' loads are issued before the
+//      first is used, about 32 per thread -- and accumulates w_k * OUT_k in
+//      registers;
 //   3. the R*d outputs are written contiguously.
-// R = 256 / PMAX keeps 32 independent loads in flight per thread at every P.
+// R = 256 / PMAX keeps 32 independent loads in flight per thread at every
+// state count.  Each output element is written by the thread that read that
+// element of every input, after reading it, so an output may overwrite the
+// rows of one of its inputs (the in-place group merge).
 
 #include <hip/hip_runtime.h>
 
@@ -49,7 +56,7 @@ __device__ inline void store_stream(float* p, f32x4 v) {
 template <int D, int PMAX>
 __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p, int row_tiles) {
   constexpr int R = kThreads / PMAX;                  // rows per block
-  constexpr int CH = R * D / 4;                       // float4 chunks per slot block
+  constexpr int CH = R * D / 4;                       // float4 chunks per state block
   constexpr int PER = (CH + kThreads - 1) / kThreads; // chunks per thread
   __shared__ float w_lds[R][PMAX];
 
@@ -58,31 +65,32 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p, in
   const int hq = blockIdx.x / row_tiles;              // h * P + q
   const int q = hq % p.P;
   const int h = hq / p.P;
+  const uint32_t live = p.live[q];
   const int len_q = min(p.S, p.N - q * p.S);
   const int i0 = rt * R;
   const int rows = min(R, len_q - i0);
-  const size_t slot0 = static_cast<size_t>(hq) * p.P;  // slot of pair (q, 0) of head h
+  if (live == 0 || rows <= 0) return;                 // block-uniform
+  const int64_t in_row0 = (h * p.in_hs + q * p.in_qs) * p.S + i0;
+  const int64_t out_row0 = h * p.out_hs + q * p.out_qs + i0;
 
   // 1. weights
   {
     const int r = tid / PMAX, k = tid % PMAX;
-    const bool live = k < p.P && r < rows;
-    float l = live ? p.LSEs[(slot0 + k) * p.S + i0 + r] : -__builtin_inff();
+    const bool lv = k < p.n_in && ((live >> k) & 1u) && r < rows;
+    float l = lv ? p.in_L[k][in_row0 + r] : -__builtin_inff();
     float m = l;
 #pragma unroll
     for (int off = 1; off < PMAX; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
-    const float e = live ? __builtin_amdgcn_exp2f((l - m) * 1.4426950408889634f) : 0.0f;
+    const float e = lv ? __builtin_amdgcn_exp2f((l - m) * 1.4426950408889634f) : 0.0f;
     float z = e;
 #pragma unroll
     for (int off = 1; off < PMAX; off <<= 1) z += __shfl_xor(z, off);
     w_lds[r][k] = e / z;
-    if (k == 0 && r < rows)
-      p.LSE[static_cast<size_t>(h) * p.N + q * p.S + i0 + r] =
-          m + __builtin_amdgcn_logf(z) * 0.69314718055994531f;
+    if (k == 0 && r < rows) p.LSE[out_row0 + r] = m + __builtin_amdgcn_logf(z) * 0.69314718055994531f;
   }
   __syncthreads();
 
-  // 2. stream the slots
+  // 2. stream the states
   const int valid = rows * (D / 4);
   f32x4 acc[PER];
   f32x4 o[PMAX][PER];
@@ -90,8 +98,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p, in
   for (int j = 0; j < PER; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < PMAX; ++k) {
-    if (k < p.P) {
-      const float* src = p.Os + ((slot0 + k) * p.S + i0) * D;
+    if (k < p.n_in && ((live >> k) & 1u)) {
+      const float* src = p.in_O[k] + in_row0 * D;
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         const int c = tid + j * kThreads;
@@ -101,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p, in
   }
 #pragma unroll
   for (int k = 0; k < PMAX; ++k) {
-    if (k < p.P) {
+    if (k < p.n_in && ((live >> k) & 1u)) {
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         const int c = tid + j * kThreads;
@@ -111,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p, in
   }
 
   // 3. write
-  float* dst = p.O + (static_cast<size_t>(h) * p.N + q * p.S + i0) * D;
+  float* dst = p.O + out_row0 * D;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int c = tid + j * kThreads;
@@ -132,15 +140,16 @@ hipError_t launch(const MergeParams& p, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_d(const MergeParams& p, hipStream_t stream) {
-  if (p.P <= 4) return launch<D, 4>(p, stream);
-  if (p.P <= 8) return launch<D, 8>(p, stream);
-  if (p.P <= 16) return launch<D, 16>(p, stream);
+  if (p.n_in <= 4) return launch<D, 4>(p, stream);
+  if (p.n_in <= 8) return launch<D, 8>(p, stream);
+  if (p.n_in <= 16) return launch<D, 16>(p, stream);
   return launch<D, 32>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
+  if (p.n_in < 1 || p.n_in > 32) return hipErrorInvalidValue;
   switch (p.d) {
     case 64: return launch_d<64>(p, stream);
     case 72: return launch_d<72>(p, stream);

@@ -327,7 +327,7 @@ __device__ __attribute__((always_inline)) inline void tile_pv(WaveState<D, NQT, 
 template <int D, int NQT>
 constexpr int waves_per_simd() { return NQT == 2 ? 1 : 2; }
 
-template <int D, int WAVES, int NQT, int SCHED, int BC>
+template <int D, int WAVES, int NQT, int SCHED, int BC, bool GROUPED>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
                           amdgpu_waves_per_eu(waves_per_simd<D, NQT>(), waves_per_simd<D, NQT>())))
 void partial_kernel(const PartialParams p) {
@@ -366,11 +366,47 @@ void partial_kernel(const PartialParams p) {
   const int rest = item / p.q_tiles;
   const int pi = rest % p.n_pairs;
   const int h = rest / p.n_pairs;
-  const int pair = p.pairs[pi];
-  const int qp = pair / p.P, kp = pair - qp * p.P;
-  const int q0 = qp * p.S, k0 = kp * p.S;
+  const int it = p.pairs[pi];
+  // Keys of the item: the concatenated key index j < len_k lives at token
+  // k0 + j, or k0 + j + S once j >= len0 (a gap over query partition q when
+  // it sits strictly inside a group; len0 = len_k otherwise).
+  int qp, k0, len_k, len0;
+  float* obase;   // OUT row 0 of this item's state
+  float* lbase;   // LSE row 0
+  if constexpr (!GROUPED) {
+    qp = it / p.P;
+    const int kp = it - qp * p.P;
+    k0 = kp * p.S;
+    len_k = min(p.S, p.N - k0);
+    len0 = len_k;
+    const size_t slot = static_cast<size_t>(h) * p.P * p.P + it;
+    obase = p.O + slot * p.S * D;
+    lbase = p.LSE + slot * p.S;
+  } else {
+    qp = it >> 6;
+    const int s = it & 63;
+    const int a = s == 0 ? qp : (s - 1) * p.g;                 // member partitions [a, b)
+    const int b = s == 0 ? qp + 1 : min(a + p.g, p.P);
+    int kb = a * p.S, ke = min(b * p.S, p.N);
+    len0 = -1;
+    if (s != 0 && a <= qp && qp < b) {                          // the group holds q: leave it out
+      if (qp == a) {
+        kb = (a + 1) * p.S;
+      } else if (qp == b - 1) {
+        ke = qp * p.S;
+      } else {
+        len0 = qp * p.S - kb;                                   // q is interior, so its partition is full
+      }
+    }
+    k0 = kb;
+    len_k = ke - kb - (len0 >= 0 ? p.S : 0);
+    if (len0 < 0) len0 = len_k;
+    const size_t row0 = (static_cast<size_t>(h) * p.P + qp) * p.S;
+    obase = p.gO[s] + row0 * D;
+    lbase = p.gLSE[s] + row0;
+  }
+  const int q0 = qp * p.S;
   const int len_q = min(p.S, p.N - q0);
-  const int len_k = min(p.S, p.N - k0);
   const size_t head = static_cast<size_t>(h) * p.N * D;
   const __bf16* Qh = p.Q + head + static_cast<size_t>(q0) * D;
   const __bf16* Kh = p.K + head + static_cast<size_t>(k0) * D;
@@ -461,15 +497,31 @@ void partial_kernel(const PartialParams p) {
     vrow_of[i] = r;
     vgoff[i] = pos < D / 8 ? r * D + ((pos ^ G::vswz(r)) << 3) : -1;   // -1: spare chunk, not loaded
   }
+  // Global source of LDS row r of key tile kt (element offset `goff` of
+  // that row): the tile's first token is a scalar unless the tile runs past
+  // the last key (rows there repeat the last key) or straddles the gap;
+  // those tiles map each row on its own.
+  auto tile_src = [&](const __bf16* base, int kt, int r, int goff) __attribute__((always_inline)) {
+    const int t0 = kt * kBc;
+    if constexpr (!GROUPED) {
+      if (t0 + kBc > len_k && t0 + r >= len_k) return base + static_cast<size_t>(len_k - 1 - r) * D + goff;
+      return base + static_cast<size_t>(t0) * D + goff;
+    } else {
+      if (t0 + kBc <= len_k && (t0 + kBc <= len0 || t0 >= len0)) {
+        return base + static_cast<size_t>(t0 + (t0 >= len0 ? p.S : 0)) * D + goff;
+      }
+      int j = min(t0 + r, len_k - 1);
+      j += j >= len0 ? p.S : 0;
+      return base + static_cast<size_t>(j) * D + (goff - r * D);
+    }
+  };
   auto gload_direct = [&](int kt_k, __bf16* kdst, int kt_v, __bf16* vdst) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < (G::direct ? kRoundsK : 0); ++i) {
       if (kGroupsK % WAVES != 0 && i * WAVES + swave >= kGroupsK) break;   // wave-uniform
       const int lds_elem0 = (i * WAVES + swave) * 64 * 8;   // first element this wave writes
       if (kt_k >= 0) {
-        const __bf16* src = Kh + static_cast<size_t>(kt_k) * kBc * D + kgoff[i];
-        if (kt_k * kBc + kBc > len_k && kt_k * kBc + krow_of[i] >= len_k)   // past a ragged end: repeat the last row
-          src = Kh + static_cast<size_t>(len_k - 1 - krow_of[i]) * D + kgoff[i];
+        const __bf16* src = tile_src(Kh, kt_k, krow_of[i], kgoff[i]);
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                          (__attribute__((address_space(3))) void*)(kdst + lds_elem0), 16, 0, 0);
       }
@@ -479,9 +531,7 @@ void partial_kernel(const PartialParams p) {
       if (kGroupsV % WAVES != 0 && i * WAVES + swave >= kGroupsV) break;   // wave-uniform
       const int lds_elem0 = (i * WAVES + swave) * 64 * 8;
       if (kt_v >= 0 && (G::vcpr == D / 8 || vgoff[i] >= 0)) {
-        const __bf16* src = Vh + static_cast<size_t>(kt_v) * kBc * D + vgoff[i];
-        if (kt_v * kBc + kBc > len_k && kt_v * kBc + vrow_of[i] >= len_k)
-          src = Vh + static_cast<size_t>(len_k - 1 - vrow_of[i]) * D + vgoff[i];
+        const __bf16* src = tile_src(Vh, kt_v, vrow_of[i], vgoff[i]);
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                          (__attribute__((address_space(3))) void*)(vdst + lds_elem0), 16, 0, 0);
       }
@@ -498,11 +548,13 @@ void partial_kernel(const PartialParams p) {
         if (c < kBc * G::chunks) {
           const int key = c / G::chunks, ch = c % G::chunks;
           if (kt_k >= 0) {
-            const int krow = min(kt_k * kBc + key, len_k - 1);
+            int krow = min(kt_k * kBc + key, len_k - 1);
+            if constexpr (GROUPED) krow += krow >= len0 ? p.S : 0;
             kreg[i] = *reinterpret_cast<const u32x4*>(Kh + static_cast<size_t>(krow) * D + ch * 8);
           }
           if (kt_v >= 0) {
-            const int vrow = min(kt_v * kBc + key, len_k - 1);
+            int vrow = min(kt_v * kBc + key, len_k - 1);
+            if constexpr (GROUPED) vrow += vrow >= len0 ? p.S : 0;
             vreg[i] = *reinterpret_cast<const u32x4*>(Vh + static_cast<size_t>(vrow) * D + ch * 8);
           }
         }
@@ -633,7 +685,6 @@ void partial_kernel(const PartialParams p) {
   }
 
   // Epilogue: OUT = O / l_rounded, LSE = ln2 * (m + log2 l), into the slot.
-  const size_t slot = static_cast<size_t>(h) * p.P * p.P + pair;
 #pragma unroll
   for (int c = 0; c < NQT; ++c) {
     const float l_tot = w.l_run[c] + xor32(w.l_run[c]);
@@ -649,7 +700,7 @@ void partial_kernel(const PartialParams p) {
     const float inv = 1.0f / lr_tot;
     const int row = row0 + 32 * c;
     if (row < len_q) {
-      float* orow = p.O + (slot * p.S + row) * D;
+      float* orow = obase + static_cast<size_t>(row) * D;
 #pragma unroll
       for (int v = 0; v < G::vTiles; ++v)
 #pragma unroll
@@ -661,7 +712,7 @@ void partial_kernel(const PartialParams p) {
             *reinterpret_cast<f32x4*>(orow + dim) = o;
           }
         }
-      if (hw == 0) p.LSE[slot * p.S + row] = (w.m_run[c] + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+      if (hw == 0) lbase[row] = (w.m_run[c] + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
     }
   }
 }
@@ -687,8 +738,13 @@ hipError_t launch(PartialParams& p, hipStream_t stream) {
   constexpr int sched = DITANGO_SCHED >= 0 ? DITANGO_SCHED : (D == 72 ? 2 : 0);
   constexpr int bc = DITANGO_BC;
   static_assert(sched == 0 || sched == 2, "loop schedules: 0 (plain) or 2 (software-pipelined)");
-  hipLaunchKernelGGL((partial_kernel<D, WAVES, NQT, sched, bc>), dim3(p.n_blocks), dim3(64 * WAVES), 0,
-                     stream, p);
+  if (p.grouped) {
+    hipLaunchKernelGGL((partial_kernel<D, WAVES, NQT, sched, bc, true>), dim3(p.n_blocks), dim3(64 * WAVES), 0,
+                       stream, p);
+  } else {
+    hipLaunchKernelGGL((partial_kernel<D, WAVES, NQT, sched, bc, false>), dim3(p.n_blocks), dim3(64 * WAVES), 0,
+                       stream, p);
+  }
   return hipGetLastError();
 }
 

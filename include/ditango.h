@@ -134,10 +134,96 @@ int ditango_state_merge(const ditango_states_t* st, float* O, float* LSE, void* 
 #define DITANGO_MASK_RANDOM  4
 int ditango_mask_build(int32_t policy, int32_t P, int32_t n, uint64_t seed, uint8_t* mask_out);
 
+/* ---------------------------------------------------------------------
+ * Grouped, composed state cache (state-selection section: the p partition
+ * states are grouped into groups of g adjacent partitions, the group that
+ * holds the local state keeping g - 1; selective compute and reuse, Fig. 6:
+ * the remote states are composed and the composite is cached; ring-based
+ * composed attention: a fresh group state is the composition of its
+ * members' partial states; Dynamic Group State Compose: groups are merged k
+ * at a time when memory runs short, and an anchor step returns to g).
+ *
+ * Groups are fixed and contiguous: G_j = {j g, ..., min((j+1) g, P) - 1},
+ * j < m = ceil(P/g).  Query partition q owns 1 + m slots:
+ *   slot 0      the local pair (q, q)
+ *   slot 1 + j  the composed state of G_j without q (empty, and never read
+ *               or written, when G_j = {q})
+ * Per step a slot is COMPUTE when any of its members is marked fresh in the
+ * pair mask [P][P] (the local slot follows mask[q][q]), else REUSE.  A fresh
+ * group state is computed in one pass over the keys of all its members,
+ * which is their composition (Eq. 4) up to rounding.  The row merge composes
+ * the non-empty slots.  Slot buffers are separate so that slots released by
+ * a group merge can be freed:
+ *   O[s]   device fp32 [H][P][S][d]   row r of (h, q) = query row q*S + r
+ *   LSE[s] device fp32 [H][P][S]
+ *   tc     host int32 [P][DITANGO_MAX_SLOTS]; tc[q][s] = last step slot s of
+ *          q was computed (-1: never); entries of empty slots stay -1.
+ * 1 + ceil(P/g) must not exceed DITANGO_MAX_SLOTS (g = 1 needs P <= 31).
+ * --------------------------------------------------------------------- */
+#define DITANGO_MAX_SLOTS 32
+
+typedef struct {
+  ditango_shape_t shape;
+  int32_t  S;                      /* ceil(N/P), set by ditango_gstates_init  */
+  int32_t  g0;                     /* group size at init and after a reset    */
+  int32_t  g;                      /* current group size, g0 * (merge factors) */
+  float*   O[DITANGO_MAX_SLOTS];   /* slot buffers; NULL beyond the used slots */
+  float*   LSE[DITANGO_MAX_SLOTS];
+  int32_t* tc;
+} ditango_gstates_t;
+
+/* Slots per query partition for group size g: 1 + ceil(P/g), or 0 if P or g
+ * is out of range or the count exceeds DITANGO_MAX_SLOTS. */
+int32_t ditango_group_slots(int32_t P, int32_t g);
+
+/* Device bytes of ONE slot buffer for `shape`: *o_bytes for O[s] and
+ * *lse_bytes for LSE[s] (either may be NULL).  Returns their sum, 0 if the
+ * shape is invalid. */
+size_t ditango_gstates_slot_bytes(const ditango_shape_t* shape, size_t* o_bytes, size_t* lse_bytes);
+
+/* Bind ditango_group_slots(P, g) caller-owned slot buffers (16-byte aligned,
+ * sizes above) and a host tc array of P * DITANGO_MAX_SLOTS int32; marks
+ * every slot empty (tc = -1).  Errors: EINVAL. */
+int ditango_gstates_init(ditango_gstates_t* st, const ditango_shape_t* shape, int32_t g,
+                         float* const* O, float* const* LSE, int32_t* tc);
+
+/* Fresh partial attention for every COMPUTE slot (see above) on every head,
+ * written over the slot.  REUSE slots are not touched and get no work.
+ * Checks first that every non-empty REUSE slot holds a state, else
+ * DITANGO_ENOCACHE.  Does not change tc.  Errors: EINVAL, ENOCACHE, EHIP. */
+int ditango_group_attn_partial(const void* Q, const void* K, const void* V, const uint8_t* mask,
+                               ditango_gstates_t* st, void* stream);
+
+/* Commit step `step` (host only): tc[q][s] = step for every COMPUTE slot.
+ * If computed_out is not NULL it receives uint8 [P][ditango_group_slots(P, g)]
+ * with 1 exactly at the COMPUTE slots (empty slots 0).  Errors: EINVAL (step
+ * < 0, below an existing tc, or a REUSE slot that was never computed). */
+int ditango_group_cache_update(ditango_gstates_t* st, const uint8_t* mask, int32_t step,
+                               uint8_t* computed_out);
+
+/* Compose (Eq. 4) the non-empty slots of every row into O device fp32
+ * [H][N][d] and LSE device fp32 [H][N].  Every non-empty slot must hold a
+ * state, else DITANGO_ENOCACHE.  Errors: EINVAL, ENOCACHE, EHIP. */
+int ditango_group_merge(const ditango_gstates_t* st, float* O, float* LSE, void* stream);
+
+/* Dynamic Group State Compose: group size g -> k*g, in place.  New group i
+ * covers old groups k*i .. k*i+k-1; its state is their composition (Eq. 4,
+ * empty ones skipped) written over old slot 1 + i, and its tc is the oldest
+ * of theirs.  Slots >= ditango_group_slots(P, k*g) are released: their
+ * pointers in `st` become NULL and the caller may free those buffers once
+ * the stream has passed this call.  Every non-empty slot must hold a state,
+ * else DITANGO_ENOCACHE; k >= 2.  Errors: EINVAL, ENOCACHE, EHIP. */
+int ditango_group_compose(ditango_gstates_t* st, int32_t k, void* stream);
+
+/* Return to the original group size g0 before an anchor step: binds
+ * ditango_group_slots(P, g0) slot buffers (kept ones may be passed again)
+ * and marks every slot empty.  Errors: EINVAL. */
+int ditango_group_reset(ditango_gstates_t* st, float* const* O, float* const* LSE);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* ditango_last_error(void);
 
-/* Library ABI version (this header: 1). */
+/* Library ABI version (this header: 2). */
 int32_t ditango_version(void);
 
 #ifdef __cplusplus

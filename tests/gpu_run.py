@@ -49,3 +49,39 @@ def run_steps(w, masks=None, steps=None, on_step=None, label=""):
             on_step(t, mask, reused, cache, O, LSE)
         del Q, K, V
     return cache
+
+
+def run_group_steps(w, g, masks=None, steps=None, compose_at=None, on_step=None, label=""):
+    """Run the grouped-cache path of the library over the steps of workload w.
+
+    compose_at: optional {t: k}: merge groups by k right before step t.
+    on_step(t, mask, computed, cache, O, LSE) is called after each step.
+    """
+    import torch
+
+    import context_state_reuse_amd as lib
+
+    n = w.steps if steps is None else steps
+    cache = lib.GroupedStateCache(w.H, w.N, w.d, w.P, g)
+    stream = synth.InputStream(w)
+    O = torch.empty((w.H, w.N, w.d), dtype=torch.float32, device="cuda")
+    LSE = torch.empty((w.H, w.N), dtype=torch.float32, device="cuda")
+    for t in range(n):
+        t0 = time.time()
+        qb, kb, vb = stream.next()
+        Q, K, V = to_device(qb), to_device(kb), to_device(vb)
+        del qb, kb, vb
+        if compose_at and t in compose_at:
+            cache.compose(compose_at[t])
+            log(f"  [{label or w.name}] before step {t}: groups merged to g={cache.g}, {cache.n_slots} slots")
+        mask = lib.workload_mask(w, t) if masks is None or t not in masks else np.asarray(masks[t], np.uint8)
+        lib.ditango_group_attn_partial(Q, K, V, mask, cache)
+        computed = lib.ditango_group_cache_update(cache, mask, t)
+        lib.ditango_group_merge(cache, O, LSE)
+        torch.cuda.synchronize()
+        log(f"  [{label or w.name}] step {t}: g={cache.g}, {int(computed.sum())} slots computed, "
+            f"{time.time() - t0:.1f}s")
+        if on_step is not None:
+            on_step(t, mask, computed, cache, O, LSE)
+        del Q, K, V
+    return cache
