@@ -68,6 +68,31 @@ def group_decisions(mask: np.ndarray, g: int) -> np.ndarray:
     return out
 
 
+def nearest_groups_mask(P: int, g: int, n: int) -> np.ndarray:
+    """Locality selection at group granularity: per query partition q the
+    local pair plus the n groups nearest to q, a group's distance being that
+    of its closest member other than q, ties to the lower group index.
+
+    The page selects per group (state-selection section) and motivates the
+    grouping by the spatial locality of Fig. 5a; this is the fixed-policy
+    counterpart of the per-pair nearest-n masks (its planner is not built).
+    """
+    if n < 0:
+        raise ValueError("n must be >= 0")
+    m = np.zeros((P, P), dtype=np.uint8)
+    for q in range(P):
+        m[q, q] = 1
+        cands = []
+        for j in range(n_groups(P, g)):
+            mem = slot_members(P, g, q, 1 + j)
+            if mem:
+                cands.append((min(abs(q - k) for k in mem), j, mem))
+        cands.sort(key=lambda c: (c[0], c[1]))
+        for _, _, mem in cands[:n]:
+            m[q, mem] = 1
+    return m
+
+
 class GroupedStateReuseOracle:
     """Selective compute and reuse with one cached state per (query partition, slot)."""
 

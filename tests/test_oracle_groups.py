@@ -17,7 +17,7 @@ import pytest
 
 import synth
 from oracle.groups import (GroupedStateReuseOracle, group_decisions, n_slots,
-                           slot_members)
+                           nearest_groups_mask, slot_members)
 from oracle.masks import all_fresh, all_reuse, radius_mask
 from oracle.reuse import ReuseError, StateReuseOracle
 from oracle.state import compose, compose2, partial_state, partition_bounds
@@ -201,3 +201,39 @@ def test_reuse_without_state_and_reset():
     orc.compose_groups(2)
     orc.reset()
     assert orc.g == 2 and np.all(orc.tc == -1) and orc.tc.shape == (w.P, n_slots(w.P, 2))
+
+
+def test_nearest_groups_mask_example():
+    """P = 8, g = 2 (groups {0,1} {2,3} {4,5} {6,7}), two nearest groups, by hand:
+    q=0: {1} at 1, {2,3} at 2 -> 0,1,2,3;  q=3: {2} at 1, {4,5} at 1 -> 2,3,4,5;
+    q=4: {2,3} at 1 (lower index wins the tie with {5}), {5} at 1 -> 2,3,4,5;
+    q=7: {6} at 1, {4,5} at 2 -> 4,5,6,7."""
+    m = nearest_groups_mask(8, 2, 2)
+    assert list(np.flatnonzero(m[0])) == [0, 1, 2, 3]
+    assert list(np.flatnonzero(m[3])) == [2, 3, 4, 5]
+    assert list(np.flatnonzero(m[4])) == [2, 3, 4, 5]
+    assert list(np.flatnonzero(m[7])) == [4, 5, 6, 7]
+    # P = 5, g = 2, one group: q = 4 (its own group {4} is empty) takes {2, 3}
+    m = nearest_groups_mask(5, 2, 1)
+    assert list(np.flatnonzero(m[4])) == [2, 3, 4] and list(np.flatnonzero(m[0])) == [0, 1]
+    assert np.array_equal(nearest_groups_mask(6, 3, 0), np.eye(6, dtype=np.uint8))
+    # P = 8, g = 4, one group: for q = 4 both {0..3} and {5,6,7} are at distance 1
+    # (their closest members 3 and 5); the lower group wins
+    assert list(np.flatnonzero(nearest_groups_mask(8, 4, 1)[4])) == [0, 1, 2, 3, 4]
+
+
+@pytest.mark.parametrize("P,g,n", [(32, 4, 2), (16, 4, 1), (8, 2, 1), (13, 3, 2), (32, 8, 3), (7, 7, 1)])
+def test_nearest_groups_mask_is_group_aligned(P, g, n):
+    """Every group is wholly fresh or wholly reused, and each row keeps q plus
+    the members of exactly min(n, non-empty groups) groups."""
+    m = nearest_groups_mask(P, g, n)
+    for q in range(P):
+        assert m[q, q] == 1
+        chosen = 0
+        for s in range(1, n_slots(P, g)):
+            mem = slot_members(P, g, q, s)
+            vals = {int(m[q, k]) for k in mem}
+            assert len(vals) <= 1
+            chosen += vals == {1}
+        live = sum(1 for s in range(1, n_slots(P, g)) if slot_members(P, g, q, s))
+        assert chosen == min(n, live)
