@@ -46,6 +46,13 @@ def parse():
     ap.add_argument("--cpu-steps", type=int, default=0, help="timed steady-state steps of the oracle (0: auto)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--group", type=int, default=0,
+                    help="run the grouped, composed state cache with this group size (0: per-pair cache)")
+    ap.add_argument("--compose", type=int, default=0,
+                    help="with --group: after the timed steps, time one merge of groups by this factor")
+    ap.add_argument("--group-masks", choices=("nearest", "workload"), default="nearest",
+                    help="with --group: group-aligned masks (local pair plus the nearest groups, as many "
+                         "fresh partitions per row as the workload's masks) or the workload's own pair masks")
     return ap.parse_args()
 
 
@@ -63,6 +70,20 @@ def merge_bytes(w) -> float:
 def state_store_bytes(w, mask) -> float:
     lens = np.array([min(w.S, w.N - p * w.S) for p in range(w.P)], dtype=np.float64)
     return float(w.H * (w.d + 1) * 4 * (lens[:, None] * mask).sum())
+
+
+def group_work(w, g, computed):
+    """Fresh FLOPs (4 * len_q * keys * d per computed slot and head) and
+    merge bytes (live slots' d+1 floats read plus d+1 written per row and
+    head) of one grouped step."""
+    from context_state_reuse_amd import group_slot_keys, group_slot_live
+    lens = [min(w.S, w.N - q * w.S) for q in range(w.P)]
+    ns = computed.shape[1]
+    flops = sum(4.0 * w.d * w.H * lens[q] * group_slot_keys(w.N, w.P, g, q, s)
+                for q in range(w.P) for s in range(ns) if computed[q, s])
+    live = [sum(1 for s in range(ns) if group_slot_live(w.P, g, q, s)) for q in range(w.P)]
+    mbytes = sum(4.0 * w.H * lens[q] * (w.d + 1) * (live[q] + 1) for q in range(w.P))
+    return flops, mbytes
 
 
 def source_hash(*names) -> str:
@@ -153,22 +174,46 @@ def main():
         bits = stream.next()
         qkv.append(tuple(torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev) for b in bits))
     del stream
-    cache = lib.StateCache(w.H, w.N, w.d, w.P)
+    g = args.group
+    if g:
+        cache = lib.GroupedStateCache(w.H, w.N, w.d, w.P, g)
+        cache_bytes = cache.device_bytes
+    else:
+        cache = lib.StateCache(w.H, w.N, w.d, w.P)
+        cache_bytes = sum(lib.ditango_states_bytes(cache.shape))
     O = torch.empty((w.H, w.N, w.d), dtype=torch.float32, device=dev)
     LSE = torch.empty((w.H, w.N), dtype=torch.float32, device=dev)
 
     step_no = [0]
+    computed_log = []
+    n_groups = max(1, round(w.n_fresh / g)) if g else 0
+    if g and args.group_masks == "nearest":
+        gmask = lib.ditango_group_mask_build(w.P, g, n_groups)
+        mask_of = lambda t: lib.ditango_mask_build("all", w.P) if t == 0 else gmask
+        mask_desc = f"local pair + {n_groups} nearest group(s) of {g}"
+    else:
+        mask_of = lambda t: lib.workload_mask(w, t)
+        mask_desc = f"{w.policy}-{w.n_fresh}"
 
     def step(t: int, events=None):
-        mask = lib.workload_mask(w, t)
+        mask = mask_of(t)
         Q, K, V = qkv[t]
         if events is not None:
             events[0].record()
-        lib.ditango_attn_partial(Q, K, V, mask, cache)
+        if g:
+            lib.ditango_group_attn_partial(Q, K, V, mask, cache)
+        else:
+            lib.ditango_attn_partial(Q, K, V, mask, cache)
         if events is not None:
             events[1].record()
-        lib.ditango_state_cache_update(cache, mask, step_no[0])
-        lib.ditango_state_merge(cache, O, LSE)
+        if g:
+            computed = lib.ditango_group_cache_update(cache, mask, step_no[0])
+            lib.ditango_group_merge(cache, O, LSE)
+            if events is not None:
+                computed_log.append(computed)
+        else:
+            lib.ditango_state_cache_update(cache, mask, step_no[0])
+            lib.ditango_state_merge(cache, O, LSE)
         if events is not None:
             events[2].record()
         step_no[0] += 1
@@ -204,26 +249,63 @@ def main():
     t_merge = np.mean([e[1].elapsed_time(e[2]) for e in evs])
     dense = 4.0 * w.N * w.N * w.d * w.H
     value = dense / (ms_step * 1e-3) / 1e12
-    fresh = np.mean([fresh_flops(w, m) for m in masks])
-    reuse = 1.0 - np.mean([m.mean() for m in masks])
-    mb = merge_bytes(w)
-    sb = np.mean([state_store_bytes(w, m) for m in masks])
+    if g:
+        work = [group_work(w, g, c) for c in computed_log]
+        fresh = np.mean([f for f, _ in work])
+        mb = np.mean([b for _, b in work])
+        lens = np.array([min(w.S, w.N - p * w.S) for p in range(w.P)], dtype=np.float64)
+        sb = np.mean([w.H * (w.d + 1) * 4 * (lens[:, None] * c).sum() for c in computed_log])
+        reuse = 1.0 - np.mean([c.sum() / sum(lib.group_slot_live(w.P, g, q, s) for q in range(w.P)
+                                              for s in range(c.shape[1])) for c in computed_log])
+    else:
+        fresh = np.mean([fresh_flops(w, m) for m in masks])
+        reuse = 1.0 - np.mean([m.mean() for m in masks])
+        mb = merge_bytes(w)
+        sb = np.mean([state_store_bytes(w, m) for m in masks])
 
     partial_tflops = fresh / (t_partial * 1e-3) / 1e12
     merge_gbs = mb / (t_merge * 1e-3) / 1e9
     src = source_hash("partial.hip")
+    cache_desc = (f"grouped, g={g}: {cache.n_slots} slots per query partition" if g
+                  else "per pair: P slots per query partition")
+    compose_rec = None
+    if g and args.compose:
+        # one in-place merge of groups by args.compose; bytes: every live old
+        # group state read once, every new group state written once
+        k = args.compose
+        lens = [min(w.S, w.N - q * w.S) for q in range(w.P)]
+        m_old, g_new = cache.n_slots - 1, g * k
+        m_new = lib.ditango_group_slots(w.P, g_new) - 1
+        cbytes = 0.0
+        for q in range(w.P):
+            for i in range(m_new):
+                parts = sum(lib.group_slot_live(w.P, g, q, 1 + j) for j in range(k * i, min(k * i + k, m_old)))
+                cbytes += (parts + (1 if parts else 0)) * 4.0 * w.H * lens[q] * (w.d + 1)
+        before = cache.device_bytes
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        cache.compose(k, after=ev[1].record)
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1])
+        compose_rec = {"factor": k, "group_size_from": g, "group_size_to": g_new, "ms": round(ms, 4),
+                       "bytes": cbytes, "gbs": round(cbytes / (ms * 1e-3) / 1e9, 1),
+                       "cache_bytes_before": before, "cache_bytes_after": cache.device_bytes}
+
     if t_partial >= t_merge:
         roof = {"kernel": "partial_kernel", "bound": "mfma", "achieved": round(partial_tflops, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(partial_tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": stored_traffic("partial", w.name, src),
+                "traffic": None if g else stored_traffic("partial", w.name, src),
                 "avg_launch_ms": round(float(t_partial), 4),
-                "algorithmic_per_launch": f"{fresh:.4e} FLOP (4*len_q*len_k*d per fresh pair and head)"}
+                "algorithmic_per_launch": f"{fresh:.4e} FLOP (4*len_q*len_k*d per fresh "
+                                          f"{'slot, len_k = keys of its members' if g else 'pair'} and head)"}
     else:
         roof = {"kernel": "merge_kernel", "bound": "hbm", "achieved": round(merge_gbs, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(merge_gbs / PEAK_HBM_GBS, 4),
-                "traffic": stored_traffic("merge", w.name, source_hash("merge.hip")),
+                "traffic": None if g else stored_traffic("merge", w.name, source_hash("merge.hip")),
                 "avg_launch_ms": round(float(t_merge), 4),
-                "algorithmic_per_launch": f"{mb:.4e} B (P*(d+1)*4 read + (d+1)*4 written per row and head)"}
+                "algorithmic_per_launch": f"{mb:.4e} B ({'live slots' if g else 'P'}*(d+1)*4 read + (d+1)*4 "
+                                          f"written per row and head)"}
 
     out = {
         "metric": METRIC,
@@ -239,9 +321,12 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.F}x{w.Hh}x{w.W} = {w.N} tokens, H={w.H}, d={w.d}, P={w.P}, "
-                               f"{w.policy}-{w.n_fresh} mask", "tokens": w.N, "heads": w.H, "head_dim": w.d,
+                               f"{mask_desc} mask", "tokens": w.N, "heads": w.H, "head_dim": w.d,
                    "partitions": w.P, "reuse_ratio": round(float(reuse), 4),
+                   "state_cache": cache_desc,
+                   "cache_bytes": cache_bytes,
                    "fresh_pairs_per_step": float(np.mean([m.sum() for m in masks])),
+                   **({"computed_slots_per_step": float(np.mean([c.sum() for c in computed_log]))} if g else {}),
                    "parallelism": "none (all partitions on one GPU)"},
         "roofline": roof,
         "kernels": {
@@ -252,7 +337,9 @@ def main():
                       "hbm_frac": round(merge_gbs / PEAK_HBM_GBS, 4), "bytes": mb},
         },
     }
-    if not args.no_cpu_baseline:
+    if compose_rec is not None:
+        out["group_compose"] = compose_rec
+    if not args.no_cpu_baseline and not g:
         # about 12 s of timed oracle work: the oracle sustains roughly 7e10
         # fp64 FLOP/s on the fresh pairs of a step (measured on the image sample)
         steps = args.cpu_steps or 3

@@ -44,7 +44,7 @@ EXPORTED = ("ditango_states_bytes", "ditango_states_init", "ditango_attn_partial
             "ditango_last_error", "ditango_version",
             "ditango_group_slots", "ditango_gstates_slot_bytes", "ditango_gstates_init",
             "ditango_group_attn_partial", "ditango_group_cache_update", "ditango_group_merge",
-            "ditango_group_compose", "ditango_group_reset")
+            "ditango_group_compose", "ditango_group_reset", "ditango_group_mask_build")
 
 
 class DitangoError(RuntimeError):
@@ -71,8 +71,12 @@ class ditango_gstates_t(ctypes.Structure):
 
 def _load():
     if not os.path.exists(_LIB_PATH):
-        raise ImportError(f"{_LIB_PATH} is missing: build it first (python -m context_state_reuse_amd.build)")
+        raise ImportError(f"{_LIB_PATH} is missing: build it first (python context_state_reuse_amd/build.py)")
     lib = ctypes.CDLL(_LIB_PATH)
+    missing = [n for n in EXPORTED if not hasattr(lib, n)]
+    if missing:
+        raise ImportError(f"{_LIB_PATH} lacks {', '.join(missing)}: it predates these sources, rebuild it "
+                          f"(python context_state_reuse_amd/build.py)")
     vp, i32, u8p = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_uint8)
     lib.ditango_states_bytes.restype = ctypes.c_size_t
     lib.ditango_states_bytes.argtypes = [ctypes.POINTER(ditango_shape_t), ctypes.POINTER(ctypes.c_size_t),
@@ -111,6 +115,8 @@ def _load():
     lib.ditango_group_compose.argtypes = [gst, i32, vp]
     lib.ditango_group_reset.restype = ctypes.c_int
     lib.ditango_group_reset.argtypes = [gst, ptab, ptab]
+    lib.ditango_group_mask_build.restype = ctypes.c_int
+    lib.ditango_group_mask_build.argtypes = [i32, i32, i32, u8p]
     return lib
 
 
@@ -236,6 +242,30 @@ def ditango_group_slots(P: int, g: int) -> int:
     return int(lib.ditango_group_slots(int(P), int(g)))
 
 
+def group_slot_range(P: int, g: int, q: int, s: int) -> tuple[int, int]:
+    """Partitions [a, b) spanned by slot s of query partition q (slot 0: q itself)."""
+    if s == 0:
+        return q, q + 1
+    a = (s - 1) * g
+    return a, min(a + g, P)
+
+
+def group_slot_live(P: int, g: int, q: int, s: int) -> bool:
+    """The slot holds a state (a group that is {q} alone does not)."""
+    a, b = group_slot_range(P, g, q, s)
+    return s == 0 or b - a > 1 or a != q
+
+
+def group_slot_keys(N: int, P: int, g: int, q: int, s: int) -> int:
+    """Keys whose attention the state of slot s of q covers."""
+    S = -(-N // P)
+    a, b = group_slot_range(P, g, q, s)
+    n = min(b * S, N) - a * S
+    if s != 0 and a <= q < b:
+        n -= min(S, N - q * S)
+    return n
+
+
 def _ptab(ptrs):
     arr = (ctypes.c_void_p * DITANGO_MAX_SLOTS)()
     for i, x in enumerate(ptrs):
@@ -293,10 +323,15 @@ class GroupedStateCache:
     def device_bytes(self) -> int:
         return sum(t.numel() * 4 for t in self.O + self.LSE)
 
-    def compose(self, k: int = 2, stream=None) -> None:
-        """Dynamic Group State Compose: group size g -> k g; frees released slots."""
+    def compose(self, k: int = 2, stream=None, after=None) -> None:
+        """Dynamic Group State Compose: group size g -> k g; frees released slots.
+
+        ``after`` (optional) is called right after the work is enqueued,
+        before the buffers are released (e.g. to record a timing event)."""
         import torch
         _check(lib.ditango_group_compose(ctypes.byref(self.st), int(k), _stream(stream)))
+        if after is not None:
+            after()
         n = self.n_slots
         if len(self.O) > n:
             # the released buffers are read by the queued group merges
@@ -343,3 +378,10 @@ def ditango_group_merge(cache: GroupedStateCache, O=None, LSE=None, stream=None)
 
 def ditango_group_compose(cache: GroupedStateCache, k: int = 2, stream=None) -> None:
     cache.compose(k, stream)
+
+
+def ditango_group_mask_build(P: int, g: int, n: int) -> np.ndarray:
+    """Pair mask selecting, per query partition, the local pair and the n nearest groups."""
+    out = np.zeros((P, P), dtype=np.uint8) if 1 <= P <= DITANGO_MAX_P else np.zeros(1, dtype=np.uint8)
+    _check(lib.ditango_group_mask_build(int(P), int(g), int(n), _u8(out)))
+    return out

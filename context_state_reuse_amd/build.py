@@ -1,6 +1,7 @@
 """Builds libditango.so in-tree with hipcc for gfx950.
 
-Usage: python -m context_state_reuse_amd.build  (or __graft_entry__.build()).
+Usage: python context_state_reuse_amd/build.py  (or __graft_entry__.build()).
+Run it as a file: importing the package first would load the library.
 Always recompiles.  Flags: -O3, C++17, gfx950 only, and packed fp32 VALU
 instructions disabled (the kernels are written for scalar fp32 VALU).
 """

@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
 #include <cstdarg>
 #include <cstdio>
 #include <algorithm>
@@ -527,6 +528,31 @@ int ditango_group_reset(ditango_gstates_t* st, float* const* O, float* const* LS
   }
   st->g = st->g0;
   for (int i = 0; i < st->shape.P * DITANGO_MAX_SLOTS; ++i) st->tc[i] = -1;
+  return ok();
+}
+
+int ditango_group_mask_build(int32_t P, int32_t g, int32_t n, uint8_t* mask_out) {
+  if (!mask_out) return fail(DITANGO_EINVAL, "mask_out is NULL");
+  if (P < 1 || P > DITANGO_MAX_P) return fail(DITANGO_EINVAL, "P=%d outside 1..%d", P, DITANGO_MAX_P);
+  if (g < 1 || n < 0) return fail(DITANGO_EINVAL, "group size g=%d must be >= 1 and n=%d >= 0", g, n);
+  std::memset(mask_out, 0, static_cast<size_t>(P) * P);
+  const int m = (P + g - 1) / g;
+  std::vector<std::pair<int, int>> cand;   // (distance, group)
+  for (int q = 0; q < P; ++q) {
+    mask_out[q * P + q] = 1;
+    cand.clear();
+    for (int j = 0; j < m; ++j) {
+      int dist = -1;
+      for (int k = j * g; k < std::min((j + 1) * g, P); ++k)
+        if (k != q && (dist < 0 || std::abs(q - k) < dist)) dist = std::abs(q - k);
+      if (dist >= 0) cand.push_back({dist, j});
+    }
+    std::sort(cand.begin(), cand.end());
+    for (int i = 0; i < std::min<int>(n, static_cast<int>(cand.size())); ++i) {
+      const int j = cand[i].second;
+      for (int k = j * g; k < std::min((j + 1) * g, P); ++k) mask_out[q * P + k] = 1;
+    }
+  }
   return ok();
 }
 

@@ -18,8 +18,8 @@
 //      first is used, about 32 per thread -- and accumulates w_k * OUT_k in
 //      registers;
 //   3. the R*d outputs are written contiguously.
-// R = 256 / PMAX keeps 32 independent loads in flight per thread at every
-// state count.  Each output element is written by the thread that read that
+// R = 256 / PMAX keeps up to 32 independent loads in flight per thread; the
+// template chosen for a state count is in launch_d.  Each output element is written by the thread that read that
 // element of every input, after reading it, so an output may overwrite the
 // rows of one of its inputs (the in-place group merge).
 
@@ -138,11 +138,21 @@ hipError_t launch(const MergeParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// State-count template per head dim, from a sweep on MI355X (row merges and
+// group merges of 2 to 32 states): the instantiations that the compiler
+// builds at 256 VGPRs -- d = 128 with 4 lanes per row, d = 64 with 2 --
+// reach only 55-65% of the bandwidth of their neighbours, so those counts
+// use the next template up.
 template <int D>
 hipError_t launch_d(const MergeParams& p, hipStream_t stream) {
-  if (p.n_in <= 4) return launch<D, 4>(p, stream);
-  if (p.n_in <= 8) return launch<D, 8>(p, stream);
-  if (p.n_in <= 16) return launch<D, 16>(p, stream);
+  const int n = p.n_in;
+  if constexpr (D == 128) {
+    if (n <= 2) return launch<D, 2>(p, stream);
+  } else if constexpr (D == 64) {
+    if (n <= 4) return launch<D, 4>(p, stream);
+  }
+  if (n <= 8) return launch<D, 8>(p, stream);
+  if (n <= 16) return launch<D, 16>(p, stream);
   return launch<D, 32>(p, stream);
 }
 

@@ -220,6 +220,15 @@ int ditango_group_compose(ditango_gstates_t* st, int32_t k, void* stream);
  * and marks every slot empty.  Errors: EINVAL. */
 int ditango_group_reset(ditango_gstates_t* st, float* const* O, float* const* LSE);
 
+/* Group-aligned locality mask (state-selection section: selection per group;
+ * locality of Fig. 5a): writes the pair mask uint8 [P][P] with, per query
+ * partition q, mask[q][q] = 1 and every member of the n groups nearest to q
+ * set, where a group's distance is min |q - k| over its members k != q
+ * (groups that are {q} alone are skipped) and ties go to the lower group
+ * index.  Every group is then wholly COMPUTE or wholly REUSE.  Errors:
+ * EINVAL (P outside 1..32, g < 1, n < 0). */
+int ditango_group_mask_build(int32_t P, int32_t g, int32_t n, uint8_t* mask_out);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* ditango_last_error(void);
 

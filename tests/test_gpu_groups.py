@@ -108,6 +108,14 @@ def test_group_merges_match_oracle():
     _compare(w, 1, masks=masks, compose_at={2: 2, 4: 2}, label="merges")
 
 
+def test_group_aligned_masks_match_oracle():
+    """Masks that select whole groups (local pair plus the nearest groups)."""
+    from oracle.groups import nearest_groups_mask
+    w = _scaled("stress", "stress_gmask", 5, 16, 27, 2, steps=4)
+    m = nearest_groups_mask(w.P, 4, 2)
+    _compare(w, 4, masks={0: all_fresh(w.P), 1: m, 2: m, 3: m}, compose_at={3: 2}, label="group masks")
+
+
 def test_group_merge_frees_slots_and_reset():
     import torch
     import context_state_reuse_amd as lib

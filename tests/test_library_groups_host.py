@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import synth
-from oracle.groups import group_decisions, n_slots
+from oracle.groups import group_decisions, n_slots, nearest_groups_mask
 from oracle.masks import step_mask as oracle_step_mask
 
 import context_state_reuse_amd as lib
@@ -138,3 +138,17 @@ def test_cache_update_checks_and_reset():
     assert binding.lib.ditango_group_reset(ctypes.byref(f.st), tabs[0], tabs[1]) == 0
     assert f.st.g == 2 and f.st.O[2] == 0x300000 and np.all(f.tc == -1)
     assert binding.lib.ditango_group_reset(ctypes.byref(f.st), _tab([0x100000]), tabs[1]) == lib.DITANGO_EINVAL
+
+
+def test_group_mask_builder_matches_oracle():
+    for P in (1, 2, 3, 5, 8, 13, 16, 31, 32):
+        for g in (1, 2, 3, 4, 8, 40):
+            for n in (0, 1, 2, 3, 40):
+                assert np.array_equal(lib.ditango_group_mask_build(P, g, n), nearest_groups_mask(P, g, n)), (P, g, n)
+
+
+@pytest.mark.parametrize("args", [(0, 2, 1), (33, 2, 1), (8, 0, 1), (8, 2, -1)])
+def test_group_mask_builder_rejects(args):
+    with pytest.raises(lib.DitangoError) as e:
+        lib.ditango_group_mask_build(*args)
+    assert e.value.code == lib.DITANGO_EINVAL
