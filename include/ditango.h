@@ -212,7 +212,9 @@ int ditango_group_merge(const ditango_gstates_t* st, float* O, float* LSE, void*
  * of theirs.  Slots >= ditango_group_slots(P, k*g) are released: their
  * pointers in `st` become NULL and the caller may free those buffers once
  * the stream has passed this call.  Every non-empty slot must hold a state,
- * else DITANGO_ENOCACHE; k >= 2.  Errors: EINVAL, ENOCACHE, EHIP. */
+ * else DITANGO_ENOCACHE; k >= 2.  Errors: EINVAL, ENOCACHE (both before any
+ * work), EHIP (a launch failed part-way: the slot contents are then
+ * undefined and the caller should reset and recompute at an anchor step). */
 int ditango_group_compose(ditango_gstates_t* st, int32_t k, void* stream);
 
 /* Return to the original group size g0 before an anchor step: binds

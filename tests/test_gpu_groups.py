@@ -140,7 +140,7 @@ def test_group_merge_frees_slots_and_reset():
         lib.ditango_group_merge(cache)
 
 
-FULL_GROUPED = [("stress", 4), ("long", 4), ("video_25", 2)]
+FULL_GROUPED = [("stress", 4), ("long", 4), ("video_25", 2), ("image", 3)]
 
 
 @pytest.mark.parametrize("name,g", FULL_GROUPED, ids=[f"{n}_g{g}" for n, g in FULL_GROUPED])
