@@ -50,6 +50,9 @@ def parse():
                     help="run the grouped, composed state cache with this group size (0: per-pair cache)")
     ap.add_argument("--compose", type=int, default=0,
                     help="with --group: after the timed steps, time one merge of groups by this factor")
+    ap.add_argument("--window-residual", action="store_true",
+                    help="window attention with residual sharing: the anchor step computes every pair and caches "
+                         "full-minus-window outputs; steady steps compute the window pairs (nearest partitions) only")
     ap.add_argument("--group-masks", choices=("nearest", "workload"), default="nearest",
                     help="with --group: group-aligned masks (local pair plus the nearest groups, as many "
                          "fresh partitions per row as the workload's masks) or the workload's own pair masks")
@@ -187,7 +190,17 @@ def main():
     step_no = [0]
     computed_log = []
     n_groups = max(1, round(w.n_fresh / g)) if g else 0
-    if g and args.group_masks == "nearest":
+    wr = args.window_residual
+    if wr and g:
+        print("--window-residual works on the per-pair cache; drop --group", file=sys.stderr)
+        sys.exit(2)
+    if wr:
+        wmask = lib.ditango_mask_build("radius", w.P, 1) if w.policy == "radius" else \
+            lib.ditango_mask_build("nearest", w.P, min(w.n_fresh, w.P))
+        R = torch.empty((w.H, w.N, w.d), dtype=torch.float32, device=dev)
+        mask_of = lambda t: lib.ditango_mask_build("all", w.P) if t == 0 else wmask
+        mask_desc = f"window residual, window = {'radius-1' if w.policy == 'radius' else 'nearest-' + str(w.n_fresh)}"
+    elif g and args.group_masks == "nearest":
         gmask = lib.ditango_group_mask_build(w.P, g, n_groups)
         mask_of = lambda t: lib.ditango_mask_build("all", w.P) if t == 0 else gmask
         mask_desc = f"local pair + {n_groups} nearest group(s) of {g}"
@@ -211,6 +224,10 @@ def main():
             lib.ditango_group_merge(cache, O, LSE)
             if events is not None:
                 computed_log.append(computed)
+        elif wr:
+            lib.ditango_state_cache_update(cache, mask, step_no[0])
+            lib.ditango_window_residual_merge(cache, wmask, lib.DITANGO_WR_FULL if t == 0 else lib.DITANGO_WR_WINDOW,
+                                              R, O, LSE)
         else:
             lib.ditango_state_cache_update(cache, mask, step_no[0])
             lib.ditango_state_merge(cache, O, LSE)
@@ -262,6 +279,10 @@ def main():
         reuse = 1.0 - np.mean([m.mean() for m in masks])
         mb = merge_bytes(w)
         sb = np.mean([state_store_bytes(w, m) for m in masks])
+        if wr:
+            # window step: the window states and the residual read, one output written
+            lens = np.array([min(w.S, w.N - p * w.S) for p in range(w.P)], dtype=np.float64)
+            mb = float(4.0 * w.H * (lens * (wmask.sum(axis=1) * (w.d + 1) + w.d + (w.d + 1))).sum())
 
     partial_tflops = fresh / (t_partial * 1e-3) / 1e12
     merge_gbs = mb / (t_merge * 1e-3) / 1e9
@@ -295,14 +316,14 @@ def main():
     if t_partial >= t_merge:
         roof = {"kernel": "partial_kernel", "bound": "mfma", "achieved": round(partial_tflops, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(partial_tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": None if g else stored_traffic("partial", w.name, src),
+                "traffic": None if (g or wr) else stored_traffic("partial", w.name, src),
                 "avg_launch_ms": round(float(t_partial), 4),
                 "algorithmic_per_launch": f"{fresh:.4e} FLOP (4*len_q*len_k*d per fresh "
                                           f"{'slot, len_k = keys of its members' if g else 'pair'} and head)"}
     else:
         roof = {"kernel": "merge_kernel", "bound": "hbm", "achieved": round(merge_gbs, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(merge_gbs / PEAK_HBM_GBS, 4),
-                "traffic": None if g else stored_traffic("merge", w.name, source_hash("merge.hip")),
+                "traffic": None if (g or wr) else stored_traffic("merge", w.name, source_hash("merge.hip")),
                 "avg_launch_ms": round(float(t_merge), 4),
                 "algorithmic_per_launch": f"{mb:.4e} B ({'live slots' if g else 'P'}*(d+1)*4 read + (d+1)*4 "
                                           f"written per row and head)"}
@@ -323,7 +344,7 @@ def main():
         "config": {"workload": f"{w.name}: {w.F}x{w.Hh}x{w.W} = {w.N} tokens, H={w.H}, d={w.d}, P={w.P}, "
                                f"{mask_desc} mask", "tokens": w.N, "heads": w.H, "head_dim": w.d,
                    "partitions": w.P, "reuse_ratio": round(float(reuse), 4),
-                   "state_cache": cache_desc,
+                   "state_cache": ("per pair, window states only, plus a residual [H][N][d]" if wr else cache_desc),
                    "cache_bytes": cache_bytes,
                    "fresh_pairs_per_step": float(np.mean([m.sum() for m in masks])),
                    **({"computed_slots_per_step": float(np.mean([c.sum() for c in computed_log]))} if g else {}),
@@ -339,7 +360,7 @@ def main():
     }
     if compose_rec is not None:
         out["group_compose"] = compose_rec
-    if not args.no_cpu_baseline and not g:
+    if not args.no_cpu_baseline and not g and not wr:
         # about 12 s of timed oracle work: the oracle sustains roughly 7e10
         # fp64 FLOP/s on the fresh pairs of a step (measured on the image sample)
         steps = args.cpu_steps or 3

@@ -44,7 +44,8 @@ EXPORTED = ("ditango_states_bytes", "ditango_states_init", "ditango_attn_partial
             "ditango_last_error", "ditango_version",
             "ditango_group_slots", "ditango_gstates_slot_bytes", "ditango_gstates_init",
             "ditango_group_attn_partial", "ditango_group_cache_update", "ditango_group_merge",
-            "ditango_group_compose", "ditango_group_reset", "ditango_group_mask_build")
+            "ditango_group_compose", "ditango_group_reset", "ditango_group_mask_build",
+            "ditango_window_residual_merge")
 
 
 class DitangoError(RuntimeError):
@@ -117,6 +118,8 @@ def _load():
     lib.ditango_group_reset.argtypes = [gst, ptab, ptab]
     lib.ditango_group_mask_build.restype = ctypes.c_int
     lib.ditango_group_mask_build.argtypes = [i32, i32, i32, u8p]
+    lib.ditango_window_residual_merge.restype = ctypes.c_int
+    lib.ditango_window_residual_merge.argtypes = [ctypes.POINTER(ditango_states_t), u8p, i32, vp, vp, vp, vp]
     return lib
 
 
@@ -215,6 +218,28 @@ def ditango_state_merge(cache: StateCache, O=None, LSE=None, stream=None):
             raise ValueError(f"{nm} must be a contiguous float32 device tensor of shape {shp}")
     _check(lib.ditango_state_merge(ctypes.byref(cache.st), ctypes.c_void_p(O.data_ptr()),
                                    ctypes.c_void_p(LSE.data_ptr()), _stream(stream)))
+    return O, LSE
+
+
+DITANGO_WR_FULL = 0
+DITANGO_WR_WINDOW = 1
+
+
+def ditango_window_residual_merge(cache: StateCache, window, mode: int, R, O=None, LSE=None, stream=None):
+    """Window attention with residual sharing: FULL writes O, LSE and R; WINDOW reads R."""
+    import torch
+    w = _mask(window, cache.P)
+    if O is None:
+        O = torch.empty((cache.H, cache.N, cache.d), dtype=torch.float32, device=cache.O.device)
+    if LSE is None:
+        LSE = torch.empty((cache.H, cache.N), dtype=torch.float32, device=cache.O.device)
+    for t, shp, nm in ((R, (cache.H, cache.N, cache.d), "R"), (O, (cache.H, cache.N, cache.d), "O"),
+                       (LSE, (cache.H, cache.N), "LSE")):
+        if not (t.is_cuda and t.dtype == torch.float32 and t.is_contiguous() and tuple(t.shape) == shp):
+            raise ValueError(f"{nm} must be a contiguous float32 device tensor of shape {shp}")
+    _check(lib.ditango_window_residual_merge(ctypes.byref(cache.st), _u8(w), int(mode), ctypes.c_void_p(R.data_ptr()),
+                                             ctypes.c_void_p(O.data_ptr()), ctypes.c_void_p(LSE.data_ptr()),
+                                             _stream(stream)))
     return O, LSE
 
 

@@ -315,6 +315,53 @@ int ditango_state_merge(const ditango_states_t* st, float* O, float* LSE, void* 
   return ok();
 }
 
+int ditango_window_residual_merge(const ditango_states_t* st, const uint8_t* window, int32_t mode, float* R,
+                                  float* O, float* LSE, void* stream) {
+  int rc = check_states(st);
+  if (rc) return rc;
+  const int P = st->shape.P;
+  if ((rc = check_mask(window, P))) return rc;
+  if (mode != DITANGO_WR_FULL && mode != DITANGO_WR_WINDOW)
+    return fail(DITANGO_EINVAL, "window-residual mode %d is neither FULL nor WINDOW", mode);
+  if (!R || !O || !LSE) return fail(DITANGO_EINVAL, "R, O and LSE must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(R) | reinterpret_cast<uintptr_t>(O) | reinterpret_cast<uintptr_t>(LSE)) & 15u)
+    return fail(DITANGO_EINVAL, "R, O and LSE must be 16-byte aligned");
+  ditango::MergeParams m;
+  std::memset(&m, 0, sizeof m);
+  for (int q = 0; q < P; ++q) {
+    for (int k = 0; k < P; ++k)
+      if (window[q * P + k]) m.wlive[q] |= 1u << k;
+    if (!m.wlive[q]) return fail(DITANGO_EINVAL, "query partition %d has an empty window", q);
+    m.live[q] = mode == DITANGO_WR_FULL ? (P == 32 ? 0xffffffffu : (1u << P) - 1u) : m.wlive[q];
+  }
+  for (int q = 0; q < P; ++q)
+    for (int k = 0; k < P; ++k)
+      if (((m.live[q] >> k) & 1u) && st->tc[q * P + k] < 0)
+        return fail(DITANGO_ENOCACHE, "pair (q=%d, k=%d) holds no state", q, k);
+  const size_t slot_o = static_cast<size_t>(st->S) * st->shape.d;
+  for (int k = 0; k < P; ++k) {
+    m.in_O[k] = st->O + k * slot_o;
+    m.in_L[k] = st->LSE + static_cast<size_t>(k) * st->S;
+  }
+  m.in_hs = static_cast<int64_t>(P) * P;
+  m.in_qs = P;
+  m.out_hs = st->shape.N;
+  m.out_qs = st->S;
+  m.O = O;
+  m.LSE = LSE;
+  m.res = R;
+  m.res_mode = mode == DITANGO_WR_FULL ? 1 : 2;
+  m.n_in = P;
+  m.H = st->shape.H;
+  m.N = st->shape.N;
+  m.P = P;
+  m.S = st->S;
+  m.d = st->shape.d;
+  hipError_t e = ditango::launch_merge(m, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DITANGO_EHIP, "merge kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int32_t ditango_group_slots(int32_t P, int32_t g) { return group_slots(P, g); }
 
 size_t ditango_gstates_slot_bytes(const ditango_shape_t* shape, size_t* o_bytes, size_t* lse_bytes) {

@@ -45,14 +45,27 @@ struct PartialParams {
 // + r)*d and LSE + h*out_hs + q*out_qs + r.  A (h, q) with no live state is
 // skipped.  The row merge of both caches and the in-place group merge of
 // the grouped cache are instances.
+//
+// Window attention with residual sharing (res_mode != 0; res laid out like
+// O): res_mode 1 also writes res = OUT - (composition of the states in
+// wlive[q]); res_mode 2 adds res to OUT.
 struct MergeParams {
   const float* in_O[DITANGO_MAX_SLOTS];
   const float* in_L[DITANGO_MAX_SLOTS];
   uint32_t live[DITANGO_MAX_P];
+  uint32_t wlive[DITANGO_MAX_P];
+  // Filled by launch_merge from live/wlive: the live states of query
+  // partition q as a list idx[q][0 .. cnt[q]), and the window bits over
+  // that list, so a row's lanes cover only its live states.
+  uint8_t idx[DITANGO_MAX_P][DITANGO_MAX_SLOTS];
+  uint8_t cnt[DITANGO_MAX_P];
+  uint32_t wpos[DITANGO_MAX_P];
   int64_t in_hs, in_qs;     // in units of S rows
   int64_t out_hs, out_qs;   // in rows
   float* O;
   float* LSE;
+  float* res;
+  int32_t res_mode;
   int32_t n_in;             // <= DITANGO_MAX_SLOTS
   int32_t H, N, P, S, d;
 };

@@ -22,6 +22,12 @@
 // template chosen for a state count is in launch_d.  Each output element is written by the thread that read that
 // element of every input, after reading it, so an output may overwrite the
 // rows of one of its inputs (the in-place group merge).
+//
+// RES = 1 (full step of window attention with residual sharing, DiTFastAttn
+// page): a second weight set renormalised over the window states gives the
+// window composition in the same pass, and res = OUT - OUT_window is
+// written beside OUT.  RES = 2 (window step): OUT of the window states plus
+// the cached res.
 
 #include <hip/hip_runtime.h>
 
@@ -53,31 +59,38 @@ __device__ inline void store_stream(float* p, f32x4 v) {
   }
 }
 
-template <int D, int PMAX>
+// COMPACT: lanes walk the compacted live list idx[q][0 .. cnt[q]) (one more
+// indirection per state) instead of state indices 0 .. n_in with liveness
+// bits; chosen only when it lets a narrower template (fewer lanes per row)
+// serve the launch.
+template <int D, int PMAX, int RES, bool COMPACT>
 __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p, int row_tiles) {
   constexpr int R = kThreads / PMAX;                  // rows per block
   constexpr int CH = R * D / 4;                       // float4 chunks per state block
   constexpr int PER = (CH + kThreads - 1) / kThreads; // chunks per thread
   __shared__ float w_lds[R][PMAX];
+  __shared__ float wr_lds[RES == 1 ? R : 1][PMAX];     // weights of res = OUT - OUT_window
 
   const int tid = threadIdx.x;
   const int rt = blockIdx.x % row_tiles;
   const int hq = blockIdx.x / row_tiles;              // h * P + q
   const int q = hq % p.P;
   const int h = hq / p.P;
-  const uint32_t live = p.live[q];
+  const int cnt = COMPACT ? p.cnt[q] : p.n_in;        // lanes in use per row
+  const uint32_t live = COMPACT ? 0xffffffffu : p.live[q];
   const int len_q = min(p.S, p.N - q * p.S);
   const int i0 = rt * R;
   const int rows = min(R, len_q - i0);
-  if (live == 0 || rows <= 0) return;                 // block-uniform
+  if (cnt == 0 || (live & (cnt >= 32 ? 0xffffffffu : (1u << cnt) - 1u)) == 0 || rows <= 0) return;   // block-uniform
+  auto state = [&](int k) __attribute__((always_inline)) { return COMPACT ? static_cast<int>(p.idx[q][k]) : k; };
   const int64_t in_row0 = (h * p.in_hs + q * p.in_qs) * p.S + i0;
   const int64_t out_row0 = h * p.out_hs + q * p.out_qs + i0;
 
   // 1. weights
   {
     const int r = tid / PMAX, k = tid % PMAX;
-    const bool lv = k < p.n_in && ((live >> k) & 1u) && r < rows;
-    float l = lv ? p.in_L[k][in_row0 + r] : -__builtin_inff();
+    const bool lv = k < cnt && ((live >> k) & 1u) && r < rows;
+    float l = lv ? p.in_L[state(k)][in_row0 + r] : -__builtin_inff();
     float m = l;
 #pragma unroll
     for (int off = 1; off < PMAX; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
@@ -86,6 +99,17 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p, in
 #pragma unroll
     for (int off = 1; off < PMAX; off <<= 1) z += __shfl_xor(z, off);
     w_lds[r][k] = e / z;
+    if constexpr (RES == 1) {
+      const bool win = lv && (((COMPACT ? p.wpos[q] : p.wlive[q]) >> k) & 1u);
+      float mw = win ? l : -__builtin_inff();
+#pragma unroll
+      for (int off = 1; off < PMAX; off <<= 1) mw = fmaxf(mw, __shfl_xor(mw, off));
+      const float ew = win ? __builtin_amdgcn_exp2f((l - mw) * 1.4426950408889634f) : 0.0f;
+      float zw = ew;
+#pragma unroll
+      for (int off = 1; off < PMAX; off <<= 1) zw += __shfl_xor(zw, off);
+      wr_lds[r][k] = e / z - ew / zw;
+    }
     if (k == 0 && r < rows) p.LSE[out_row0 + r] = m + __builtin_amdgcn_logf(z) * 0.69314718055994531f;
   }
   __syncthreads();
@@ -93,13 +117,18 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p, in
   // 2. stream the states
   const int valid = rows * (D / 4);
   f32x4 acc[PER];
+  f32x4 racc[RES == 1 ? PER : 1];
   f32x4 o[PMAX][PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (RES == 1) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) racc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 #pragma unroll
   for (int k = 0; k < PMAX; ++k) {
-    if (k < p.n_in && ((live >> k) & 1u)) {
-      const float* src = p.in_O[k] + in_row0 * D;
+    if (k < cnt && ((live >> k) & 1u)) {
+      const float* src = p.in_O[state(k)] + in_row0 * D;
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         const int c = tid + j * kThreads;
@@ -109,32 +138,50 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p, in
   }
 #pragma unroll
   for (int k = 0; k < PMAX; ++k) {
-    if (k < p.n_in && ((live >> k) & 1u)) {
+    if (k < cnt && ((live >> k) & 1u)) {
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         const int c = tid + j * kThreads;
-        if (c < valid) acc[j] += w_lds[c / (D / 4)][k] * o[k][j];
+        if (c < valid) {
+          acc[j] += w_lds[c / (D / 4)][k] * o[k][j];
+          if constexpr (RES == 1) racc[j] += wr_lds[c / (D / 4)][k] * o[k][j];
+        }
       }
     }
   }
 
   // 3. write
   float* dst = p.O + out_row0 * D;
+  float* rdst = p.res + out_row0 * D;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int c = tid + j * kThreads;
-    if (c < valid) store_stream(dst + 4 * c, acc[j]);
+    if (c < valid) {
+      if constexpr (RES == 2) acc[j] += load_stream(rdst + 4 * c);
+      store_stream(dst + 4 * c, acc[j]);
+      if constexpr (RES == 1) store_stream(rdst + 4 * c, racc[j]);
+    }
   }
 }
 
 template <int D, int PMAX>
-hipError_t launch(const MergeParams& p, hipStream_t stream) {
+hipError_t launch(const MergeParams& p, bool compact, hipStream_t stream) {
   constexpr int R = kThreads / PMAX;
   const int row_tiles = (p.S + R - 1) / R;
   const int64_t blocks = static_cast<int64_t>(p.H) * p.P * row_tiles;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((merge_kernel<D, PMAX>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, p,
-                     row_tiles);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+  if (p.res_mode == 1) {          // every state of a row takes part: never compacted
+    hipLaunchKernelGGL((merge_kernel<D, PMAX, 1, false>), grid, block, 0, stream, p, row_tiles);
+  } else if (p.res_mode == 2) {
+    if (compact) hipLaunchKernelGGL((merge_kernel<D, PMAX, 2, true>), grid, block, 0, stream, p, row_tiles);
+    else hipLaunchKernelGGL((merge_kernel<D, PMAX, 2, false>), grid, block, 0, stream, p, row_tiles);
+  } else if (p.res_mode == 0) {
+    if (compact) hipLaunchKernelGGL((merge_kernel<D, PMAX, 0, true>), grid, block, 0, stream, p, row_tiles);
+    else hipLaunchKernelGGL((merge_kernel<D, PMAX, 0, false>), grid, block, 0, stream, p, row_tiles);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -144,26 +191,54 @@ hipError_t launch(const MergeParams& p, hipStream_t stream) {
 // reach only 55-65% of the bandwidth of their neighbours, so those counts
 // use the next template up.
 template <int D>
-hipError_t launch_d(const MergeParams& p, hipStream_t stream) {
-  const int n = p.n_in;
-  if constexpr (D == 128) {
-    if (n <= 2) return launch<D, 2>(p, stream);
-  } else if constexpr (D == 64) {
-    if (n <= 4) return launch<D, 4>(p, stream);
+int lanes_per_row(int n) {
+  if (D == 128 && n <= 2) return 2;
+  if (D == 64 && n <= 4) return 4;
+  if (n <= 8) return 8;
+  if (n <= 16) return 16;
+  return 32;
+}
+
+template <int D>
+hipError_t launch_d(const MergeParams& p, int most, hipStream_t stream) {
+  const bool compact = lanes_per_row<D>(most) < lanes_per_row<D>(p.n_in);
+  switch (lanes_per_row<D>(compact ? most : p.n_in)) {
+    case 2:
+      if constexpr (D == 128) return launch<D, 2>(p, compact, stream);
+      break;
+    case 4:
+      if constexpr (D == 64) return launch<D, 4>(p, compact, stream);
+      break;
+    case 8: return launch<D, 8>(p, compact, stream);
+    case 16: return launch<D, 16>(p, compact, stream);
+    default: return launch<D, 32>(p, compact, stream);
   }
-  if (n <= 8) return launch<D, 8>(p, stream);
-  if (n <= 16) return launch<D, 16>(p, stream);
-  return launch<D, 32>(p, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
-  if (p.n_in < 1 || p.n_in > 32) return hipErrorInvalidValue;
+hipError_t launch_merge(const MergeParams& p_in, hipStream_t stream) {
+  if (p_in.n_in < 1 || p_in.n_in > DITANGO_MAX_SLOTS || p_in.P > DITANGO_MAX_P) return hipErrorInvalidValue;
+  MergeParams p = p_in;
+  int most = 0;
+  for (int q = 0; q < p.P; ++q) {
+    int c = 0;
+    uint32_t wp = 0;
+    for (int k = 0; k < p.n_in; ++k)
+      if ((p.live[q] >> k) & 1u) {
+        if ((p.wlive[q] >> k) & 1u) wp |= 1u << c;
+        p.idx[q][c++] = static_cast<uint8_t>(k);
+      }
+    p.cnt[q] = static_cast<uint8_t>(c);
+    p.wpos[q] = wp;
+    most = c > most ? c : most;
+  }
+  if (most == 0) return hipSuccess;                   // no state takes part anywhere
   switch (p.d) {
-    case 64: return launch_d<64>(p, stream);
-    case 72: return launch_d<72>(p, stream);
-    case 128: return launch_d<128>(p, stream);
+    case 64: return launch_d<64>(p, most, stream);
+    case 72: return launch_d<72>(p, most, stream);
+    case 128: return launch_d<128>(p, most, stream);
     default: return hipErrorInvalidValue;
   }
 }

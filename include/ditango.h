@@ -134,6 +134,24 @@ int ditango_state_merge(const ditango_states_t* st, float* O, float* LSE, void* 
 #define DITANGO_MASK_RANDOM  4
 int ditango_mask_build(int32_t policy, int32_t P, int32_t n, uint64_t seed, uint8_t* mask_out);
 
+/* Window attention with residual sharing at partition granularity (the
+ * DiTFastAttn page: window attention plus a cached full-minus-window
+ * residual), on the per-pair states.  window [P][P] (host, 0/1, at least one
+ * 1 per row) names the window partitions of every query partition.
+ *   DITANGO_WR_FULL    every pair must hold a state: O, LSE = composition of
+ *                      all P states (full attention when all are fresh), and
+ *                      R = O - (composition of the window states)
+ *   DITANGO_WR_WINDOW  the window pairs must hold states: O = composition of
+ *                      the window states + R, LSE = that composition's LSE
+ * R: device fp32 [H][N][d] (caller-owned; written in FULL mode, read in
+ * WINDOW mode).  O, LSE as for ditango_state_merge.  Reads only the window
+ * states in WINDOW mode.  Errors: EINVAL, ENOCACHE (a needed pair holds no
+ * state), EHIP. */
+#define DITANGO_WR_FULL   0
+#define DITANGO_WR_WINDOW 1
+int ditango_window_residual_merge(const ditango_states_t* st, const uint8_t* window, int32_t mode, float* R,
+                                  float* O, float* LSE, void* stream);
+
 /* ---------------------------------------------------------------------
  * Grouped, composed state cache (state-selection section: the p partition
  * states are grouped into groups of g adjacent partitions, the group that

@@ -85,3 +85,35 @@ def run_group_steps(w, g, masks=None, steps=None, compose_at=None, on_step=None,
             on_step(t, mask, computed, cache, O, LSE)
         del Q, K, V
     return cache
+
+
+def run_window_residual_steps(w, window, steps=None, on_step=None, label=""):
+    """Window attention with residual sharing through the library: step 0
+    computes every pair and caches the residual, later steps compute the
+    window pairs only.  on_step(t, cache, R, O, LSE) after each step."""
+    import torch
+
+    import context_state_reuse_amd as lib
+
+    n = w.steps if steps is None else steps
+    cache = lib.StateCache(w.H, w.N, w.d, w.P)
+    stream = synth.InputStream(w)
+    R = torch.empty((w.H, w.N, w.d), dtype=torch.float32, device="cuda")
+    O = torch.empty_like(R)
+    LSE = torch.empty((w.H, w.N), dtype=torch.float32, device="cuda")
+    window = np.asarray(window, np.uint8)
+    for t in range(n):
+        t0 = time.time()
+        qb, kb, vb = stream.next()
+        Q, K, V = to_device(qb), to_device(kb), to_device(vb)
+        mask = np.ones((w.P, w.P), np.uint8) if t == 0 else window
+        lib.ditango_attn_partial(Q, K, V, mask, cache)
+        lib.ditango_state_cache_update(cache, mask, t)
+        lib.ditango_window_residual_merge(cache, window, lib.DITANGO_WR_FULL if t == 0 else lib.DITANGO_WR_WINDOW,
+                                          R, O, LSE)
+        torch.cuda.synchronize()
+        log(f"  [{label or w.name}] window-residual step {t}: {time.time() - t0:.1f}s")
+        if on_step is not None:
+            on_step(t, cache, R, O, LSE)
+        del Q, K, V
+    return cache

@@ -171,3 +171,21 @@ def test_cache_update_matches_oracle_tc_over_a_workload():
         assert binding.lib.ditango_state_cache_update(ctypes.byref(f.st), _u8(m), t, None) == 0
         orc.tc[m == 1] = t
         assert np.array_equal(f.tc.reshape(w.P, w.P), orc.tc)
+
+
+def test_window_residual_merge_checks_before_launch():
+    f = _FakeStates(P=4)
+    wr = binding.lib.ditango_window_residual_merge
+    fake = ctypes.c_void_p(0x30000)
+    win = radius_mask(4, 1)
+    # FULL needs every pair; nothing is computed yet
+    assert wr(ctypes.byref(f.st), _u8(win), lib.DITANGO_WR_FULL, fake, fake, fake, None) == lib.DITANGO_ENOCACHE
+    # WINDOW needs only the window pairs: still missing here
+    assert wr(ctypes.byref(f.st), _u8(win), lib.DITANGO_WR_WINDOW, fake, fake, fake, None) == lib.DITANGO_ENOCACHE
+    empty = win.copy()
+    empty[1] = 0
+    assert wr(ctypes.byref(f.st), _u8(empty), lib.DITANGO_WR_WINDOW, fake, fake, fake, None) == lib.DITANGO_EINVAL
+    assert wr(ctypes.byref(f.st), _u8(win), 7, fake, fake, fake, None) == lib.DITANGO_EINVAL
+    assert wr(ctypes.byref(f.st), _u8(win), lib.DITANGO_WR_FULL, None, fake, fake, None) == lib.DITANGO_EINVAL
+    odd = ctypes.c_void_p(0x30004)
+    assert wr(ctypes.byref(f.st), _u8(win), lib.DITANGO_WR_FULL, odd, fake, fake, None) == lib.DITANGO_EINVAL
