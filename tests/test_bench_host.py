@@ -1,0 +1,47 @@
+"""bench.py's host-side contract (CPU): it refuses more than one GPU, and its
+FLOP and byte accounting matches the workload definitions."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_fresh_flops_and_merge_bytes_image():
+    w = synth.get("image")
+    m = np.zeros((w.P, w.P), np.uint8)
+    m[0, 0] = m[3, 4] = 1
+    # every partition of the image workload holds S = 2048 tokens
+    assert bench.fresh_flops(w, m) == 2 * 4.0 * 2048 * 2048 * 72 * 16
+    assert bench.merge_bytes(w) == 16 * 16384 * 9 * 73 * 4
+    assert bench.state_store_bytes(w, m) == 16 * 73 * 4 * 2 * 2048
+
+
+def test_fresh_flops_ragged_stress():
+    w = synth.get("stress")
+    m = np.zeros((w.P, w.P), np.uint8)
+    m[w.P - 1, w.P - 1] = 1          # the ragged last partition against itself
+    last = w.N - (w.P - 1) * w.S
+    assert last == 531 and bench.fresh_flops(w, m) == 4.0 * last * last * w.d * w.H
+
+
+def test_group_accounting_at_group_size_one_is_per_pair():
+    w = synth.get("tiny")
+    from oracle.groups import group_decisions
+    m = np.array([[1, 1, 0, 0], [1, 1, 1, 0], [0, 1, 1, 1], [0, 0, 1, 1]], np.uint8)
+    computed = group_decisions(m, 1)
+    flops, mbytes = bench.group_work(w, 1, computed)
+    assert flops == bench.fresh_flops(w, m)
+    assert mbytes == bench.merge_bytes(w)
