@@ -90,10 +90,16 @@ def group_work(w, g, computed):
 
 
 def source_hash(*names) -> str:
+    """Hash of the kernel sources with comments and whitespace removed, so a
+    stored counter run stays matched to its code across comment edits."""
+    import re
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "context_state_reuse_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "context_state_reuse_amd", "csrc", n)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

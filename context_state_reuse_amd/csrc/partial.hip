@@ -4,7 +4,10 @@
 // block computes the attention state (OUT, LSE) of a tile of query rows of
 // partition q against all keys of partition k (DiTango page, attention-state
 // section; the per-step partial attention of its ring-based composed
-// attention) and stores it into the pair's cache slot.
+// attention) and stores it into the pair's cache slot.  For the grouped
+// cache a work item is (q, slot) instead and its keys are those of all the
+// slot's member partitions, which yields their composed state (Eq. 4) in
+// one pass.
 //
 // Formulation.  The scores are built transposed, S^T = K Q^T, with
 // v_mfma_f32_32x32x16_bf16 (A = a 32-key block of K from LDS, B = Q^T held in
@@ -16,8 +19,9 @@
 // operand reproduces).  V stays row-major in LDS and is read transposed with
 // ds_read_b64_tr_b16.  O^T accumulates in fp32 and P is rounded to bf16 for
 // the product.  Two row sums are kept: the fp32 sum of the unrounded
-// probabilities gives LSE, and the sum of the rounded ones (v_dot2c_f32_bf16)
-// normalises OUT, so the weights applied to V sum to one as used.
+// probabilities gives LSE, and the sum of the rounded ones (v_dot2c_f32_bf16,
+// or for d = 72 a ones column of V that makes it a row of O^T) normalises
+// OUT, so the weights applied to V sum to one as used.
 //
 // Softmax runs in base 2 with the scale folded into one FMA.  A tile's
 // probabilities are taken against the running max without first computing
@@ -26,11 +30,12 @@
 // rescaled.  The final division by the row sum makes the result exact.
 //
 // Block = 4 or 8 waves of 32 query rows each (128 or 256 rows), two waves
-// per SIMD (<= 256 VGPRs each, no accumulator spills to AGPRs), so one wave's
-// MFMAs overlap the other's softmax.  K/V tiles of 64 keys are
-// double-buffered in LDS: the next tile's global loads are in flight while
-// the current tile is multiplied.  The grid is the compacted list of
-// fresh (head, pair, query tile) items: no block exists for a reused pair.
+// per SIMD (<= 256 VGPRs each, no accumulator spills to AGPRs), so a SIMD
+// can issue one wave's softmax while the other's MFMAs run.  K/V tiles of 64
+// keys are double-buffered in LDS and filled by direct global-to-LDS loads:
+// the next tile's loads are in flight while the current tile is multiplied.
+// The grid is the compacted list of fresh work items: no block exists for a
+// reused pair.
 
 #include <hip/hip_runtime.h>
 
