@@ -13,5 +13,6 @@ from .binding import (DITANGO_EHIP, DITANGO_EINVAL, DITANGO_ENOCACHE,  # noqa: F
                       ditango_group_slots,
                       group_slot_keys, group_slot_live,
                       ditango_mask_build, ditango_state_cache_update, ditango_state_merge,
-                      ditango_states_bytes, ditango_version, ditango_window_residual_merge, make_shape,
+                      ditango_states_bytes, ditango_step, ditango_version, ditango_window_residual_merge,
+                      make_shape,
                       workload_mask)

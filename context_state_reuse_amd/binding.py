@@ -45,7 +45,7 @@ EXPORTED = ("ditango_states_bytes", "ditango_states_init", "ditango_attn_partial
             "ditango_group_slots", "ditango_gstates_slot_bytes", "ditango_gstates_init",
             "ditango_group_attn_partial", "ditango_group_cache_update", "ditango_group_merge",
             "ditango_group_compose", "ditango_group_reset", "ditango_group_mask_build",
-            "ditango_window_residual_merge")
+            "ditango_window_residual_merge", "ditango_step")
 
 
 class DitangoError(RuntimeError):
@@ -118,6 +118,8 @@ def _load():
     lib.ditango_group_reset.argtypes = [gst, ptab, ptab]
     lib.ditango_group_mask_build.restype = ctypes.c_int
     lib.ditango_group_mask_build.argtypes = [i32, i32, i32, u8p]
+    lib.ditango_step.restype = ctypes.c_int
+    lib.ditango_step.argtypes = [vp, vp, vp, u8p, i32, ctypes.POINTER(ditango_states_t), vp, vp, u8p, vp]
     lib.ditango_window_residual_merge.restype = ctypes.c_int
     lib.ditango_window_residual_merge.argtypes = [ctypes.POINTER(ditango_states_t), u8p, i32, vp, vp, vp, vp]
     return lib
@@ -219,6 +221,25 @@ def ditango_state_merge(cache: StateCache, O=None, LSE=None, stream=None):
     _check(lib.ditango_state_merge(ctypes.byref(cache.st), ctypes.c_void_p(O.data_ptr()),
                                    ctypes.c_void_p(LSE.data_ptr()), _stream(stream)))
     return O, LSE
+
+
+def ditango_step(Q, K, V, mask, step: int, cache: StateCache, O=None, LSE=None, stream=None):
+    """One denoising step through the library's own driver: partial attention,
+    t_c update and composition.  Returns (O, LSE, reused)."""
+    import torch
+    m = _mask(mask, cache.P)
+    if O is None:
+        O = torch.empty((cache.H, cache.N, cache.d), dtype=torch.float32, device=cache.O.device)
+    if LSE is None:
+        LSE = torch.empty((cache.H, cache.N), dtype=torch.float32, device=cache.O.device)
+    for t, shp, nm in ((O, (cache.H, cache.N, cache.d), "O"), (LSE, (cache.H, cache.N), "LSE")):
+        if not (t.is_cuda and t.dtype == torch.float32 and t.is_contiguous() and tuple(t.shape) == shp):
+            raise ValueError(f"{nm} must be a contiguous float32 device tensor of shape {shp}")
+    reused = np.zeros((cache.P, cache.P), dtype=np.uint8)
+    _check(lib.ditango_step(_qkv(Q, cache, "Q"), _qkv(K, cache, "K"), _qkv(V, cache, "V"), _u8(m), int(step),
+                            ctypes.byref(cache.st), ctypes.c_void_p(O.data_ptr()), ctypes.c_void_p(LSE.data_ptr()),
+                            _u8(reused), _stream(stream)))
+    return O, LSE, reused
 
 
 DITANGO_WR_FULL = 0

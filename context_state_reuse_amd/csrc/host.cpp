@@ -315,6 +315,30 @@ int ditango_state_merge(const ditango_states_t* st, float* O, float* LSE, void* 
   return ok();
 }
 
+int ditango_step(const void* Q, const void* K, const void* V, const uint8_t* mask, int32_t step,
+                 ditango_states_t* st, float* O, float* LSE, uint8_t* reused_out, void* stream) {
+  int rc = check_states(st);
+  if (rc) return rc;
+  const int P = st->shape.P;
+  if ((rc = check_mask(mask, P))) return rc;
+  if (!O || !LSE) return fail(DITANGO_EINVAL, "O and LSE must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(O) | reinterpret_cast<uintptr_t>(LSE)) & 15u)
+    return fail(DITANGO_EINVAL, "O and LSE must be 16-byte aligned");
+  if (step < 0) return fail(DITANGO_EINVAL, "step=%d must be >= 0", step);
+  for (int i = 0; i < P * P; ++i) {
+    if (st->tc[i] > step)
+      return fail(DITANGO_EINVAL, "step=%d is earlier than pair %d's last computation step %d", step, i,
+                  st->tc[i]);
+    if (!mask[i] && st->tc[i] < 0)
+      return fail(DITANGO_ENOCACHE, "pair (q=%d, k=%d) is marked REUSE but was never computed", i / P, i % P);
+  }
+  // After the checks above the three calls cannot fail on their arguments;
+  // only a launch error remains, reported as EHIP.
+  if ((rc = ditango_attn_partial(Q, K, V, mask, st, stream))) return rc;
+  if ((rc = ditango_state_cache_update(st, mask, step, reused_out))) return rc;
+  return ditango_state_merge(st, O, LSE, stream);
+}
+
 int ditango_window_residual_merge(const ditango_states_t* st, const uint8_t* window, int32_t mode, float* R,
                                   float* O, float* LSE, void* stream) {
   int rc = check_states(st);

@@ -115,6 +115,15 @@ int ditango_state_cache_update(ditango_states_t* st, const uint8_t* mask, int32_
  * else DITANGO_ENOCACHE.  Errors: EINVAL, ENOCACHE, EHIP. */
 int ditango_state_merge(const ditango_states_t* st, float* O, float* LSE, void* stream);
 
+/* One denoising step of one layer (anchor steps included): the partial
+ * attention of the COMPUTE pairs, the t_c update and the composition, i.e.
+ * ditango_attn_partial, ditango_state_cache_update and ditango_state_merge
+ * in that order on `stream`, with every check done before anything is
+ * launched or any t_c changes.  reused_out as in ditango_state_cache_update
+ * (may be NULL).  Errors: EINVAL, ENOCACHE, EHIP. */
+int ditango_step(const void* Q, const void* K, const void* V, const uint8_t* mask, int32_t step,
+                 ditango_states_t* st, float* O, float* LSE, uint8_t* reused_out, void* stream);
+
 /* Selection-mask builder for the locality policies used by the workloads
  * (state-selection section; locality of Fig. 5a).  Writes uint8 [P][P]:
  *   DITANGO_MASK_ALL      every pair fresh (an anchor step)

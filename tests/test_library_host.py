@@ -189,3 +189,17 @@ def test_window_residual_merge_checks_before_launch():
     assert wr(ctypes.byref(f.st), _u8(win), lib.DITANGO_WR_FULL, None, fake, fake, None) == lib.DITANGO_EINVAL
     odd = ctypes.c_void_p(0x30004)
     assert wr(ctypes.byref(f.st), _u8(win), lib.DITANGO_WR_FULL, odd, fake, fake, None) == lib.DITANGO_EINVAL
+
+
+def test_step_checks_everything_before_work():
+    f = _FakeStates(P=4)
+    fake = ctypes.c_void_p(0x30000)
+    step = binding.lib.ditango_step
+    m1 = radius_mask(4, 1)
+    # a REUSE pair was never computed: refused, t_c untouched
+    assert step(fake, fake, fake, _u8(m1), 0, ctypes.byref(f.st), fake, fake, None, None) == lib.DITANGO_ENOCACHE
+    assert np.all(f.tc == -1)
+    f.tc[:] = 3
+    assert step(fake, fake, fake, _u8(m1), 2, ctypes.byref(f.st), fake, fake, None, None) == lib.DITANGO_EINVAL
+    assert step(fake, fake, fake, _u8(m1), 4, ctypes.byref(f.st), None, fake, None, None) == lib.DITANGO_EINVAL
+    assert np.all(f.tc == 3)
