@@ -54,6 +54,8 @@ int check_shape(const ditango_shape_t* s, int32_t* S_out) {
   if (!(s->scale > 0.0f) || !std::isfinite(s->scale))
     return fail(DITANGO_EINVAL, "scale must be finite and > 0");
   if (s->N < s->P) return fail(DITANGO_EINVAL, "N=%d < P=%d leaves an empty partition", s->N, s->P);
+  if (static_cast<int64_t>(s->N) * s->d > (int64_t{1} << 30))
+    return fail(DITANGO_EINVAL, "N=%d x d=%d exceeds 2^30 elements per head", s->N, s->d);
   const int64_t S = (static_cast<int64_t>(s->N) + s->P - 1) / s->P;
   if (static_cast<int64_t>(s->P - 1) * S >= s->N)
     return fail(DITANGO_EINVAL, "N=%d, P=%d: partitions of %lld tokens leave the last one empty",

@@ -32,8 +32,9 @@
 // Block = 4 or 8 waves of 32 query rows each (128 or 256 rows), two waves
 // per SIMD (<= 256 VGPRs each, no accumulator spills to AGPRs), so a SIMD
 // can issue one wave's softmax while the other's MFMAs run.  K/V tiles of 64
-// keys are double-buffered in LDS and filled by direct global-to-LDS loads:
-// the next tile's loads are in flight while the current tile is multiplied.
+// keys are double-buffered in LDS and filled by direct buffer-to-LDS loads
+// (buffer_load ... lds): the next tile's loads are in flight while the
+// current tile is multiplied.
 // The grid is the compacted list of fresh work items: no block exists for a
 // reused pair.
 
@@ -55,6 +56,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 
+// Direct tile loads as buffer_load ... lds (1) or global_load_lds (0).
+#ifndef DITANGO_BUFFER_LDS
+#define DITANGO_BUFFER_LDS 1
+#endif
 #ifndef DITANGO_ONES_ROW
 #define DITANGO_ONES_ROW 1
 #endif
@@ -81,7 +86,7 @@ struct Geometry {
   // rows x 64 B: a stride of 16 or 48 (mod 64) dwords puts those rows on
   // disjoint banks.
   //
-  // Direct layout: filled by global_load_lds_dwordx4 (a wave writes 64
+  // Direct layout: filled by 16-byte direct loads to LDS (a wave writes 64
   // consecutive 16-byte chunks, so a row's stride is a whole number of
   // chunks).  For d = 64 and 128 rows are unpadded and the 16-byte chunk c
   // of row r sits at position c ^ f(r); the global load of position p
@@ -472,7 +477,7 @@ void partial_kernel(const PartialParams p) {
   // Tile transfers.  gload(kt_k, kt_v) starts fetching K tile kt_k and V
   // tile kt_v (-1: none); swrite(kbuf, vbuf) completes them into those LDS
   // buffers.  Direct layout: gload itself streams global memory into the
-  // buffers (global_load_lds_dwordx4) and swrite only waits for it; the
+  // buffers (16-byte direct loads to LDS) and swrite only waits for it; the
   // buffers passed to swrite must be the ones given to the matching gload.
   // Staged layout: gload fills registers and swrite stores them.
 
@@ -520,15 +525,34 @@ void partial_kernel(const PartialParams p) {
       return base + static_cast<size_t>(j) * D + (goff - r * D);
     }
   };
+  // Buffer descriptors over this item's keys, from token k0 to the end of the
+  // sequence (fewer than 2^31 bytes: the host limits N * d to 2^30).  The
+  // direct loads go through buffer_load ... lds: the compiler's wait-count
+  // tracking keeps its LDS writes apart from the operand reads, whereas a
+  // global_load_lds in flight makes it wait for every outstanding LDS read
+  // before each use (+7-8% at d = 72 and 128).  Offsets past the end read 0.
+  const int kv_bytes = (p.N - k0) * D * 2;
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(Kh), 0, kv_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(Vh), 0, kv_bytes, 0x00020000);
+  auto dma = [&](__amdgpu_buffer_rsrc_t rsrc, const __bf16* base, const __bf16* src, __bf16* dst)
+                 __attribute__((always_inline)) {
+#if DITANGO_BUFFER_LDS
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)dst, 16,
+                                             static_cast<int>(src - base) * 2, 0, 0, 0);
+#else
+    (void)rsrc;
+    (void)base;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+#endif
+  };
   auto gload_direct = [&](int kt_k, __bf16* kdst, int kt_v, __bf16* vdst) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < (G::direct ? kRoundsK : 0); ++i) {
       if (kGroupsK % WAVES != 0 && i * WAVES + swave >= kGroupsK) break;   // wave-uniform
       const int lds_elem0 = (i * WAVES + swave) * 64 * 8;   // first element this wave writes
       if (kt_k >= 0) {
-        const __bf16* src = tile_src(Kh, kt_k, krow_of[i], kgoff[i]);
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                         (__attribute__((address_space(3))) void*)(kdst + lds_elem0), 16, 0, 0);
+        dma(krsrc, Kh, tile_src(Kh, kt_k, krow_of[i], kgoff[i]), kdst + lds_elem0);
       }
     }
 #pragma unroll
@@ -536,9 +560,7 @@ void partial_kernel(const PartialParams p) {
       if (kGroupsV % WAVES != 0 && i * WAVES + swave >= kGroupsV) break;   // wave-uniform
       const int lds_elem0 = (i * WAVES + swave) * 64 * 8;
       if (kt_v >= 0 && (G::vcpr == D / 8 || vgoff[i] >= 0)) {
-        const __bf16* src = tile_src(Vh, kt_v, vrow_of[i], vgoff[i]);
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                         (__attribute__((address_space(3))) void*)(vdst + lds_elem0), 16, 0, 0);
+        dma(vrsrc, Vh, tile_src(Vh, kt_v, vrow_of[i], vgoff[i]), vdst + lds_elem0);
       }
     }
   };

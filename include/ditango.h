@@ -53,7 +53,7 @@ extern "C" {
  * every partition must be non-empty (P * ceil(N/P) - N < ceil(N/P)). */
 typedef struct {
   int32_t H;      /* attention heads                                   */
-  int32_t N;      /* tokens in the flattened sequence                  */
+  int32_t N;      /* tokens in the flattened sequence; N * d <= 2^30   */
   int32_t d;      /* head dimension                                    */
   int32_t P;      /* partitions                                        */
   float   scale;  /* score scale applied to q.k, normally 1/sqrt(d)    */

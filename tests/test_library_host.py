@@ -78,11 +78,19 @@ def test_mask_builder_rejects(args):
 
 
 @pytest.mark.parametrize("H,N,d,P", [(1, 10, 96, 2), (1, 10, 64, 0), (1, 10, 64, 33), (0, 10, 64, 2),
-                                     (1, 3, 64, 4), (1, 10, 64, 6)])
+                                     (1, 3, 64, 4), (1, 10, 64, 6), (1, 2**30 // 128 + 1, 128, 8),
+                                     (1, 2**30 // 72 + 1, 72, 8)])
 def test_shape_rejected(H, N, d, P):
     ob = ctypes.c_size_t(0)
     assert binding.lib.ditango_states_bytes(ctypes.byref(lib.make_shape(H, N, d, P)), ctypes.byref(ob), None) == 0
     assert binding.lib.ditango_last_error()
+
+
+def test_shape_at_the_size_limit_accepted():
+    # K/V of one head are addressed with 32-bit byte offsets: N * d <= 2^30
+    ob = ctypes.c_size_t(0)
+    assert binding.lib.ditango_states_bytes(ctypes.byref(lib.make_shape(1, 2**30 // 128, 128, 8)),
+                                            ctypes.byref(ob), None) > 0
 
 
 class _FakeStates:
