@@ -51,6 +51,21 @@ def _run(cmd: list[str]) -> None:
         print(out, file=sys.stderr)
 
 
+def _check_kernel_stubs(path: str) -> None:
+    """The host pass can drop a kernel's launch stub without a diagnostic
+    (device code it cannot compile for the host); the library would then
+    fail to load.  Reject it here with the kernels named."""
+    nm = shutil.which("nm")
+    if nm is None:
+        return
+    r = subprocess.run([nm, "-D", "-C", "--undefined-only", path], stdout=subprocess.PIPE,
+                       stderr=subprocess.STDOUT, text=True)
+    missing = [ln.split("U", 1)[-1].strip() for ln in r.stdout.splitlines() if "__device_stub__" in ln]
+    if missing:
+        os.remove(path)
+        raise RuntimeError("kernel launch stubs missing from the host code:\n  " + "\n  ".join(missing))
+
+
 def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     """Compile every source and link `out`.  `defines` (e.g. ["X=1"]) build
     a variant library for side-by-side measurement."""
@@ -68,6 +83,7 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
             f.result()
     tmp = out + ".tmp"
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *[o for _, o in jobs]])
+    _check_kernel_stubs(tmp)
     os.replace(tmp, out)
     if verbose:
         print(f"built {out}")

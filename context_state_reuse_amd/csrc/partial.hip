@@ -30,11 +30,11 @@
 // rescaled.  The final division by the row sum makes the result exact.
 //
 // Block = 4 or 8 waves of 32 query rows each (128 or 256 rows), two waves
-// per SIMD (<= 256 VGPRs each, no accumulator spills to AGPRs), so a SIMD
-// can issue one wave's softmax while the other's MFMAs run.  K/V tiles of 64
-// keys are double-buffered in LDS and filled by direct buffer-to-LDS loads
-// (buffer_load ... lds): the next tile's loads are in flight while the
-// current tile is multiplied.
+// per SIMD (<= 256 VGPRs each, no accumulator spills to AGPRs; three at
+// d = 64), so a SIMD can issue one wave's softmax while another's MFMAs
+// run.  K/V tiles of 64 keys are double-buffered in LDS and filled by
+// direct buffer-to-LDS loads (buffer_load ... lds): the next tile's loads
+// are in flight while the current tile is multiplied.
 // The grid is the compacted list of fresh work items: no block exists for a
 // reused pair.
 
@@ -329,17 +329,38 @@ __device__ __attribute__((always_inline)) inline void tile_pv(WaveState<D, NQT, 
   }
 }
 
+// One 16-byte chunk per lane of a key tile into LDS (buffer_load ... lds):
+// the descriptor starts at the tile's first key t0 of `base` (rows of d
+// bf16) and ends at key `len`, so a lane's offset is its fixed element
+// offset `elem` in the tile and rows at or past `len` read zeros.  Built
+// here rather than in the kernel's lambdas, which are also compiled for the
+// host, where the descriptor builtin does not exist.
+template <int D>
+__device__ __attribute__((always_inline)) inline void tile_load_lds(const __bf16* base, int t0, int len, int elem,
+                                                                    __bf16* dst) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<__bf16*>(base) + static_cast<size_t>(t0) * D, 0, (len - t0) * D * 2, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, elem * 2, 0, 0, 0);
+}
+
+// Waves per SIMD: two (<= 256 VGPRs each) for d = 72 and 128.  d = 64 fits
+// in 168 VGPRs and runs 4-wave blocks at three waves per SIMD (three blocks
+// per CU): the third wave keeps the VALU issuing while the others wait
+// (+7-11% on the 32-partition d = 64 workload; four spill).
+#ifndef DITANGO_D64_WAVES_PER_SIMD
+#define DITANGO_D64_WAVES_PER_SIMD 3
+#endif
+template <int D, int NQT, int WAVES>
+constexpr int waves_per_simd() { return NQT == 2 ? 1 : (D == 64 && WAVES == 4 ? DITANGO_D64_WAVES_PER_SIMD : 2); }
+
 // Block = WAVES waves, each owning NQT column tiles of 32 queries.  NQT = 1
 // runs two waves per SIMD (<= 256 registers each); NQT = 2 halves the LDS
 // operand traffic per MFMA and runs one wave per SIMD.  K/V tiles of 64 keys
 // are double-buffered in LDS: the next tile's global loads are in flight
 // while the current tile is multiplied; one barrier per tile.
-template <int D, int NQT>
-constexpr int waves_per_simd() { return NQT == 2 ? 1 : 2; }
-
 template <int D, int WAVES, int NQT, int SCHED, int BC, bool GROUPED>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
-                          amdgpu_waves_per_eu(waves_per_simd<D, NQT>(), waves_per_simd<D, NQT>())))
+                          amdgpu_waves_per_eu(waves_per_simd<D, NQT, WAVES>(), waves_per_simd<D, NQT, WAVES>())))
 void partial_kernel(const PartialParams p) {
   using G = Geometry<D>;
   constexpr int kBc = BC;                          // keys per K/V tile (32, 64 or 128)
@@ -546,13 +567,22 @@ void partial_kernel(const PartialParams p) {
                                      (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
 #endif
   };
+  // Per-pair items with buffer loads: a descriptor per tile, based at the
+  // tile's first key and ending at the item's last key (scalar arithmetic),
+  // so each lane's offset is its fixed in-tile offset and rows past the last
+  // key read zeros (their scores are masked).  No per-lane address math.
+  constexpr bool kTileRsrc = DITANGO_BUFFER_LDS && !GROUPED;
   auto gload_direct = [&](int kt_k, __bf16* kdst, int kt_v, __bf16* vdst) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < (G::direct ? kRoundsK : 0); ++i) {
       if (kGroupsK % WAVES != 0 && i * WAVES + swave >= kGroupsK) break;   // wave-uniform
       const int lds_elem0 = (i * WAVES + swave) * 64 * 8;   // first element this wave writes
       if (kt_k >= 0) {
-        dma(krsrc, Kh, tile_src(Kh, kt_k, krow_of[i], kgoff[i]), kdst + lds_elem0);
+        if constexpr (kTileRsrc) {
+          tile_load_lds<D>(Kh, kt_k * kBc, len_k, kgoff[i], kdst + lds_elem0);
+        } else {
+          dma(krsrc, Kh, tile_src(Kh, kt_k, krow_of[i], kgoff[i]), kdst + lds_elem0);
+        }
       }
     }
 #pragma unroll
@@ -560,7 +590,11 @@ void partial_kernel(const PartialParams p) {
       if (kGroupsV % WAVES != 0 && i * WAVES + swave >= kGroupsV) break;   // wave-uniform
       const int lds_elem0 = (i * WAVES + swave) * 64 * 8;
       if (kt_v >= 0 && (G::vcpr == D / 8 || vgoff[i] >= 0)) {
-        dma(vrsrc, Vh, tile_src(Vh, kt_v, vrow_of[i], vgoff[i]), vdst + lds_elem0);
+        if constexpr (kTileRsrc) {
+          tile_load_lds<D>(Vh, kt_v * kBc, len_k, vgoff[i], vdst + lds_elem0);
+        } else {
+          dma(vrsrc, Vh, tile_src(Vh, kt_v, vrow_of[i], vgoff[i]), vdst + lds_elem0);
+        }
       }
     }
   };
@@ -787,6 +821,7 @@ int partial_rows_per_block(int d, int S) {
   const int qpw = d == 128 ? DITANGO_D128_QPW : 32;
   const int wide = 4 * 2 * 32, narrow = 4 * 32;   // 8 or 4 column tiles per block
   (void)qpw;
+  if (d == 64 && DITANGO_D64_WAVES_PER_SIMD > 2) return narrow;   // 4-wave blocks, three per CU
   // 256 rows per block unless 128-row blocks waste clearly less of a ragged
   // partition (e.g. S = 549: 3 x 256 rows hold 71% useful work, 5 x 128 hold 86%).
   const long waste_w = (S + wide - 1) / wide * static_cast<long>(wide) - S;
