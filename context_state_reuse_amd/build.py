@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libditango.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["host.cpp", "partial.hip", "merge.hip"]
+SOURCES = ["host.cpp", "partial.hip", "merge.hip", "stats.hip"]
 ARCH = "gfx950"
 
 

@@ -184,7 +184,7 @@ extern "C" {
 
 const char* ditango_last_error(void) { return g_err.c_str(); }
 
-int32_t ditango_version(void) { return 2; }
+int32_t ditango_version(void) { return 3; }
 
 size_t ditango_states_bytes(const ditango_shape_t* shape, size_t* o_bytes, size_t* lse_bytes) {
   int32_t S = 0;
@@ -314,6 +314,207 @@ int ditango_state_merge(const ditango_states_t* st, float* O, float* LSE, void* 
   m.d = st->shape.d;
   hipError_t e = ditango::launch_merge(m, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(DITANGO_EHIP, "merge kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int ditango_pair_stats(const ditango_states_t* st, const float* LSE, const uint8_t* select, float* W, float* SIG,
+                       void* stream) {
+  int rc = check_states(st);
+  if (rc) return rc;
+  const int P = st->shape.P;
+  if ((rc = check_mask(select, P))) return rc;
+  if (!LSE || !W) return fail(DITANGO_EINVAL, "LSE and W must be non-NULL");
+  bool any = false;
+  for (int i = 0; i < P * P; ++i) any |= select[i] != 0;
+  if (any && !SIG) return fail(DITANGO_EINVAL, "SIG must be non-NULL when pairs are selected");
+  if (reinterpret_cast<uintptr_t>(SIG) & 15u) return fail(DITANGO_EINVAL, "SIG must be 16-byte aligned");
+  for (int i = 0; i < P * P; ++i)
+    if (st->tc[i] < 0) return fail(DITANGO_ENOCACHE, "pair (q=%d, k=%d) holds no state", i / P, i % P);
+  ditango::StatsParams sp;
+  std::memset(&sp, 0, sizeof sp);
+  sp.O = st->O;
+  sp.LSE_slot = st->LSE;
+  sp.LSE = LSE;
+  sp.W = W;
+  sp.SIG = SIG;
+  for (int q = 0; q < P; ++q)
+    for (int k = 0; k < P; ++k)
+      if (select[q * P + k]) sp.sel[q] |= 1u << k;
+  sp.H = st->shape.H;
+  sp.N = st->shape.N;
+  sp.P = P;
+  sp.S = st->S;
+  sp.d = st->shape.d;
+  hipError_t e = ditango::launch_stats(sp, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DITANGO_EHIP, "stats kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// ---- anchor-guided planner (host only) ----
+//
+// DiTango page, error-analysis and state-selection sections (Eq. 5-9,
+// Algorithm 1): ASE of a cached state = importance w times an error that
+// grows with the cache age; groups (local state apart, always computed) are
+// computed when their summed ASE exceeds eps, reused otherwise; anchor steps
+// compute everything when the local state drifts too far, and re-measure w,
+// the scale ratios alpha and eps.  The page's equations are lost; the
+// concrete model (signature drift, alpha = pair drift / local drift, eps as
+// the target-reuse quantile of the errors corrected at the anchor) is the one
+// stated in ditango.h.
+
+namespace {
+
+// ||new - ref|| / ||ref|| over the heads' signatures of one pair; 0 when both
+// are zero, infinity when only ref is.
+double sig_drift(const float* a, int a_hs, const float* b, int b_hs, int H, int d) {
+  double num = 0.0, den = 0.0;
+  for (int h = 0; h < H; ++h)
+    for (int c = 0; c < d; ++c) {
+      const double x = a[static_cast<size_t>(h) * a_hs + c], y = b[static_cast<size_t>(h) * b_hs + c];
+      num += (x - y) * (x - y);
+      den += y * y;
+    }
+  if (den == 0.0) return num == 0.0 ? 0.0 : HUGE_VAL;
+  return std::sqrt(num) / std::sqrt(den);
+}
+
+int planner_groups(const ditango_planner_t* pl) { return (pl->P + pl->g - 1) / pl->g; }
+
+// Members of group j for query partition q: [j g, min((j+1) g, P)) without q.
+int group_members(const ditango_planner_t* pl, int q, int j, int* out) {
+  int n = 0;
+  for (int k = j * pl->g; k < std::min((j + 1) * pl->g, pl->P); ++k)
+    if (k != q) out[n++] = k;
+  return n;
+}
+
+int check_planner(const ditango_planner_t* pl) {
+  if (!pl) return fail(DITANGO_EINVAL, "planner is NULL");
+  if (pl->P < 1 || pl->P > DITANGO_MAX_P || pl->g < 1 || pl->g > pl->P || pl->H < 1 || pl->d < 1 || !pl->sigref)
+    return fail(DITANGO_EINVAL, "planner is not initialised");
+  return DITANGO_OK;
+}
+
+}  // namespace
+
+int ditango_planner_init(ditango_planner_t* pl, int32_t P, int32_t g, int32_t H, int32_t d, float target_reuse,
+                         float drift_max, int32_t warmup, float* sigref) {
+  if (!pl || !sigref) return fail(DITANGO_EINVAL, "planner and sigref must be non-NULL");
+  if (P < 1 || P > DITANGO_MAX_P) return fail(DITANGO_EINVAL, "P=%d outside 1..%d", P, DITANGO_MAX_P);
+  if (g < 1 || g > P) return fail(DITANGO_EINVAL, "group size g=%d outside 1..P", g);
+  if (H < 1 || d < 1) return fail(DITANGO_EINVAL, "H=%d and d=%d must be >= 1", H, d);
+  if (!(target_reuse >= 0.0f && target_reuse <= 1.0f)) return fail(DITANGO_EINVAL, "target_reuse outside [0, 1]");
+  if (!(drift_max >= 0.0f)) return fail(DITANGO_EINVAL, "drift_max must be >= 0");
+  if (warmup < 2) return fail(DITANGO_EINVAL, "warmup=%d must be >= 2", warmup);
+  std::memset(pl, 0, sizeof *pl);
+  pl->P = P;
+  pl->g = g;
+  pl->H = H;
+  pl->d = d;
+  pl->target_reuse = target_reuse;
+  pl->drift_max = drift_max;
+  pl->warmup = warmup;
+  pl->eps = HUGE_VAL;
+  pl->sigref = sigref;
+  return ok();
+}
+
+int ditango_planner_plan(ditango_planner_t* pl, int32_t step, const float* sig, uint8_t* mask_out,
+                         int32_t* anchor_out) {
+  int rc = check_planner(pl);
+  if (rc) return rc;
+  if (!sig || !mask_out) return fail(DITANGO_EINVAL, "sig and mask_out must be non-NULL");
+  if (step < 0) return fail(DITANGO_EINVAL, "step=%d must be >= 0", step);
+  const int P = pl->P, d = pl->d, H = pl->H;
+  const int sig_hs = P * P * d;    // head stride of sig [H][P][P][d]
+  double dmax = 0.0;
+  for (int q = 0; q < P; ++q) {
+    pl->D[q] = pl->has_ref ? sig_drift(sig + static_cast<size_t>(q * P + q) * d, sig_hs, pl->sigref + static_cast<size_t>(q) * d,
+                                       P * d, H, d)
+                           : 0.0;
+    dmax = std::max(dmax, pl->D[q]);
+  }
+  pl->anchor = step < pl->warmup || !pl->has_ref || dmax > pl->drift_max;
+  if (anchor_out) *anchor_out = pl->anchor;
+  if (pl->anchor) {
+    std::memset(mask_out, 1, static_cast<size_t>(P) * P);
+    return ok();
+  }
+  std::memset(mask_out, 0, static_cast<size_t>(P) * P);
+  for (int q = 0; q < P; ++q) {
+    mask_out[q * P + q] = 1;
+    for (int j = 0; j < planner_groups(pl); ++j) {
+      int mem[DITANGO_MAX_P];
+      const int n = group_members(pl, q, j, mem);
+      if (n == 0) continue;
+      const double grow = std::max(0.0, pl->D[q] - pl->Dc[q][j]);
+      double ase = 0.0;
+      for (int i = 0; i < n; ++i) ase += pl->W[q][mem[i]] * pl->alpha[q][mem[i]] * grow;
+      if (ase > pl->eps)
+        for (int i = 0; i < n; ++i) mask_out[q * P + mem[i]] = 1;
+    }
+  }
+  return ok();
+}
+
+int ditango_planner_update(ditango_planner_t* pl, int32_t step, const uint8_t* mask, const float* W,
+                           const float* sig_new, const float* sig_old) {
+  int rc = check_planner(pl);
+  if (rc) return rc;
+  const int P = pl->P, d = pl->d, H = pl->H;
+  if ((rc = check_mask(mask, P))) return rc;
+  if (!W || !sig_new) return fail(DITANGO_EINVAL, "W and sig_new must be non-NULL");
+  if (step < 0) return fail(DITANGO_EINVAL, "step=%d must be >= 0", step);
+  const int sig_hs = P * P * d;
+  if (pl->anchor) {
+    for (int q = 0; q < P; ++q)
+      for (int k = 0; k < P; ++k) {
+        double s = 0.0;
+        for (int h = 0; h < H; ++h) s += W[(static_cast<size_t>(h) * P + q) * P + k];
+        pl->W[q][k] = s / H;
+      }
+    if (sig_old && pl->has_ref) {
+      double e[DITANGO_MAX_P][DITANGO_MAX_P] = {};
+      for (int q = 0; q < P; ++q)
+        for (int k = 0; k < P; ++k) {
+          if (k == q) continue;
+          const size_t off = static_cast<size_t>(q * P + k) * d;
+          e[q][k] = sig_drift(sig_new + off, sig_hs, sig_old + off, sig_hs, H, d);
+          pl->alpha[q][k] = pl->D[q] > 0.0 ? e[q][k] / pl->D[q] : 0.0;
+        }
+      std::vector<double> E;
+      for (int q = 0; q < P; ++q)
+        for (int j = 0; j < planner_groups(pl); ++j) {
+          int mem[DITANGO_MAX_P];
+          const int n = group_members(pl, q, j, mem);
+          if (n == 0) continue;
+          double s = 0.0;
+          for (int i = 0; i < n; ++i) s += pl->W[q][mem[i]] * e[q][mem[i]];
+          E.push_back(s);
+        }
+      std::sort(E.begin(), E.end());
+      const long kq = E.empty() ? 0 : static_cast<long>(std::ceil(pl->target_reuse * static_cast<double>(E.size()) - 1e-12));
+      pl->eps = E.empty() ? HUGE_VAL : kq <= 0 ? -HUGE_VAL : E[std::min<size_t>(kq, E.size()) - 1];
+    }
+    for (int h = 0; h < H; ++h)
+      for (int q = 0; q < P; ++q)
+        std::memcpy(pl->sigref + (static_cast<size_t>(h) * P + q) * d,
+                    sig_new + static_cast<size_t>(h) * sig_hs + static_cast<size_t>(q * P + q) * d, sizeof(float) * d);
+    pl->has_ref = 1;
+    for (int q = 0; q < P; ++q)
+      for (int j = 0; j < DITANGO_MAX_P; ++j) pl->Dc[q][j] = 0.0;
+    pl->n_anchors += 1;
+    pl->last_anchor = step;
+  } else {
+    for (int q = 0; q < P; ++q)
+      for (int j = 0; j < planner_groups(pl); ++j) {
+        int mem[DITANGO_MAX_P];
+        const int n = group_members(pl, q, j, mem);
+        bool all = n > 0;
+        for (int i = 0; i < n; ++i) all = all && mask[q * P + mem[i]];
+        if (all) pl->Dc[q][j] = pl->D[q];
+      }
+  }
   return ok();
 }
 

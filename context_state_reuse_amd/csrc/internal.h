@@ -1,5 +1,5 @@
 // Internal interface between the host half of the library (host.cpp) and the
-// HIP kernels (partial.hip, merge.hip).  Not part of the C ABI.
+// HIP kernels (partial.hip, merge.hip, stats.hip).  Not part of the C ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -70,6 +70,20 @@ struct MergeParams {
   int32_t H, N, P, S, d;
 };
 
+// Per-pair statistics of the per-pair cache for the anchor-guided planner:
+// for every pair (q, k) and head h, W[h][q][k] = mean over q's rows r of
+// exp(LSE_slot[r] - LSE[q*S + r]); for the pairs with bit k of sel[q] set,
+// SIG[h][q][k][0..d) = mean over q's rows of OUT_slot.
+struct StatsParams {
+  const float* O;           // per-pair cache [H][P*P][S][d]
+  const float* LSE_slot;    // [H][P*P][S]
+  const float* LSE;         // merged [H][N]
+  float* W;                 // [H][P][P]
+  float* SIG;               // [H][P][P][d]
+  uint32_t sel[DITANGO_MAX_P];
+  int32_t H, N, P, S, d;
+};
+
 // Query rows handled by one block of the partial kernel for head dim d
 // (chosen by the launcher); the host uses it to size the grid.
 int partial_rows_per_block(int d, int S);
@@ -77,5 +91,6 @@ int partial_rows_per_block(int d, int S);
 // Enqueue kernels; return hipSuccess or the launch error.
 hipError_t launch_partial(PartialParams& p, int rows_per_block, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
+hipError_t launch_stats(const StatsParams& p, hipStream_t stream);
 
 }  // namespace ditango

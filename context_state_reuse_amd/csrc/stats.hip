@@ -1,0 +1,90 @@
+// Per-pair statistics of the state cache for the anchor-guided planner
+// (DiTango page, error-analysis and state-selection sections):
+//   W[h][q][k]   = mean over the rows r of query partition q of
+//                  exp(LSE_qk[r] - LSE[r]) -- the normalised weight of
+//                  partition k in the composed state, i.e. the share of q's
+//                  attention mass on k's keys (the importance w of the
+//                  error model);
+//   SIG[h][q][k] = mean over q's rows of OUT_qk, for the selected pairs --
+//                  the signature on which the planner measures how far a
+//                  state has drifted.
+// One block per (head, q, k), 256 threads; every sum is taken in a fixed
+// order (per-thread strided partial sums, then a fixed tree), so results do
+// not vary from run to run.  Reads the LSE of every slot and the OUT of the
+// selected ones: a few per cent of one merge.
+
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+
+namespace ditango {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void stats_kernel(const StatsParams p) {
+  constexpr int C = D / 4;                  // 16-byte chunks per row
+  constexpr int RG = kThreads / C;          // rows summed in parallel
+  __shared__ f32x4 part[RG][C];
+  __shared__ float wpart[kThreads / 64];
+
+  const int tid = threadIdx.x;
+  const int pair = blockIdx.x % (p.P * p.P);
+  const int h = blockIdx.x / (p.P * p.P);
+  const int q = pair / p.P, k = pair % p.P;
+  const int len_q = min(p.S, p.N - q * p.S);
+  const size_t slot = static_cast<size_t>(h) * p.P * p.P + pair;
+  const float* ls = p.LSE_slot + slot * p.S;
+  const float* lm = p.LSE + static_cast<size_t>(h) * p.N + static_cast<size_t>(q) * p.S;
+
+  // importance
+  float acc = 0.0f;
+  for (int r = tid; r < len_q; r += kThreads) acc += __expf(ls[r] - lm[r]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if ((tid & 63) == 0) wpart[tid >> 6] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kThreads / 64; ++i) s += wpart[i];
+    p.W[slot] = s / static_cast<float>(len_q);
+  }
+
+  // signature (block-uniform branch)
+  if (!((p.sel[q] >> k) & 1u)) return;
+  const float* o = p.O + slot * p.S * D;
+  const int rg = tid / C, c = tid % C;
+  f32x4 a = {0.f, 0.f, 0.f, 0.f};
+  if (rg < RG) {
+    for (int r = rg; r < len_q; r += RG) a += *reinterpret_cast<const f32x4*>(o + static_cast<size_t>(r) * D + 4 * c);
+    part[rg][c] = a;
+  }
+  __syncthreads();
+  if (tid < C) {
+    f32x4 s = part[0][tid];
+    for (int i = 1; i < RG; ++i) s += part[i][tid];
+    const float inv = 1.0f / static_cast<float>(len_q);
+    *reinterpret_cast<f32x4*>(p.SIG + slot * D + 4 * tid) = s * inv;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_stats(const StatsParams& p, hipStream_t stream) {
+  const int64_t blocks = static_cast<int64_t>(p.H) * p.P * p.P;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+  switch (p.d) {
+    case 64: hipLaunchKernelGGL(stats_kernel<64>, grid, block, 0, stream, p); break;
+    case 72: hipLaunchKernelGGL(stats_kernel<72>, grid, block, 0, stream, p); break;
+    case 128: hipLaunchKernelGGL(stats_kernel<128>, grid, block, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ditango

@@ -258,10 +258,86 @@ int ditango_group_reset(ditango_gstates_t* st, float* const* O, float* const* LS
  * EINVAL (P outside 1..32, g < 1, n < 0). */
 int ditango_group_mask_build(int32_t P, int32_t g, int32_t n, uint8_t* mask_out);
 
+/* ---- Anchor-guided selection (planner) ----
+ *
+ * Error-analysis and state-selection sections (Eq. 5-9, Algorithm 1): the
+ * Attention State Error of a cached state is its importance w (its
+ * normalised composition weight) times an error that grows with its cache
+ * age; per query partition the KV partitions are grouped (groups of g
+ * adjacent partitions, the local one apart and always computed), a group is
+ * computed when the sum of its members' ASE exceeds a threshold eps and
+ * reused otherwise; anchor steps compute everything, are triggered when the
+ * local state drifts too far, and re-measure w, the scale ratios alpha and
+ * eps (a percentile of the errors corrected at the anchor, set by a target
+ * reuse fraction).  The page's equations are lost in extraction; this
+ * library's model:
+ *   signature of a pair state: the mean of its OUT rows, per head (d values);
+ *   drift(a, b) = ||a - b|| / ||b|| over the heads' signatures concatenated;
+ *   D(q, t): drift of q's local signature at step t against the last anchor;
+ *   anchor at step < warmup (>= 2) or when max_q D(q, t) > drift_max;
+ *   at an anchor: w(q,k) = pair importance averaged over heads, e(q,k) =
+ *   drift of the pair's signature against the one cached before the step,
+ *   alpha(q,k) = e(q,k) / D(q,t) (0 if D = 0), E(q,G) = sum over members of
+ *   w e, eps = the ceil(target_reuse * n)-th smallest of the n values E
+ *   (-inf if that is 0); per-group records Dc(q,G) = 0;
+ *   between anchors: ASE(q,G) = sum over members k of w(q,k) alpha(q,k)
+ *   max(0, D(q,t) - Dc(q,G)); G is computed iff ASE > eps, and then
+ *   Dc(q,G) = D(q,t).
+ * Groups: G_j = {j g .. min((j+1) g, P) - 1} without q; empty ones skipped. */
+
+/* Per-pair statistics of the cache after a step's merge, on `stream`:
+ *   W   device fp32 [H][P][P]: W[h][q][k] = mean over q's rows r of
+ *       exp(LSE_slot(h,q,k)[r] - LSE[h][q*S + r]) for every pair -- the
+ *       share of q's attention mass on k's keys;
+ *   SIG device fp32 [H][P][P][d], 16-byte aligned: for the pairs with
+ *       select[q][k] = 1 (host uint8 [P][P]) the mean of the slot's OUT rows;
+ *       other entries are not touched (SIG may be NULL if none is selected).
+ * LSE is the merged device fp32 [H][N] of the same cache contents.  Every
+ * pair must hold a state.  Errors: EINVAL, ENOCACHE, EHIP. */
+int ditango_pair_stats(const ditango_states_t* st, const float* LSE, const uint8_t* select, float* W, float* SIG,
+                       void* stream);
+
+/* Planner state (host only; every field is set by ditango_planner_init and
+ * kept by the calls below).  sigref is a caller-owned host fp32 [H][P][d]
+ * buffer (local signatures at the last anchor). */
+typedef struct {
+  int32_t P, g, H, d, warmup;
+  float   target_reuse;   /* share of groups to reuse at the anchor error level, 0..1 */
+  float   drift_max;      /* anchor when a local state drifts more than this */
+  int32_t anchor;         /* decision of the last ditango_planner_plan */
+  int32_t has_ref, n_anchors, last_anchor;
+  double  eps;
+  double  D[DITANGO_MAX_P];
+  double  W[DITANGO_MAX_P][DITANGO_MAX_P];
+  double  alpha[DITANGO_MAX_P][DITANGO_MAX_P];
+  double  Dc[DITANGO_MAX_P][DITANGO_MAX_P];   /* [q][group] */
+  float*  sigref;
+} ditango_planner_t;
+
+/* Errors: EINVAL (P outside 1..32, g outside 1..P, H or d < 1, target_reuse
+ * outside [0, 1], drift_max < 0, warmup < 2, NULL pointers). */
+int ditango_planner_init(ditango_planner_t* pl, int32_t P, int32_t g, int32_t H, int32_t d, float target_reuse,
+                         float drift_max, int32_t warmup, float* sigref);
+
+/* Mask for step `step` (host uint8 [P][P], 1 = compute) from the signatures
+ * of the freshly computed local states: sig host fp32 [H][P][P][d], only the
+ * diagonal entries are read (compute the local pairs first, then their
+ * signatures with ditango_pair_stats).  *anchor_out (may be NULL) = 1 for an
+ * anchor step (mask all ones).  Errors: EINVAL. */
+int ditango_planner_plan(ditango_planner_t* pl, int32_t step, const float* sig, uint8_t* mask_out,
+                         int32_t* anchor_out);
+
+/* After step `step` ran with `mask`: W host fp32 [H][P][P] and sig_new host
+ * fp32 [H][P][P][d] of the cache after the step (ditango_pair_stats with
+ * select = mask), sig_old the signatures of the cache before the step (host,
+ * same layout; NULL at the first step).  Errors: EINVAL. */
+int ditango_planner_update(ditango_planner_t* pl, int32_t step, const uint8_t* mask, const float* W,
+                           const float* sig_new, const float* sig_old);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* ditango_last_error(void);
 
-/* Library ABI version (this header: 2). */
+/* Library ABI version (this header: 3). */
 int32_t ditango_version(void);
 
 #ifdef __cplusplus

@@ -1,0 +1,137 @@
+"""GPU parity of the planner's statistics and of planned steps.
+
+* ditango_pair_stats against the oracle's importance and signatures, taken
+  from the oracle's own cache of the same steps (reduced workloads, ragged
+  partitions, the three head dims).  Bar: W abs <= 2e-3 (an LSE error of
+  1e-3 in the slot and in the merged LSE moves exp(LSE_k - LSE) by at most
+  about 2e-3 relative, and W <= 1); SIG max-abs <= 2e-2 and mean-abs <= 2e-3
+  (a mean of OUT rows errs by at most OUT's bound).
+* planned steps: the library's planner picks each step's mask on the GPU
+  statistics; every mask keeps the local pairs and whole groups, and the
+  outputs match the oracle run with the same masks to the per-pair bar.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle.planner import group_members, pair_signature, pair_weights
+from oracle.reuse import StateReuseOracle
+
+from gpu_run import log, to_device
+
+pytestmark = pytest.mark.gpu
+
+TOL_W, TOL_SIG_MAX, TOL_SIG_MEAN = 2e-3, 2e-2, 2e-3
+TOL_O_MAX, TOL_O_MEAN, TOL_LSE = 2e-2, 2e-3, 1e-3
+
+
+def _scaled(base, name, F, Hh, W, H, **kw):
+    return synth.get(base).scaled(name=name, F=F, Hh=Hh, W=W, H=H, **kw)
+
+
+CASES = [
+    _scaled("image", "image_small", 1, 57, 97, 2),            # d=72, ragged last partition
+    _scaled("video_25", "video25_small", 5, 21, 29, 2),       # d=128
+    _scaled("stress", "stress_small", 5, 16, 27, 2),          # d=64, P=32
+]
+
+
+def _oracle_stats(w, orc_cache, merged_lse):
+    """Expected W [H][P][P] and SIG [H][P][P][d] from the oracle's cache."""
+    P, S = w.P, w.S
+    W = np.zeros((w.H, P, P))
+    SIG = np.zeros((w.H, P, P, w.d))
+    for h in range(w.H):
+        lm = [merged_lse[h][q * S:min((q + 1) * S, w.N)] for q in range(P)]
+        ls = [[orc_cache[(h, q, k)][1] for k in range(P)] for q in range(P)]
+        W[h] = pair_weights(ls, lm)
+        for q in range(P):
+            for k in range(P):
+                SIG[h, q, k] = pair_signature(orc_cache[(h, q, k)][0])
+    return W, SIG
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+def test_pair_stats_match_oracle(w):
+    import torch
+
+    import context_state_reuse_amd as lib
+    steps = 3
+    orc = StateReuseOracle(w.N, w.P, w.d)
+    cache = lib.StateCache(w.H, w.N, w.d, w.P)
+    stream = synth.InputStream(w)
+    ones = np.ones((w.P, w.P), np.uint8)
+    SIG = torch.zeros((w.H, w.P, w.P, w.d), dtype=torch.float32, device="cuda")
+    for t in range(steps):
+        qb, kb, vb = stream.next()
+        mask = lib.workload_mask(w, t)
+        res = orc.step(t, mask, {h: (synth.bf16_bits_to_f64(qb[h]), synth.bf16_bits_to_f64(kb[h]),
+                                     synth.bf16_bits_to_f64(vb[h])) for h in range(w.H)})
+        O, LSE, _ = lib.ditango_step(to_device(qb), to_device(kb), to_device(vb), mask, t, cache)
+        sel = ones if t == 0 else mask
+        W, SIG = lib.ditango_pair_stats(cache, LSE, sel, SIG=SIG)
+        torch.cuda.synchronize()
+        We, SIGe = _oracle_stats(w, orc.cache, res["LSE"])
+        Wg, Sg = W.cpu().numpy().astype(np.float64), SIG.cpu().numpy().astype(np.float64)
+        werr = np.abs(Wg - We).max()
+        serr = np.abs(Sg - SIGe)
+        log(f"  [{w.name}] step {t}: W abs {werr:.2e}, SIG max {serr.max():.2e} mean {serr.mean():.2e}")
+        assert werr <= TOL_W, f"{w.name} step {t}: W abs {werr:.3g}"
+        assert serr.max() <= TOL_SIG_MAX and serr.mean() <= TOL_SIG_MEAN, f"{w.name} step {t}: SIG"
+        np.testing.assert_allclose(Wg.sum(axis=2), 1.0, atol=1e-4)
+
+
+def test_pair_stats_errors():
+    import torch
+
+    import context_state_reuse_amd as lib
+    w = CASES[0]
+    cache = lib.StateCache(w.H, w.N, w.d, w.P)
+    LSE = torch.zeros((w.H, w.N), dtype=torch.float32, device="cuda")
+    with pytest.raises(lib.DitangoError) as e:          # nothing cached yet
+        lib.ditango_pair_stats(cache, LSE, np.ones((w.P, w.P), np.uint8))
+    assert e.value.code == lib.DITANGO_ENOCACHE
+
+
+def test_planned_steps_match_oracle_with_their_masks():
+    import torch
+
+    import context_state_reuse_amd as lib
+    w = _scaled("image", "image_plan", 1, 57, 97, 2, steps=8)
+    g = 2
+    cache = lib.StateCache(w.H, w.N, w.d, w.P)
+    runner = lib.PlannedSteps(cache, lib.Planner(w.P, g, w.H, w.d, target_reuse=0.6, drift_max=0.1))
+    stream = synth.InputStream(w)
+    masks, outs, anchors = {}, {}, []
+    for t in range(w.steps):
+        qb, kb, vb = stream.next()
+        mask, anchor, O, LSE = runner.step(t, to_device(qb), to_device(kb), to_device(vb))
+        torch.cuda.synchronize()
+        masks[t], outs[t] = mask.copy(), (O.cpu().numpy(), LSE.cpu().numpy())
+        anchors.append(anchor)
+        log(f"  [plan] step {t}: anchor {anchor}, fresh {int(mask.sum())}/{w.P * w.P}, eps {runner.planner.eps:.3g}")
+        assert (np.diag(mask) == 1).all()
+        for q in range(w.P):
+            for j in range(-(-w.P // g)):
+                mem = group_members(w.P, g, q, j)
+                if mem:
+                    assert len({int(mask[q, k]) for k in mem}) == 1, f"step {t}: group {j} of q={q} split"
+    # warm-up anchors, selective steps, and (local drift ~0.015 per step) one drift anchor
+    assert anchors[0] and anchors[1]
+    assert not all(anchors), "no selective step in the run"
+    assert any(anchors[2:]), "the local drift never triggered an anchor"
+    # the oracle with the same masks
+    orc = StateReuseOracle(w.N, w.P, w.d)
+    stream = synth.InputStream(w)
+    for t in range(w.steps):
+        qb, kb, vb = stream.next()
+        res = orc.step(t, masks[t], {h: (synth.bf16_bits_to_f64(qb[h]), synth.bf16_bits_to_f64(kb[h]),
+                                         synth.bf16_bits_to_f64(vb[h])) for h in range(w.H)})
+        for h in range(w.H):
+            err = np.abs(outs[t][0][h].astype(np.float64) - res["O"][h])
+            lerr = np.abs(outs[t][1][h].astype(np.float64) - res["LSE"][h])
+            assert err.max() <= TOL_O_MAX and err.mean() <= TOL_O_MEAN and lerr.max() <= TOL_LSE, \
+                f"step {t} head {h}: OUT {err.max():.3g}/{err.mean():.3g}, LSE {lerr.max():.3g}"
+    assert math.isfinite(runner.planner.eps)

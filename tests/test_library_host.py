@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_struct_layout():
-    assert lib.ditango_version() == 2
+    assert lib.ditango_version() == 3
     assert ctypes.sizeof(binding.ditango_shape_t) == 20
     assert binding.ditango_states_t.O.offset == 24 and ctypes.sizeof(binding.ditango_states_t) == 48
 
