@@ -53,6 +53,12 @@ def parse():
     ap.add_argument("--window-residual", action="store_true",
                     help="window attention with residual sharing: the anchor step computes every pair and caches "
                          "full-minus-window outputs; steady steps compute the window pairs (nearest partitions) only")
+    ap.add_argument("--planner", action="store_true",
+                    help="anchor-guided planner picks each step's mask (per-pair cache); extra measurement")
+    ap.add_argument("--plan-steps", type=int, default=16, help="denoising steps of the planned run")
+    ap.add_argument("--plan-group", type=int, default=2, help="planner group size g")
+    ap.add_argument("--plan-reuse", type=float, default=0.75, help="planner target reuse fraction")
+    ap.add_argument("--plan-drift", type=float, default=0.1, help="planner anchor drift bound")
     ap.add_argument("--group-masks", choices=("nearest", "workload"), default="nearest",
                     help="with --group: group-aligned masks (local pair plus the nearest groups, as many "
                          "fresh partitions per row as the workload's masks) or the workload's own pair masks")
@@ -157,6 +163,68 @@ def cpu_baseline(w, heads: int, steps: int):
                       f"counts 4*N^2*d per sampled head and step"}
 
 
+def planner_run(args, w, lib, torch, dev):
+    """Steps chosen by the anchor-guided planner (per-pair cache), timed per
+    phase with host synchronisation (the planner reads the statistics on the
+    host): local pairs + their signatures, planning, the other chosen pairs
+    + t_c + merge, and the statistics fed back.  Every step is timed, the
+    two warm-up anchors included."""
+    import synth
+    w = w.scaled(steps=args.plan_steps)
+    stream = synth.InputStream(w)
+    qkv = [tuple(torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev) for b in stream.next())
+           for _ in range(w.steps)]
+    cache = lib.StateCache(w.H, w.N, w.d, w.P)
+    planner = lib.Planner(w.P, args.plan_group, w.H, args.plan_reuse, args.plan_drift)
+    run = lib.PlannedSteps(cache, planner)
+    dense = 4.0 * w.N * w.N * w.d * w.H
+    # untimed: load every kernel once (first launches load code objects)
+    warm = lib.PlannedSteps(lib.StateCache(w.H, w.N, w.d, w.P),
+                            lib.Planner(w.P, args.plan_group, w.H, args.plan_reuse, args.plan_drift))
+    for t in range(3):
+        warm.step(t, *qkv[t])
+    del warm
+    masks, anchors, ms = [], [], []
+    torch.cuda.synchronize()
+    for t in range(w.steps):
+        t0 = time.perf_counter()
+        mask, anchor, _, _ = run.step(t, *qkv[t])
+        torch.cuda.synchronize()
+        ms.append((time.perf_counter() - t0) * 1e3)
+        masks.append(mask)
+        anchors.append(anchor)
+    # the same steps with the planner's masks through the plain step path:
+    # the planner's own cost is the difference
+    cache2 = lib.StateCache(w.H, w.N, w.d, w.P)
+    torch.cuda.synchronize()
+    ms_plain = []
+    for t in range(w.steps):
+        t0 = time.perf_counter()
+        lib.ditango_step(*qkv[t], masks[t], t, cache2)
+        torch.cuda.synchronize()
+        ms_plain.append((time.perf_counter() - t0) * 1e3)
+    sel = [i for i, a in enumerate(anchors) if not a]
+    ms_step = float(np.mean(ms))
+    out = {
+        "metric": METRIC, "value": round(dense / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": w.steps, "warmup": 0, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.F}x{w.Hh}x{w.W} = {w.N} tokens, H={w.H}, d={w.d}, P={w.P}, "
+                               f"{w.steps} steps, masks from the anchor-guided planner (g={args.plan_group}, "
+                               f"target reuse {args.plan_reuse}, drift bound {args.plan_drift})",
+                   "tokens": w.N, "heads": w.H, "head_dim": w.d, "partitions": w.P,
+                   "reuse_ratio": round(1.0 - float(np.mean([m.mean() for m in masks])), 4),
+                   "parallelism": "none (all partitions on one GPU)"},
+        "planner": {"anchor_steps": [i for i, a in enumerate(anchors) if a],
+                    "reuse_selective_steps": round(1.0 - float(np.mean([masks[i].mean() for i in sel])), 4) if sel else None,
+                    "ms_per_step_planned": round(ms_step, 4),
+                    "ms_per_step_same_masks_plain": round(float(np.mean(ms_plain)), 4),
+                    "ms_planned_each": [round(x, 3) for x in ms], "ms_plain_each": [round(x, 3) for x in ms_plain],
+                    "eps": planner.eps},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -175,6 +243,9 @@ def main():
     w = synth.get(args.workload)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.planner:
+        planner_run(args, w, lib, torch, dev)
+        return
 
     # ---- inputs of every step resident in HBM
     stream = synth.InputStream(w)

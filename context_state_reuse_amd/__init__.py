@@ -8,7 +8,7 @@ from .binding import (DITANGO_EHIP, DITANGO_EINVAL, DITANGO_ENOCACHE,  # noqa: F
                       DITANGO_MASK_ALL, DITANGO_MASK_NEAREST, DITANGO_MASK_NONE,
                       DITANGO_MASK_RADIUS, DITANGO_MASK_RANDOM, DITANGO_OK, EXPORTED,
                       DITANGO_MAX_SLOTS, DITANGO_WR_FULL, DITANGO_WR_WINDOW, DitangoError, GroupedStateCache, PlannedSteps, Planner, StateCache,
-                      ditango_attn_partial, ditango_group_attn_partial, ditango_pair_stats, ditango_group_cache_update,
+                      ditango_attn_partial, ditango_group_attn_partial, ditango_pair_stats, ditango_sig_drift, ditango_group_cache_update,
                       ditango_group_compose, ditango_group_mask_build, ditango_group_merge,
                       ditango_group_slots,
                       group_slot_keys, group_slot_live,

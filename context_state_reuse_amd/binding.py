@@ -45,7 +45,7 @@ EXPORTED = ("ditango_states_bytes", "ditango_states_init", "ditango_attn_partial
             "ditango_group_slots", "ditango_gstates_slot_bytes", "ditango_gstates_init",
             "ditango_group_attn_partial", "ditango_group_cache_update", "ditango_group_merge",
             "ditango_group_compose", "ditango_group_reset", "ditango_group_mask_build",
-            "ditango_window_residual_merge", "ditango_step", "ditango_pair_stats",
+            "ditango_window_residual_merge", "ditango_step", "ditango_pair_stats", "ditango_sig_drift",
             "ditango_planner_init", "ditango_planner_plan", "ditango_planner_update")
 
 
@@ -72,15 +72,14 @@ class ditango_gstates_t(ctypes.Structure):
 
 
 class ditango_planner_t(ctypes.Structure):
-    _fields_ = [("P", ctypes.c_int32), ("g", ctypes.c_int32), ("H", ctypes.c_int32), ("d", ctypes.c_int32),
-                ("warmup", ctypes.c_int32), ("target_reuse", ctypes.c_float), ("drift_max", ctypes.c_float),
-                ("anchor", ctypes.c_int32), ("has_ref", ctypes.c_int32), ("n_anchors", ctypes.c_int32),
-                ("last_anchor", ctypes.c_int32), ("eps", ctypes.c_double),
+    _fields_ = [("P", ctypes.c_int32), ("g", ctypes.c_int32), ("H", ctypes.c_int32), ("warmup", ctypes.c_int32),
+                ("target_reuse", ctypes.c_float), ("drift_max", ctypes.c_float),
+                ("anchor", ctypes.c_int32), ("n_anchors", ctypes.c_int32), ("last_anchor", ctypes.c_int32),
+                ("eps", ctypes.c_double),
                 ("D", ctypes.c_double * DITANGO_MAX_P),
                 ("W", (ctypes.c_double * DITANGO_MAX_P) * DITANGO_MAX_P),
                 ("alpha", (ctypes.c_double * DITANGO_MAX_P) * DITANGO_MAX_P),
-                ("Dc", (ctypes.c_double * DITANGO_MAX_P) * DITANGO_MAX_P),
-                ("sigref", ctypes.c_void_p)]
+                ("Dc", (ctypes.c_double * DITANGO_MAX_P) * DITANGO_MAX_P)]
 
 
 def _load():
@@ -136,12 +135,14 @@ def _load():
     lib.ditango_pair_stats.restype = ctypes.c_int
     lib.ditango_pair_stats.argtypes = [ctypes.POINTER(ditango_states_t), vp, u8p, vp, vp, vp]
     plp, f32p = ctypes.POINTER(ditango_planner_t), ctypes.POINTER(ctypes.c_float)
+    lib.ditango_sig_drift.restype = ctypes.c_int
+    lib.ditango_sig_drift.argtypes = [vp, vp, i32, i32, i32, u8p, vp, vp]
     lib.ditango_planner_init.restype = ctypes.c_int
-    lib.ditango_planner_init.argtypes = [plp, i32, i32, i32, i32, ctypes.c_float, ctypes.c_float, i32, f32p]
+    lib.ditango_planner_init.argtypes = [plp, i32, i32, i32, ctypes.c_float, ctypes.c_float, i32]
     lib.ditango_planner_plan.restype = ctypes.c_int
     lib.ditango_planner_plan.argtypes = [plp, i32, f32p, u8p, ctypes.POINTER(ctypes.c_int32)]
     lib.ditango_planner_update.restype = ctypes.c_int
-    lib.ditango_planner_update.argtypes = [plp, i32, u8p, f32p, f32p, f32p]
+    lib.ditango_planner_update.argtypes = [plp, i32, u8p, f32p, f32p]
     lib.ditango_window_residual_merge.restype = ctypes.c_int
     lib.ditango_window_residual_merge.argtypes = [ctypes.POINTER(ditango_states_t), u8p, i32, vp, vp, vp, vp]
     return lib
@@ -264,24 +265,44 @@ def ditango_step(Q, K, V, mask, step: int, cache: StateCache, O=None, LSE=None, 
     return O, LSE, reused
 
 
-def ditango_pair_stats(cache: StateCache, LSE, select, W=None, SIG=None, stream=None):
-    """Per-pair importance W [H][P][P] (every pair) and signatures SIG
-    [H][P][P][d] (pairs with select = 1; other entries untouched) of the
-    cache, given the merged LSE [H][N] of the same contents."""
+def ditango_pair_stats(cache: StateCache, LSE, select, W=None, SIG=None, stream=None, want_w=True):
+    """Per-pair importance W [H][P][P] (every pair; skipped with want_w=False,
+    LSE then unused and may be None) and signatures SIG [H][P][P][d] (pairs
+    with select = 1; other entries untouched) of the cache, given the merged
+    LSE [H][N] of the same contents."""
     import torch
     m = _mask(select, cache.P)
     dev = cache.O.device
-    if W is None:
+    if want_w and W is None:
         W = torch.empty((cache.H, cache.P, cache.P), dtype=torch.float32, device=dev)
     if SIG is None:
         SIG = torch.zeros((cache.H, cache.P, cache.P, cache.d), dtype=torch.float32, device=dev)
-    for t, shp, nm in ((LSE, (cache.H, cache.N), "LSE"), (W, (cache.H, cache.P, cache.P), "W"),
-                       (SIG, (cache.H, cache.P, cache.P, cache.d), "SIG")):
+    checks = [(SIG, (cache.H, cache.P, cache.P, cache.d), "SIG")]
+    if want_w:
+        checks += [(LSE, (cache.H, cache.N), "LSE"), (W, (cache.H, cache.P, cache.P), "W")]
+    for t, shp, nm in checks:
         if not (t.is_cuda and t.dtype == torch.float32 and t.is_contiguous() and tuple(t.shape) == shp):
             raise ValueError(f"{nm} must be a contiguous float32 device tensor of shape {shp}")
-    _check(lib.ditango_pair_stats(ctypes.byref(cache.st), ctypes.c_void_p(LSE.data_ptr()), _u8(m),
-                                  ctypes.c_void_p(W.data_ptr()), ctypes.c_void_p(SIG.data_ptr()), _stream(stream)))
-    return W, SIG
+    _check(lib.ditango_pair_stats(ctypes.byref(cache.st), ctypes.c_void_p(LSE.data_ptr() if want_w else None),
+                                  _u8(m), ctypes.c_void_p(W.data_ptr() if want_w else None),
+                                  ctypes.c_void_p(SIG.data_ptr()), _stream(stream)))
+    return (W if want_w else None), SIG
+
+
+def ditango_sig_drift(A, B, select, out=None, stream=None):
+    """out[q][k] = ||A - B|| / ||B|| over heads and dims for the selected
+    pairs of two signature tables [H][P][P][d] (device float32)."""
+    import torch
+    H, P, _, d = A.shape
+    m = _mask(select, P)
+    if out is None:
+        out = torch.zeros((P, P), dtype=torch.float32, device=A.device)
+    for t, shp, nm in ((A, (H, P, P, d), "A"), (B, (H, P, P, d), "B"), (out, (P, P), "out")):
+        if not (t.is_cuda and t.dtype == torch.float32 and t.is_contiguous() and tuple(t.shape) == shp):
+            raise ValueError(f"{nm} must be a contiguous float32 device tensor of shape {shp}")
+    _check(lib.ditango_sig_drift(ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(B.data_ptr()), int(H), int(P), int(d),
+                                 _u8(m), ctypes.c_void_p(out.data_ptr()), _stream(stream)))
+    return out
 
 
 def _f32(a: np.ndarray):
@@ -289,39 +310,35 @@ def _f32(a: np.ndarray):
 
 
 class Planner:
-    """Anchor-guided selection (host): ditango_planner_* over a numpy
-    reference-signature buffer.  Signature and importance arrays are host
-    float32 numpy arrays [H][P][P][d] and [H][P][P]."""
+    """Anchor-guided selection (host, ditango_planner_*): decisions from
+    per-partition local drifts D [P], head-wise importance W [H][P][P] and
+    per-pair drifts e [P][P] (host float32 arrays, the latter two read at
+    anchor steps only)."""
 
-    def __init__(self, P: int, g: int, H: int, d: int, target_reuse: float, drift_max: float, warmup: int = 2):
-        self.P, self.H, self.d = P, H, d
-        self.sigref = np.zeros((H, P, d), dtype=np.float32)
+    def __init__(self, P: int, g: int, H: int, target_reuse: float, drift_max: float, warmup: int = 2):
+        self.P, self.H = P, H
         self.pl = ditango_planner_t()
-        _check(lib.ditango_planner_init(ctypes.byref(self.pl), int(P), int(g), int(H), int(d), float(target_reuse),
-                                        float(drift_max), int(warmup), _f32(self.sigref)))
+        _check(lib.ditango_planner_init(ctypes.byref(self.pl), int(P), int(g), int(H), float(target_reuse),
+                                        float(drift_max), int(warmup)))
 
-    def _sig(self, a, nm):
-        a = np.ascontiguousarray(a, dtype=np.float32)
-        if a.shape != (self.H, self.P, self.P, self.d):
-            raise ValueError(f"{nm} must have shape {(self.H, self.P, self.P, self.d)}")
-        return a
-
-    def plan(self, step: int, sig) -> tuple[np.ndarray, bool]:
-        sig = self._sig(sig, "sig")
+    def plan(self, step: int, drift=None) -> tuple[np.ndarray, bool]:
+        D = None if drift is None else np.ascontiguousarray(drift, dtype=np.float32).reshape(self.P)
         mask = np.zeros((self.P, self.P), dtype=np.uint8)
         anchor = ctypes.c_int32(0)
-        _check(lib.ditango_planner_plan(ctypes.byref(self.pl), int(step), _f32(sig), _u8(mask), ctypes.byref(anchor)))
+        _check(lib.ditango_planner_plan(ctypes.byref(self.pl), int(step), None if D is None else _f32(D), _u8(mask),
+                                        ctypes.byref(anchor)))
         return mask, bool(anchor.value)
 
-    def update(self, step: int, mask, W, sig_new, sig_old=None) -> None:
+    def update(self, step: int, mask, W=None, e=None) -> None:
         m = _mask(mask, self.P)
-        W = np.ascontiguousarray(W, dtype=np.float32)
-        if W.shape != (self.H, self.P, self.P):
-            raise ValueError(f"W must have shape {(self.H, self.P, self.P)}")
-        sn = self._sig(sig_new, "sig_new")
-        so = None if sig_old is None else self._sig(sig_old, "sig_old")
-        _check(lib.ditango_planner_update(ctypes.byref(self.pl), int(step), _u8(m), _f32(W), _f32(sn),
-                                          None if so is None else _f32(so)))
+        if W is not None:
+            W = np.ascontiguousarray(W, dtype=np.float32)
+            if W.shape != (self.H, self.P, self.P):
+                raise ValueError(f"W must have shape {(self.H, self.P, self.P)}")
+        if e is not None:
+            e = np.ascontiguousarray(e, dtype=np.float32).reshape(self.P, self.P)
+        _check(lib.ditango_planner_update(ctypes.byref(self.pl), int(step), _u8(m),
+                                          None if W is None else _f32(W), None if e is None else _f32(e)))
 
     @property
     def eps(self) -> float:
@@ -332,43 +349,64 @@ class Planner:
         return int(self.pl.n_anchors)
 
     @property
-    def has_ref(self) -> bool:
-        return bool(self.pl.has_ref)
+    def anchor(self) -> bool:
+        return bool(self.pl.anchor)
 
 
 class PlannedSteps:
     """Denoising steps with the planner choosing each step's mask, on one
-    stream: the local pairs are computed first and their signatures taken;
-    the planner picks the mask; the other chosen pairs are computed, t_c
-    updated, states composed, and the statistics of the new cache fed back."""
+    stream: the local pairs are computed first and their signatures' drift
+    since the last anchor measured; the planner picks the mask; the other
+    chosen pairs are computed, t_c updated and the states composed; the
+    signatures of the fresh pairs are refreshed, and at anchor steps the
+    importance and every pair's drift against the cache before the step go
+    to the planner.  Signature tables stay on the device; only P or P*P
+    scalars per step (H*P*P at anchors) reach the host."""
 
     def __init__(self, cache: StateCache, planner: Planner):
         import torch
         self.cache, self.planner = cache, planner
         dev = cache.O.device
-        self.W = torch.empty((cache.H, cache.P, cache.P), dtype=torch.float32, device=dev)
-        self.SIG = torch.zeros((cache.H, cache.P, cache.P, cache.d), dtype=torch.float32, device=dev)
-        self.O = torch.empty((cache.H, cache.N, cache.d), dtype=torch.float32, device=dev)
-        self.LSE = torch.zeros((cache.H, cache.N), dtype=torch.float32, device=dev)
-        self.eye = np.eye(cache.P, dtype=np.uint8)
+        H, P, d = cache.H, cache.P, cache.d
+        self.W = torch.empty((H, P, P), dtype=torch.float32, device=dev)
+        self.SIG = torch.zeros((H, P, P, d), dtype=torch.float32, device=dev)      # signatures of the cache
+        self.OLD = torch.zeros_like(self.SIG)     # the cache before an anchor step
+        self.REF = torch.zeros_like(self.SIG)     # signatures at the last anchor (diagonal used)
+        self.DR = torch.zeros((P, P), dtype=torch.float32, device=dev)
+        self.O = torch.empty((H, cache.N, d), dtype=torch.float32, device=dev)
+        self.LSE = torch.zeros((H, cache.N), dtype=torch.float32, device=dev)
+        self.eye = np.eye(P, dtype=np.uint8)
+        self.off = (1 - self.eye).astype(np.uint8)
 
     def step(self, t: int, Q, K, V, stream=None):
         """Returns (mask, anchor, O, LSE); O and LSE are this object's buffers."""
         c, pl = self.cache, self.planner
-        if pl.has_ref:
+        drift = None
+        if pl.n_anchors:
             ditango_attn_partial(Q, K, V, self.eye, c, stream)
-            ditango_pair_stats(c, self.LSE, self.eye, self.W, self.SIG, stream)
-        sig_local = self.SIG.cpu().numpy()
-        mask, anchor = pl.plan(t, sig_local)
+            ditango_pair_stats(c, None, self.eye, None, self.SIG, stream, want_w=False)
+            ditango_sig_drift(self.SIG, self.REF, self.eye, self.DR, stream)
+            drift = self.DR.diagonal().cpu().numpy()
+        mask, anchor = pl.plan(t, drift)
+        if anchor and pl.n_anchors:
+            self.OLD.copy_(self.SIG)
         rest = mask.copy()
-        if pl.has_ref:
+        if pl.n_anchors:
             rest[self.eye == 1] = 0
         if rest.any():
             ditango_attn_partial(Q, K, V, rest, c, stream)
         ditango_state_cache_update(c, mask, t)
         ditango_state_merge(c, self.O, self.LSE, stream)
-        ditango_pair_stats(c, self.LSE, mask, self.W, self.SIG, stream)
-        pl.update(t, mask, self.W.cpu().numpy(), self.SIG.cpu().numpy(), sig_local if t > 0 else None)
+        ditango_pair_stats(c, self.LSE, mask, self.W, self.SIG, stream, want_w=anchor)
+        if anchor:
+            e = None
+            if pl.n_anchors:
+                ditango_sig_drift(self.SIG, self.OLD, self.off, self.DR, stream)
+                e = self.DR.cpu().numpy()
+            self.REF.copy_(self.SIG)
+            pl.update(t, mask, self.W.cpu().numpy(), e)
+        else:
+            pl.update(t, mask)
         return mask, anchor, self.O, self.LSE
 
 

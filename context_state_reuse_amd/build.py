@@ -77,7 +77,10 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".", "_") + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        jobs.append(([hipcc, *_flags(), *dflags, *lang, "-c", os.path.join(CSRC, src), "-o", obj], obj))
+        # the host half checks for NaN (scales, planner drifts): no
+        # -fno-honor-nans there
+        flags = _flags() if src.endswith(".hip") else [f for f in _flags() if f != "-fno-honor-nans"]
+        jobs.append(([hipcc, *flags, *dflags, *lang, "-c", os.path.join(CSRC, src), "-o", obj], obj))
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
         for f in [ex.submit(_run, cmd) for cmd, _ in jobs]:
             f.result()

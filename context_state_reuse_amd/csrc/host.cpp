@@ -323,7 +323,7 @@ int ditango_pair_stats(const ditango_states_t* st, const float* LSE, const uint8
   if (rc) return rc;
   const int P = st->shape.P;
   if ((rc = check_mask(select, P))) return rc;
-  if (!LSE || !W) return fail(DITANGO_EINVAL, "LSE and W must be non-NULL");
+  if (W && !LSE) return fail(DITANGO_EINVAL, "LSE must be non-NULL when W is wanted");
   bool any = false;
   for (int i = 0; i < P * P; ++i) any |= select[i] != 0;
   if (any && !SIG) return fail(DITANGO_EINVAL, "SIG must be non-NULL when pairs are selected");
@@ -339,7 +339,10 @@ int ditango_pair_stats(const ditango_states_t* st, const float* LSE, const uint8
   sp.SIG = SIG;
   for (int q = 0; q < P; ++q)
     for (int k = 0; k < P; ++k)
-      if (select[q * P + k]) sp.sel[q] |= 1u << k;
+      if (select[q * P + k]) {
+        sp.sel[q] |= 1u << k;
+        sp.pairs[sp.n_pairs++] = static_cast<uint16_t>(q * P + k);
+      }
   sp.H = st->shape.H;
   sp.N = st->shape.N;
   sp.P = P;
@@ -347,6 +350,27 @@ int ditango_pair_stats(const ditango_states_t* st, const float* LSE, const uint8
   sp.d = st->shape.d;
   hipError_t e = ditango::launch_stats(sp, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(DITANGO_EHIP, "stats kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int ditango_sig_drift(const float* A, const float* B, int32_t H, int32_t P, int32_t d, const uint8_t* select,
+                      float* out, void* stream) {
+  if (!A || !B || !out) return fail(DITANGO_EINVAL, "A, B and out must be non-NULL");
+  if (H < 1 || d < 1) return fail(DITANGO_EINVAL, "H=%d and d=%d must be >= 1", H, d);
+  int rc = check_mask(select, P);
+  if (rc) return rc;
+  ditango::DriftParams dp;
+  std::memset(&dp, 0, sizeof dp);
+  dp.A = A;
+  dp.B = B;
+  dp.out = out;
+  dp.H = H;
+  dp.P = P;
+  dp.d = d;
+  for (int i = 0; i < P * P; ++i)
+    if (select[i]) dp.pairs[dp.n_pairs++] = static_cast<uint16_t>(i);
+  hipError_t e = ditango::launch_drift(dp, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DITANGO_EHIP, "drift kernel launch: %s", hipGetErrorString(e));
   return ok();
 }
 
@@ -358,25 +382,10 @@ int ditango_pair_stats(const ditango_states_t* st, const float* LSE, const uint8
 // computed when their summed ASE exceeds eps, reused otherwise; anchor steps
 // compute everything when the local state drifts too far, and re-measure w,
 // the scale ratios alpha and eps.  The page's equations are lost; the
-// concrete model (signature drift, alpha = pair drift / local drift, eps as
-// the target-reuse quantile of the errors corrected at the anchor) is the one
-// stated in ditango.h.
+// concrete model is the one stated in ditango.h.  The planner works on
+// scalars only (drifts and importances reduced on the GPU).
 
 namespace {
-
-// ||new - ref|| / ||ref|| over the heads' signatures of one pair; 0 when both
-// are zero, infinity when only ref is.
-double sig_drift(const float* a, int a_hs, const float* b, int b_hs, int H, int d) {
-  double num = 0.0, den = 0.0;
-  for (int h = 0; h < H; ++h)
-    for (int c = 0; c < d; ++c) {
-      const double x = a[static_cast<size_t>(h) * a_hs + c], y = b[static_cast<size_t>(h) * b_hs + c];
-      num += (x - y) * (x - y);
-      den += y * y;
-    }
-  if (den == 0.0) return num == 0.0 ? 0.0 : HUGE_VAL;
-  return std::sqrt(num) / std::sqrt(den);
-}
 
 int planner_groups(const ditango_planner_t* pl) { return (pl->P + pl->g - 1) / pl->g; }
 
@@ -390,19 +399,19 @@ int group_members(const ditango_planner_t* pl, int q, int j, int* out) {
 
 int check_planner(const ditango_planner_t* pl) {
   if (!pl) return fail(DITANGO_EINVAL, "planner is NULL");
-  if (pl->P < 1 || pl->P > DITANGO_MAX_P || pl->g < 1 || pl->g > pl->P || pl->H < 1 || pl->d < 1 || !pl->sigref)
+  if (pl->P < 1 || pl->P > DITANGO_MAX_P || pl->g < 1 || pl->g > pl->P || pl->H < 1 || pl->warmup < 2)
     return fail(DITANGO_EINVAL, "planner is not initialised");
   return DITANGO_OK;
 }
 
 }  // namespace
 
-int ditango_planner_init(ditango_planner_t* pl, int32_t P, int32_t g, int32_t H, int32_t d, float target_reuse,
-                         float drift_max, int32_t warmup, float* sigref) {
-  if (!pl || !sigref) return fail(DITANGO_EINVAL, "planner and sigref must be non-NULL");
+int ditango_planner_init(ditango_planner_t* pl, int32_t P, int32_t g, int32_t H, float target_reuse,
+                         float drift_max, int32_t warmup) {
+  if (!pl) return fail(DITANGO_EINVAL, "planner is NULL");
   if (P < 1 || P > DITANGO_MAX_P) return fail(DITANGO_EINVAL, "P=%d outside 1..%d", P, DITANGO_MAX_P);
   if (g < 1 || g > P) return fail(DITANGO_EINVAL, "group size g=%d outside 1..P", g);
-  if (H < 1 || d < 1) return fail(DITANGO_EINVAL, "H=%d and d=%d must be >= 1", H, d);
+  if (H < 1) return fail(DITANGO_EINVAL, "H=%d must be >= 1", H);
   if (!(target_reuse >= 0.0f && target_reuse <= 1.0f)) return fail(DITANGO_EINVAL, "target_reuse outside [0, 1]");
   if (!(drift_max >= 0.0f)) return fail(DITANGO_EINVAL, "drift_max must be >= 0");
   if (warmup < 2) return fail(DITANGO_EINVAL, "warmup=%d must be >= 2", warmup);
@@ -410,31 +419,28 @@ int ditango_planner_init(ditango_planner_t* pl, int32_t P, int32_t g, int32_t H,
   pl->P = P;
   pl->g = g;
   pl->H = H;
-  pl->d = d;
   pl->target_reuse = target_reuse;
   pl->drift_max = drift_max;
   pl->warmup = warmup;
   pl->eps = HUGE_VAL;
-  pl->sigref = sigref;
+  pl->last_anchor = -1;
   return ok();
 }
 
-int ditango_planner_plan(ditango_planner_t* pl, int32_t step, const float* sig, uint8_t* mask_out,
+int ditango_planner_plan(ditango_planner_t* pl, int32_t step, const float* drift, uint8_t* mask_out,
                          int32_t* anchor_out) {
   int rc = check_planner(pl);
   if (rc) return rc;
-  if (!sig || !mask_out) return fail(DITANGO_EINVAL, "sig and mask_out must be non-NULL");
+  if (!mask_out) return fail(DITANGO_EINVAL, "mask_out must be non-NULL");
+  if (pl->n_anchors > 0 && !drift) return fail(DITANGO_EINVAL, "drift must be non-NULL after the first anchor");
   if (step < 0) return fail(DITANGO_EINVAL, "step=%d must be >= 0", step);
-  const int P = pl->P, d = pl->d, H = pl->H;
-  const int sig_hs = P * P * d;    // head stride of sig [H][P][P][d]
-  double dmax = 0.0;
+  const int P = pl->P;
+  bool beyond = false;
   for (int q = 0; q < P; ++q) {
-    pl->D[q] = pl->has_ref ? sig_drift(sig + static_cast<size_t>(q * P + q) * d, sig_hs, pl->sigref + static_cast<size_t>(q) * d,
-                                       P * d, H, d)
-                           : 0.0;
-    dmax = std::max(dmax, pl->D[q]);
+    pl->D[q] = pl->n_anchors > 0 ? static_cast<double>(drift[q]) : 0.0;
+    beyond = beyond || !(pl->D[q] <= pl->drift_max);   // NaN counts as beyond any bound
   }
-  pl->anchor = step < pl->warmup || !pl->has_ref || dmax > pl->drift_max;
+  pl->anchor = step < pl->warmup || pl->n_anchors == 0 || beyond;
   if (anchor_out) *anchor_out = pl->anchor;
   if (pl->anchor) {
     std::memset(mask_out, 1, static_cast<size_t>(P) * P);
@@ -458,14 +464,13 @@ int ditango_planner_plan(ditango_planner_t* pl, int32_t step, const float* sig, 
 }
 
 int ditango_planner_update(ditango_planner_t* pl, int32_t step, const uint8_t* mask, const float* W,
-                           const float* sig_new, const float* sig_old) {
+                           const float* e) {
   int rc = check_planner(pl);
   if (rc) return rc;
-  const int P = pl->P, d = pl->d, H = pl->H;
+  const int P = pl->P, H = pl->H;
   if ((rc = check_mask(mask, P))) return rc;
-  if (!W || !sig_new) return fail(DITANGO_EINVAL, "W and sig_new must be non-NULL");
+  if (pl->anchor && !W) return fail(DITANGO_EINVAL, "W must be non-NULL at an anchor step");
   if (step < 0) return fail(DITANGO_EINVAL, "step=%d must be >= 0", step);
-  const int sig_hs = P * P * d;
   if (pl->anchor) {
     for (int q = 0; q < P; ++q)
       for (int k = 0; k < P; ++k) {
@@ -473,15 +478,10 @@ int ditango_planner_update(ditango_planner_t* pl, int32_t step, const uint8_t* m
         for (int h = 0; h < H; ++h) s += W[(static_cast<size_t>(h) * P + q) * P + k];
         pl->W[q][k] = s / H;
       }
-    if (sig_old && pl->has_ref) {
-      double e[DITANGO_MAX_P][DITANGO_MAX_P] = {};
+    if (e && pl->n_anchors > 0) {
       for (int q = 0; q < P; ++q)
-        for (int k = 0; k < P; ++k) {
-          if (k == q) continue;
-          const size_t off = static_cast<size_t>(q * P + k) * d;
-          e[q][k] = sig_drift(sig_new + off, sig_hs, sig_old + off, sig_hs, H, d);
-          pl->alpha[q][k] = pl->D[q] > 0.0 ? e[q][k] / pl->D[q] : 0.0;
-        }
+        for (int k = 0; k < P; ++k)
+          if (k != q) pl->alpha[q][k] = pl->D[q] > 0.0 ? static_cast<double>(e[q * P + k]) / pl->D[q] : 0.0;
       std::vector<double> E;
       for (int q = 0; q < P; ++q)
         for (int j = 0; j < planner_groups(pl); ++j) {
@@ -489,18 +489,13 @@ int ditango_planner_update(ditango_planner_t* pl, int32_t step, const uint8_t* m
           const int n = group_members(pl, q, j, mem);
           if (n == 0) continue;
           double s = 0.0;
-          for (int i = 0; i < n; ++i) s += pl->W[q][mem[i]] * e[q][mem[i]];
+          for (int i = 0; i < n; ++i) s += pl->W[q][mem[i]] * static_cast<double>(e[q * P + mem[i]]);
           E.push_back(s);
         }
       std::sort(E.begin(), E.end());
       const long kq = E.empty() ? 0 : static_cast<long>(std::ceil(pl->target_reuse * static_cast<double>(E.size()) - 1e-12));
       pl->eps = E.empty() ? HUGE_VAL : kq <= 0 ? -HUGE_VAL : E[std::min<size_t>(kq, E.size()) - 1];
     }
-    for (int h = 0; h < H; ++h)
-      for (int q = 0; q < P; ++q)
-        std::memcpy(pl->sigref + (static_cast<size_t>(h) * P + q) * d,
-                    sig_new + static_cast<size_t>(h) * sig_hs + static_cast<size_t>(q * P + q) * d, sizeof(float) * d);
-    pl->has_ref = 1;
     for (int q = 0; q < P; ++q)
       for (int j = 0; j < DITANGO_MAX_P; ++j) pl->Dc[q][j] = 0.0;
     pl->n_anchors += 1;

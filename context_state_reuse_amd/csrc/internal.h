@@ -74,14 +74,30 @@ struct MergeParams {
 // for every pair (q, k) and head h, W[h][q][k] = mean over q's rows r of
 // exp(LSE_slot[r] - LSE[q*S + r]); for the pairs with bit k of sel[q] set,
 // SIG[h][q][k][0..d) = mean over q's rows of OUT_slot.
+// W == nullptr: importance not wanted; the grid then covers the selected
+// pairs only, listed in pairs[0 .. n_pairs).
 struct StatsParams {
   const float* O;           // per-pair cache [H][P*P][S][d]
   const float* LSE_slot;    // [H][P*P][S]
   const float* LSE;         // merged [H][N]
-  float* W;                 // [H][P][P]
+  float* W;                 // [H][P][P] or nullptr
   float* SIG;               // [H][P][P][d]
   uint32_t sel[DITANGO_MAX_P];
   int32_t H, N, P, S, d;
+  int32_t n_pairs;
+  uint16_t pairs[DITANGO_MAX_P * DITANGO_MAX_P];
+};
+
+// Drift of pair signatures between two tables A and B ([H][P][P][d]): for
+// the listed pairs, out[q*P + k] = ||A - B|| / ||B|| over the pair's heads
+// and dims (0 when both are 0, +inf when only B is).
+struct DriftParams {
+  const float* A;
+  const float* B;
+  float* out;               // [P][P]
+  int32_t H, P, d;
+  int32_t n_pairs;
+  uint16_t pairs[DITANGO_MAX_P * DITANGO_MAX_P];
 };
 
 // Query rows handled by one block of the partial kernel for head dim d
@@ -92,5 +108,6 @@ int partial_rows_per_block(int d, int S);
 hipError_t launch_partial(PartialParams& p, int rows_per_block, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_stats(const StatsParams& p, hipStream_t stream);
+hipError_t launch_drift(const DriftParams& p, hipStream_t stream);
 
 }  // namespace ditango

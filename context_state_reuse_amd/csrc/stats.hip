@@ -1,5 +1,6 @@
 // Per-pair statistics of the state cache for the anchor-guided planner
-// (DiTango page, error-analysis and state-selection sections):
+// (DiTango page, error-analysis and state-selection sections), and the
+// drift of pair signatures between two signature tables:
 //   W[h][q][k]   = mean over the rows r of query partition q of
 //                  exp(LSE_qk[r] - LSE[r]) -- the normalised weight of
 //                  partition k in the composed state, i.e. the share of q's
@@ -8,7 +9,8 @@
 //   SIG[h][q][k] = mean over q's rows of OUT_qk, for the selected pairs --
 //                  the signature on which the planner measures how far a
 //                  state has drifted.
-// One block per (head, q, k), 256 threads; every sum is taken in a fixed
+// One block per (head, q, k) -- per selected pair only when W is not
+// wanted -- 256 threads; every sum is taken in a fixed
 // order (per-thread strided partial sums, then a fixed tree), so results do
 // not vary from run to run.  Reads the LSE of every slot and the OUT of the
 // selected ones: a few per cent of one merge.
@@ -32,26 +34,28 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const StatsParams p) {
   __shared__ float wpart[kThreads / 64];
 
   const int tid = threadIdx.x;
-  const int pair = blockIdx.x % (p.P * p.P);
-  const int h = blockIdx.x / (p.P * p.P);
+  const int n = p.W ? p.P * p.P : p.n_pairs;          // blocks per head
+  const int pair = p.W ? static_cast<int>(blockIdx.x % n) : static_cast<int>(p.pairs[blockIdx.x % n]);
+  const int h = blockIdx.x / n;
   const int q = pair / p.P, k = pair % p.P;
   const int len_q = min(p.S, p.N - q * p.S);
   const size_t slot = static_cast<size_t>(h) * p.P * p.P + pair;
-  const float* ls = p.LSE_slot + slot * p.S;
-  const float* lm = p.LSE + static_cast<size_t>(h) * p.N + static_cast<size_t>(q) * p.S;
-
-  // importance
-  float acc = 0.0f;
-  for (int r = tid; r < len_q; r += kThreads) acc += __expf(ls[r] - lm[r]);
+  // importance (block-uniform branch)
+  if (p.W) {
+    const float* ls = p.LSE_slot + slot * p.S;
+    const float* lm = p.LSE + static_cast<size_t>(h) * p.N + static_cast<size_t>(q) * p.S;
+    float acc = 0.0f;
+    for (int r = tid; r < len_q; r += kThreads) acc += __expf(ls[r] - lm[r]);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if ((tid & 63) == 0) wpart[tid >> 6] = acc;
-  __syncthreads();
-  if (tid == 0) {
-    float s = 0.0f;
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if ((tid & 63) == 0) wpart[tid >> 6] = acc;
+    __syncthreads();
+    if (tid == 0) {
+      float s = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kThreads / 64; ++i) s += wpart[i];
-    p.W[slot] = s / static_cast<float>(len_q);
+      for (int i = 0; i < kThreads / 64; ++i) s += wpart[i];
+      p.W[slot] = s / static_cast<float>(len_q);
+    }
   }
 
   // signature (block-uniform branch)
@@ -72,10 +76,53 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const StatsParams p) {
   }
 }
 
+// One block per listed pair: every thread sums its strided share of the
+// pair's H*d elements, then a fixed tree.
+__global__ __launch_bounds__(kThreads) void drift_kernel(const DriftParams p) {
+  __shared__ float lnum[kThreads / 64], lden[kThreads / 64];
+  const int tid = threadIdx.x;
+  const int pair = p.pairs[blockIdx.x];
+  const int n = p.H * p.d;
+  float num = 0.0f, den = 0.0f;
+  for (int i = tid; i < n; i += kThreads) {
+    const int h = i / p.d, c = i - h * p.d;
+    const size_t off = (static_cast<size_t>(h) * p.P * p.P + pair) * p.d + c;
+    const float b = p.B[off], x = p.A[off] - b;
+    num += x * x;
+    den += b * b;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    num += __shfl_xor(num, off);
+    den += __shfl_xor(den, off);
+  }
+  if ((tid & 63) == 0) {
+    lnum[tid >> 6] = num;
+    lden[tid >> 6] = den;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float sn = 0.0f, sd = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kThreads / 64; ++i) {
+      sn += lnum[i];
+      sd += lden[i];
+    }
+    p.out[pair] = sd == 0.0f ? (sn == 0.0f ? 0.0f : __builtin_inff()) : __builtin_sqrtf(sn) / __builtin_sqrtf(sd);
+  }
+}
+
 }  // namespace
 
+hipError_t launch_drift(const DriftParams& p, hipStream_t stream) {
+  if (p.n_pairs == 0) return hipSuccess;
+  hipLaunchKernelGGL(drift_kernel, dim3(p.n_pairs), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_stats(const StatsParams& p, hipStream_t stream) {
-  const int64_t blocks = static_cast<int64_t>(p.H) * p.P * p.P;
+  const int64_t blocks = static_cast<int64_t>(p.H) * (p.W ? p.P * p.P : p.n_pairs);
+  if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
   switch (p.d) {

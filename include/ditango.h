@@ -292,47 +292,58 @@ int ditango_group_mask_build(int32_t P, int32_t g, int32_t n, uint8_t* mask_out)
  *   SIG device fp32 [H][P][P][d], 16-byte aligned: for the pairs with
  *       select[q][k] = 1 (host uint8 [P][P]) the mean of the slot's OUT rows;
  *       other entries are not touched (SIG may be NULL if none is selected).
- * LSE is the merged device fp32 [H][N] of the same cache contents.  Every
- * pair must hold a state.  Errors: EINVAL, ENOCACHE, EHIP. */
+ * LSE is the merged device fp32 [H][N] of the same cache contents.  W may be
+ * NULL (importance not wanted, LSE not read: only the selected pairs are
+ * visited).  Every pair must hold a state.  Errors: EINVAL, ENOCACHE, EHIP. */
 int ditango_pair_stats(const ditango_states_t* st, const float* LSE, const uint8_t* select, float* W, float* SIG,
                        void* stream);
 
-/* Planner state (host only; every field is set by ditango_planner_init and
- * kept by the calls below).  sigref is a caller-owned host fp32 [H][P][d]
- * buffer (local signatures at the last anchor). */
+/* Drift of pair signatures between two device tables A and B, fp32
+ * [H][P][P][d]: for the pairs with select[q][k] = 1 (host uint8 [P][P]),
+ * out[q*P + k] = ||A - B|| / ||B|| over the pair's H*d values (0 when both
+ * are 0, +inf when only B is); out is device fp32 [P][P], other entries
+ * untouched.  Errors: EINVAL, EHIP. */
+int ditango_sig_drift(const float* A, const float* B, int32_t H, int32_t P, int32_t d, const uint8_t* select,
+                      float* out, void* stream);
+
+/* Planner state (host only; set by ditango_planner_init and kept by the
+ * calls below).  It works on scalars: the drifts and importances are
+ * reduced on the GPU (ditango_pair_stats, ditango_sig_drift). */
 typedef struct {
-  int32_t P, g, H, d, warmup;
+  int32_t P, g, H, warmup;
   float   target_reuse;   /* share of groups to reuse at the anchor error level, 0..1 */
   float   drift_max;      /* anchor when a local state drifts more than this */
   int32_t anchor;         /* decision of the last ditango_planner_plan */
-  int32_t has_ref, n_anchors, last_anchor;
+  int32_t n_anchors, last_anchor;
   double  eps;
   double  D[DITANGO_MAX_P];
   double  W[DITANGO_MAX_P][DITANGO_MAX_P];
   double  alpha[DITANGO_MAX_P][DITANGO_MAX_P];
   double  Dc[DITANGO_MAX_P][DITANGO_MAX_P];   /* [q][group] */
-  float*  sigref;
 } ditango_planner_t;
 
-/* Errors: EINVAL (P outside 1..32, g outside 1..P, H or d < 1, target_reuse
- * outside [0, 1], drift_max < 0, warmup < 2, NULL pointers). */
-int ditango_planner_init(ditango_planner_t* pl, int32_t P, int32_t g, int32_t H, int32_t d, float target_reuse,
-                         float drift_max, int32_t warmup, float* sigref);
+/* Errors: EINVAL (P outside 1..32, g outside 1..P, H < 1, target_reuse
+ * outside [0, 1], drift_max < 0, warmup < 2, NULL planner). */
+int ditango_planner_init(ditango_planner_t* pl, int32_t P, int32_t g, int32_t H, float target_reuse,
+                         float drift_max, int32_t warmup);
 
-/* Mask for step `step` (host uint8 [P][P], 1 = compute) from the signatures
- * of the freshly computed local states: sig host fp32 [H][P][P][d], only the
- * diagonal entries are read (compute the local pairs first, then their
- * signatures with ditango_pair_stats).  *anchor_out (may be NULL) = 1 for an
- * anchor step (mask all ones).  Errors: EINVAL. */
-int ditango_planner_plan(ditango_planner_t* pl, int32_t step, const float* sig, uint8_t* mask_out,
+/* Mask for step `step` (host uint8 [P][P], 1 = compute) from drift, host
+ * fp32 [P]: D(q, t), the drift of q's freshly computed local signature
+ * against the one at the last anchor (compute the local pairs first; read
+ * only after the first anchor, may be NULL before).  A NaN drift counts as
+ * beyond any bound.  *anchor_out (may be NULL) = 1 for an anchor step (mask
+ * all ones).  Errors: EINVAL. */
+int ditango_planner_plan(ditango_planner_t* pl, int32_t step, const float* drift, uint8_t* mask_out,
                          int32_t* anchor_out);
 
-/* After step `step` ran with `mask`: W host fp32 [H][P][P] and sig_new host
- * fp32 [H][P][P][d] of the cache after the step (ditango_pair_stats with
- * select = mask), sig_old the signatures of the cache before the step (host,
- * same layout; NULL at the first step).  Errors: EINVAL. */
+/* After step `step` ran with `mask`.  At an anchor step (the last plan
+ * returned one) it reads W, host fp32 [H][P][P], the importance of the cache
+ * after the step (ditango_pair_stats), and e, host fp32 [P][P] (diagonal not
+ * read), each pair's signature drift against the signature it had before the
+ * step (ditango_sig_drift; NULL at the first anchor); between anchors it reads
+ * only the mask and W, e may be NULL.  Errors: EINVAL. */
 int ditango_planner_update(ditango_planner_t* pl, int32_t step, const uint8_t* mask, const float* W,
-                           const float* sig_new, const float* sig_old);
+                           const float* e);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* ditango_last_error(void);

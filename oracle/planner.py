@@ -132,10 +132,16 @@ class AnchorPlanner:
         P = self.P
         sig = np.asarray(sig_local, dtype=np.float64)
         if self.sigref is not None:
-            self.D = np.array([rel_drift(sig[:, q, q, :], self.sigref[:, q, :]) for q in range(P)])
+            D = np.array([rel_drift(sig[:, q, q, :], self.sigref[:, q, :]) for q in range(P)])
         else:
-            self.D = np.zeros(P)
-        self.anchor = t < self.warmup or self.sigref is None or float(np.max(self.D)) > self.drift_max
+            D = np.zeros(P)
+        return self.plan_drift(t, D)
+
+    def plan_drift(self, t: int, D) -> tuple[np.ndarray, bool]:
+        """plan() from the local drifts D[q] themselves (ignored before the first anchor)."""
+        P = self.P
+        self.D = np.asarray(D, dtype=np.float64).copy() if self.n_anchors else np.zeros(P)
+        self.anchor = t < self.warmup or self.n_anchors == 0 or not float(np.max(self.D)) <= self.drift_max
         if self.anchor:
             return np.ones((P, P), dtype=np.uint8), True
         mask = np.eye(P, dtype=np.uint8)
@@ -152,22 +158,33 @@ class AnchorPlanner:
 
     def update(self, t: int, mask, W_heads, sig_new, sig_old=None) -> None:
         P = self.P
-        mask = np.asarray(mask, dtype=np.uint8)
-        sig_new = np.asarray(sig_new, dtype=np.float64)
+        e = None
         if self.anchor:
-            self.W = np.mean(np.asarray(W_heads, dtype=np.float64), axis=0)
+            sig_new = np.asarray(sig_new, dtype=np.float64)
             if sig_old is not None and self.sigref is not None:
                 sig_old = np.asarray(sig_old, dtype=np.float64)
-                e = np.zeros((P, P))
+                e = np.array([[rel_drift(sig_new[:, q, k, :], sig_old[:, q, k, :]) if k != q else 0.0
+                               for k in range(P)] for q in range(P)])
+            self.sigref = np.array([sig_new[:, q, q, :] for q in range(P)]).transpose(1, 0, 2).copy()
+        self.update_drift(t, mask, None if W_heads is None else np.mean(np.asarray(W_heads, np.float64), axis=0), e)
+
+    def update_drift(self, t: int, mask, W, e) -> None:
+        """update() from the head-mean importance W[q][k] and the pairs' drifts
+        e[q][k] against the cache before the step (both read at anchors only;
+        e None at the first anchor)."""
+        P = self.P
+        mask = np.asarray(mask, dtype=np.uint8)
+        if self.anchor:
+            self.W = np.asarray(W, dtype=np.float64).copy()
+            if e is not None and self.n_anchors > 0:
+                e = np.asarray(e, dtype=np.float64)
                 for q in range(P):
                     for k in range(P):
                         if k != q:
-                            e[q, k] = rel_drift(sig_new[:, q, k, :], sig_old[:, q, k, :])
                             self.alpha[q, k] = e[q, k] / self.D[q] if self.D[q] > 0 else 0.0
                 E = [sum(self.W[q, k] * e[q, k] for k in group_members(P, self.g, q, j))
                      for q in range(P) for j in range(self.m) if group_members(P, self.g, q, j)]
                 self.eps = reuse_threshold(E, self.rho)
-            self.sigref = np.array([sig_new[:, q, q, :] for q in range(P)]).transpose(1, 0, 2).copy()
             self.Dc[:] = 0.0
             self.n_anchors += 1
         else:

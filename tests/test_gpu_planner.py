@@ -81,6 +81,40 @@ def test_pair_stats_match_oracle(w):
         assert werr <= TOL_W, f"{w.name} step {t}: W abs {werr:.3g}"
         assert serr.max() <= TOL_SIG_MAX and serr.mean() <= TOL_SIG_MEAN, f"{w.name} step {t}: SIG"
         np.testing.assert_allclose(Wg.sum(axis=2), 1.0, atol=1e-4)
+        # signatures alone (no importance, selected pairs only): the same values
+        _, SIG2 = lib.ditango_pair_stats(cache, None, sel, SIG=torch.full_like(SIG, 7.0), want_w=False)
+        S2 = SIG2.cpu().numpy()
+        assert np.array_equal(S2[:, sel == 1], SIG.cpu().numpy()[:, sel == 1])
+        assert (S2[:, sel == 0] == 7.0).all()
+
+
+@pytest.mark.parametrize("H,P,d", [(2, 8, 72), (48, 32, 64), (1, 3, 128)])
+def test_sig_drift_matches_oracle(H, P, d):
+    import torch
+
+    import context_state_reuse_amd as lib
+    from oracle.planner import rel_drift
+    rng = np.random.default_rng(H * 1000 + P)
+    B = rng.normal(size=(H, P, P, d)).astype(np.float32)
+    A = (B + rng.uniform(0, 0.3, size=(1, P, P, 1)) * rng.normal(size=B.shape)).astype(np.float32)
+    B[:, 0, 1] = 0.0                                # ||B|| = 0: 0 if A is 0 too, else inf
+    A[:, 0, 1] = 0.0
+    B[:, 1, 0] = 0.0
+    sel = (rng.uniform(size=(P, P)) < 0.6).astype(np.uint8)
+    sel[0, 1] = sel[1, 0] = 1
+    out = torch.full((P, P), -1.0, dtype=torch.float32, device="cuda")
+    lib.ditango_sig_drift(torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda(), sel, out)
+    o = out.cpu().numpy()
+    for q in range(P):
+        for k in range(P):
+            if not sel[q, k]:
+                assert o[q, k] == -1.0
+                continue
+            ref = rel_drift(A[:, q, k], B[:, q, k])
+            if math.isinf(ref):
+                assert math.isinf(o[q, k])
+            else:
+                assert o[q, k] == pytest.approx(ref, rel=1e-5, abs=1e-7), (q, k)
 
 
 def test_pair_stats_errors():
@@ -102,7 +136,7 @@ def test_planned_steps_match_oracle_with_their_masks():
     w = _scaled("image", "image_plan", 1, 57, 97, 2, steps=8)
     g = 2
     cache = lib.StateCache(w.H, w.N, w.d, w.P)
-    runner = lib.PlannedSteps(cache, lib.Planner(w.P, g, w.H, w.d, target_reuse=0.6, drift_max=0.1))
+    runner = lib.PlannedSteps(cache, lib.Planner(w.P, g, w.H, target_reuse=0.6, drift_max=0.1))
     stream = synth.InputStream(w)
     masks, outs, anchors = {}, {}, []
     for t in range(w.steps):

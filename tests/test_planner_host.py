@@ -13,38 +13,49 @@ import pytest
 
 import context_state_reuse_amd as lib
 from context_state_reuse_amd import binding
-from oracle.planner import AnchorPlanner
+from oracle.planner import AnchorPlanner, rel_drift
 
 
 def _drive(P, g, H, d, rho, drift_max, steps, seed, warmup=2):
+    """Signatures evolve at pair-specific rates; the drifts the planner needs
+    are computed once (float32, as the GPU reductions deliver them) and fed
+    to both planners."""
     rng = np.random.default_rng(seed)
     rho32, dm32 = float(np.float32(rho)), float(np.float32(drift_max))
-    cpp = lib.Planner(P, g, H, d, rho32, dm32, warmup)
+    cpp = lib.Planner(P, g, H, rho32, dm32, warmup)
     orc = AnchorPlanner(P, g, rho32, dm32, warmup)
     truth = rng.normal(size=(H, P, P, d)).astype(np.float32)        # states the inputs would give now
     rate = rng.uniform(0.0, 0.2, size=(1, P, P, 1)).astype(np.float32)
     table = truth.copy()                                              # signatures of the cached states
+    ref = None                                                        # signatures at the last anchor
     anchors = 0
     for t in range(steps):
         truth = (truth + rate * rng.normal(size=truth.shape)).astype(np.float32)
-        before = table.copy()
         for q in range(P):                       # the local states are computed first
             table[:, q, q] = truth[:, q, q]
-        sig_local = table.copy()
-        m_c, a_c = cpp.plan(t, sig_local)
-        m_o, a_o = orc.plan(t, sig_local)
+        D = None if ref is None else np.array([rel_drift(table[:, q, q], ref[:, q, q]) for q in range(P)],
+                                              dtype=np.float32)
+        m_c, a_c = cpp.plan(t, D)
+        m_o, a_o = orc.plan_drift(t, D if D is not None else np.zeros(P))
         assert a_c == a_o, (t, seed)
         assert (m_c == m_o).all(), (t, seed, m_c, m_o)
         assert (np.diag(m_c) == 1).all()
         anchors += a_c
+        old = table.copy()
         for q in range(P):
             for k in range(P):
                 if m_c[q, k]:
                     table[:, q, k] = truth[:, q, k]
         W = rng.dirichlet(np.ones(P), size=(H, P)).astype(np.float32)
-        old = None if t == 0 else sig_local
-        cpp.update(t, m_c, W, table, old)
-        orc.update(t, m_c, W, table, old)
+        if a_c:
+            e = None if ref is None else np.array([[rel_drift(table[:, q, k], old[:, q, k]) if k != q else 0.0
+                                                    for k in range(P)] for q in range(P)], dtype=np.float32)
+            cpp.update(t, m_c, W, e)
+            orc.update_drift(t, m_c, np.mean(W.astype(np.float64), axis=0), e)
+            ref = table.copy()
+        else:
+            cpp.update(t, m_c)
+            orc.update_drift(t, m_c, None, None)
         pl = cpp.pl
         if math.isinf(orc.eps):
             assert math.isinf(pl.eps) and (pl.eps > 0) == (orc.eps > 0)
@@ -54,7 +65,6 @@ def _drive(P, g, H, d, rho, drift_max, steps, seed, warmup=2):
         np.testing.assert_allclose(np.array([row[:P] for row in pl.alpha])[:P], orc.alpha, rtol=1e-12, atol=0)
         np.testing.assert_allclose(np.array([row[:orc.m] for row in pl.Dc])[:P], orc.Dc, rtol=1e-12, atol=0)
         assert pl.n_anchors == orc.n_anchors
-        del before
     return anchors
 
 
@@ -72,21 +82,32 @@ def test_library_planner_mixes_anchor_and_selective_steps():
     assert anchors == 2
 
 
+def test_planner_nan_drift_forces_an_anchor():
+    pl = lib.Planner(4, 2, 1, 0.5, 10.0)
+    for t in range(2):
+        m, a = pl.plan(t, None if t == 0 else np.zeros(4, np.float32))
+        pl.update(t, m, np.full((1, 4, 4), 0.25, np.float32), None if t == 0 else np.zeros((4, 4), np.float32))
+    m, a = pl.plan(2, np.array([0.0, np.nan, 0.0, 0.0], np.float32))
+    assert a and m.all()
+
+
 def test_planner_rejects_bad_arguments():
-    ref = np.zeros((2, 4, 4), np.float32)
     pl = binding.ditango_planner_t()
-    f = binding._f32(ref)
     init = binding.lib.ditango_planner_init
-    assert init(ctypes.byref(pl), 4, 2, 2, 4, 0.5, 0.1, 2, f) == lib.DITANGO_OK
-    for args in [(0, 2, 2, 4, 0.5, 0.1, 2), (33, 2, 2, 4, 0.5, 0.1, 2), (4, 0, 2, 4, 0.5, 0.1, 2),
-                 (4, 5, 2, 4, 0.5, 0.1, 2), (4, 2, 0, 4, 0.5, 0.1, 2), (4, 2, 2, 4, 1.5, 0.1, 2),
-                 (4, 2, 2, 4, 0.5, -0.1, 2), (4, 2, 2, 4, 0.5, 0.1, 1)]:
-        assert init(ctypes.byref(pl), *args, f) == lib.DITANGO_EINVAL, args
-    assert init(ctypes.byref(pl), 4, 2, 2, 4, 0.5, 0.1, 2, None) == lib.DITANGO_EINVAL
-    # an uninitialised planner is refused
+    assert init(ctypes.byref(pl), 4, 2, 2, 0.5, 0.1, 2) == lib.DITANGO_OK
+    for args in [(0, 2, 2, 0.5, 0.1, 2), (33, 2, 2, 0.5, 0.1, 2), (4, 0, 2, 0.5, 0.1, 2), (4, 5, 2, 0.5, 0.1, 2),
+                 (4, 2, 0, 0.5, 0.1, 2), (4, 2, 2, 1.5, 0.1, 2), (4, 2, 2, 0.5, -0.1, 2), (4, 2, 2, 0.5, 0.1, 1)]:
+        assert init(ctypes.byref(pl), *args) == lib.DITANGO_EINVAL, args
+    assert init(None, 4, 2, 2, 0.5, 0.1, 2) == lib.DITANGO_EINVAL
+    # an uninitialised planner is refused; drift is required after the first anchor
     blank = binding.ditango_planner_t()
     mask = np.zeros((4, 4), np.uint8)
-    sig = np.zeros((2, 4, 4, 4), np.float32)
-    assert binding.lib.ditango_planner_plan(ctypes.byref(blank), 0, binding._f32(sig), binding._u8(mask),
-                                            None) == lib.DITANGO_EINVAL
+    assert binding.lib.ditango_planner_plan(ctypes.byref(blank), 0, None, binding._u8(mask), None) == lib.DITANGO_EINVAL
     assert binding.lib.ditango_last_error()
+    p = lib.Planner(4, 2, 1, 0.5, 0.1)
+    m, a = p.plan(0, None)
+    with pytest.raises(lib.DitangoError):
+        p.update(0, m, None, None)                    # W is required at an anchor
+    p.update(0, m, np.full((1, 4, 4), 0.25, np.float32))
+    with pytest.raises(lib.DitangoError):
+        p.plan(1, None)                               # drift is required after the first anchor
