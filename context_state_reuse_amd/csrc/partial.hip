@@ -567,11 +567,29 @@ void partial_kernel(const PartialParams p) {
                                      (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
 #endif
   };
-  // Per-pair items with buffer loads: a descriptor per tile, based at the
-  // tile's first key and ending at the item's last key (scalar arithmetic),
-  // so each lane's offset is its fixed in-tile offset and rows past the last
-  // key read zeros (their scores are masked).  No per-lane address math.
-  constexpr bool kTileRsrc = DITANGO_BUFFER_LDS && !GROUPED;
+  // With buffer loads a tile gets a descriptor of its own, based at the
+  // tile's first key and ending at the last key of its contiguous run
+  // (scalar arithmetic), so each lane's offset is its fixed in-tile offset
+  // and rows past the end read zeros (their scores are masked): no per-lane
+  // address math.  A grouped item's tile that straddles the gap over q keeps
+  // the per-lane row mapping.
+  constexpr bool kTileRsrc = DITANGO_BUFFER_LDS;
+  auto tile_load = [&](const __bf16* base, __amdgpu_buffer_rsrc_t whole, int kt, int elem, int r, __bf16* dst)
+                       __attribute__((always_inline)) {
+    const int t0 = kt * kBc;
+    if constexpr (!GROUPED) {
+      (void)whole;
+      (void)r;
+      tile_load_lds<D>(base, t0, len_k, elem, dst);
+    } else {
+      if (t0 + kBc <= len0 || t0 >= len0 || len0 == len_k) {   // one side of the gap (block-uniform)
+        const bool after = t0 >= len0;
+        tile_load_lds<D>(base, t0 + (after ? p.S : 0), after ? len_k + p.S : len0, elem, dst);
+      } else {
+        dma(whole, base, tile_src(base, kt, r, elem), dst);
+      }
+    }
+  };
   auto gload_direct = [&](int kt_k, __bf16* kdst, int kt_v, __bf16* vdst) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < (G::direct ? kRoundsK : 0); ++i) {
@@ -579,7 +597,7 @@ void partial_kernel(const PartialParams p) {
       const int lds_elem0 = (i * WAVES + swave) * 64 * 8;   // first element this wave writes
       if (kt_k >= 0) {
         if constexpr (kTileRsrc) {
-          tile_load_lds<D>(Kh, kt_k * kBc, len_k, kgoff[i], kdst + lds_elem0);
+          tile_load(Kh, krsrc, kt_k, kgoff[i], krow_of[i], kdst + lds_elem0);
         } else {
           dma(krsrc, Kh, tile_src(Kh, kt_k, krow_of[i], kgoff[i]), kdst + lds_elem0);
         }
@@ -591,7 +609,7 @@ void partial_kernel(const PartialParams p) {
       const int lds_elem0 = (i * WAVES + swave) * 64 * 8;
       if (kt_v >= 0 && (G::vcpr == D / 8 || vgoff[i] >= 0)) {
         if constexpr (kTileRsrc) {
-          tile_load_lds<D>(Vh, kt_v * kBc, len_k, vgoff[i], vdst + lds_elem0);
+          tile_load(Vh, vrsrc, kt_v, vgoff[i], vrow_of[i], vdst + lds_elem0);
         } else {
           dma(vrsrc, Vh, tile_src(Vh, kt_v, vrow_of[i], vgoff[i]), vdst + lds_elem0);
         }
