@@ -354,8 +354,8 @@ template <int D, int NQT, int WAVES>
 constexpr int waves_per_simd() { return NQT == 2 ? 1 : (D == 64 && WAVES == 4 ? DITANGO_D64_WAVES_PER_SIMD : 2); }
 
 // Block = WAVES waves, each owning NQT column tiles of 32 queries.  NQT = 1
-// runs two waves per SIMD (<= 256 registers each); NQT = 2 halves the LDS
-// operand traffic per MFMA and runs one wave per SIMD.  K/V tiles of 64 keys
+// runs two waves per SIMD (<= 256 registers each; three at d = 64); NQT = 2
+// halves the LDS operand traffic per MFMA and runs one wave per SIMD.  K/V tiles of 64 keys
 // are double-buffered in LDS: the next tile's global loads are in flight
 // while the current tile is multiplied; one barrier per tile.
 template <int D, int WAVES, int NQT, int SCHED, int BC, bool GROUPED>

@@ -82,6 +82,22 @@ def test_library_planner_mixes_anchor_and_selective_steps():
     assert anchors == 2
 
 
+def test_planner_single_partition_has_no_groups():
+    # P = 1: the only pair is the local one, always computed; no group ever decides anything
+    pl = lib.Planner(1, 1, 2, 0.5, 0.1)
+    orc = AnchorPlanner(1, 1, 0.5, float(np.float32(0.1)))
+    for t in range(5):
+        D = None if t == 0 else np.array([0.05 * t], np.float32)
+        m, a = pl.plan(t, D)
+        mo, ao = orc.plan_drift(t, D if D is not None else np.zeros(1))
+        assert m.tolist() == [[1]] and a == ao and (mo == m).all()
+        W = np.ones((2, 1, 1), np.float32)
+        e = None if t == 0 else np.zeros((1, 1), np.float32)
+        pl.update(t, m, W if a else None, e if a else None)
+        orc.update_drift(t, m, np.ones((1, 1)) if a else None, e if a else None)
+        assert pl.eps == orc.eps
+
+
 def test_planner_nan_drift_forces_an_anchor():
     pl = lib.Planner(4, 2, 1, 0.5, 10.0)
     for t in range(2):
