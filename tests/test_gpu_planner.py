@@ -169,3 +169,39 @@ def test_planned_steps_match_oracle_with_their_masks():
             assert err.max() <= TOL_O_MAX and err.mean() <= TOL_O_MEAN and lerr.max() <= TOL_LSE, \
                 f"step {t} head {h}: OUT {err.max():.3g}/{err.mean():.3g}, LSE {lerr.max():.3g}"
     assert math.isfinite(runner.planner.eps)
+
+
+def test_planned_full_size_image_on_sampled_rows():
+    """The full image workload (16 heads, 16384 tokens) for 8 planned steps;
+    the oracle replays the chosen masks for two heads on sampled rows."""
+    import torch
+
+    import context_state_reuse_amd as lib
+    from oracle.reuse import run_workload
+    w = synth.get("image").scaled(steps=8)
+    heads = [0, w.H - 1]
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[q * w.S, min((q + 1) * w.S, w.N) - 1, *rng.integers(q * w.S, min((q + 1) * w.S, w.N), 4)]
+                                     for q in range(w.P)]))
+    cache = lib.StateCache(w.H, w.N, w.d, w.P)
+    runner = lib.PlannedSteps(cache, lib.Planner(w.P, 2, w.H, target_reuse=0.75, drift_max=0.1))
+    stream = synth.InputStream(w)
+    masks, outs, anchors = {}, {}, []
+    r_t = torch.tensor(rows, device="cuda")
+    for t in range(w.steps):
+        qb, kb, vb = stream.next()
+        mask, anchor, O, LSE = runner.step(t, to_device(qb), to_device(kb), to_device(vb))
+        masks[t] = mask.copy()
+        outs[t] = (O[heads][:, r_t].cpu().numpy(), LSE[heads][:, r_t].cpu().numpy())
+        anchors.append(anchor)
+        log(f"  [plan image] step {t}: anchor {anchor}, fresh {int(mask.sum())}/{w.P * w.P}")
+        del qb, kb, vb
+    assert anchors[0] and anchors[1] and not all(anchors)
+    ref = {}
+    run_workload(w, heads=heads, rows=rows, masks=masks, on_step=lambda t, m, r: ref.__setitem__(t, r))
+    for t in range(w.steps):
+        for hi, h in enumerate(heads):
+            err = np.abs(outs[t][0][hi].astype(np.float64) - ref[t]["O"][h])
+            lerr = np.abs(outs[t][1][hi].astype(np.float64) - ref[t]["LSE"][h])
+            assert err.max() <= TOL_O_MAX and err.mean() <= TOL_O_MEAN and lerr.max() <= TOL_LSE, \
+                f"step {t} head {h}: OUT {err.max():.3g}/{err.mean():.3g}, LSE {lerr.max():.3g}"
