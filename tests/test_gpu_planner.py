@@ -35,6 +35,8 @@ CASES = [
     _scaled("image", "image_small", 1, 57, 97, 2),            # d=72, ragged last partition
     _scaled("video_25", "video25_small", 5, 21, 29, 2),       # d=128
     _scaled("stress", "stress_small", 5, 16, 27, 2),          # d=64, P=32
+    _scaled("tiny", "one_token_last", 1, 3, 7, 2, P=5),       # N=21, S=5: last partition of 1 token
+    _scaled("tiny", "single_partition", 1, 9, 13, 1, P=1),    # P=1: the local pair only
 ]
 
 
