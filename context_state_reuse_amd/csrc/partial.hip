@@ -30,9 +30,9 @@
 // rescaled.  The final division by the row sum makes the result exact.
 //
 // Block = 4 or 8 waves of 32 query rows each (128 or 256 rows), two waves
-// per SIMD (<= 256 VGPRs each, no accumulator spills to AGPRs; three at
-// d = 64), so a SIMD can issue one wave's softmax while another's MFMAs
-// run.  K/V tiles of 64 keys are double-buffered in LDS and filled by
+// per SIMD at d = 128 (<= 256 VGPRs each, no accumulator spills to AGPRs),
+// three at d = 64 and 72 (4-wave blocks, <= 168 VGPRs), so a SIMD can issue
+// one wave's softmax while another's MFMAs run.  K/V tiles of 64 keys are double-buffered in LDS and filled by
 // direct buffer-to-LDS loads (buffer_load ... lds): the next tile's loads
 // are in flight while the current tile is multiplied.
 // The grid is the compacted list of fresh work items: no block exists for a
@@ -343,18 +343,29 @@ __device__ __attribute__((always_inline)) inline void tile_load_lds(const __bf16
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, elem * 2, 0, 0, 0);
 }
 
-// Waves per SIMD: two (<= 256 VGPRs each) for d = 72 and 128.  d = 64 fits
-// in 168 VGPRs and runs 4-wave blocks at three waves per SIMD (three blocks
-// per CU): the third wave keeps the VALU issuing while the others wait
-// (+7-11% on the 32-partition d = 64 workload; four spill).
+// Waves per SIMD.  d = 64 and 72 fit in 168 VGPRs (d = 72 with the plain
+// loop; 8 bytes per lane spill, outside the tile loop) and run 4-wave
+// blocks at three waves per SIMD (three blocks per CU): one wave alone
+// issues VALU at about half rate, so the third wave keeps the VALU busy
+// while the others wait (+7-11% at d = 64, +6-9% at d = 72; four spill).
+// d = 128 needs about 250 VGPRs, and three of its blocks would need more
+// LDS than a CU has, so it runs two (<= 256 VGPRs each).
 #ifndef DITANGO_D64_WAVES_PER_SIMD
 #define DITANGO_D64_WAVES_PER_SIMD 3
 #endif
+#ifndef DITANGO_D72_WAVES_PER_SIMD
+#define DITANGO_D72_WAVES_PER_SIMD 3
+#endif
 template <int D, int NQT, int WAVES>
-constexpr int waves_per_simd() { return NQT == 2 ? 1 : (D == 64 && WAVES == 4 ? DITANGO_D64_WAVES_PER_SIMD : 2); }
+constexpr int waves_per_simd() {
+  return NQT == 2 ? 1
+         : (D == 64 && WAVES == 4) ? DITANGO_D64_WAVES_PER_SIMD
+         : (D == 72 && WAVES == 4) ? DITANGO_D72_WAVES_PER_SIMD
+                                   : 2;
+}
 
 // Block = WAVES waves, each owning NQT column tiles of 32 queries.  NQT = 1
-// runs two waves per SIMD (<= 256 registers each; three at d = 64); NQT = 2
+// runs two waves per SIMD (<= 256 registers each; three at d = 64 and 72); NQT = 2
 // halves the LDS operand traffic per MFMA and runs one wave per SIMD.  K/V tiles of 64 keys
 // are double-buffered in LDS: the next tile's global loads are in flight
 // while the current tile is multiplied; one barrier per tile.
@@ -797,9 +808,10 @@ void partial_kernel(const PartialParams p) {
 }
 
 // Loop schedule per head dim, from side-by-side measurement on MI355X: the
-// in-wave pipeline (2) wins at d = 72 (about 3%), the plain loop (0) at
-// d = 64 (about 4%) and d = 128 (where the pipeline's second score buffer
-// leaves fewer registers for LDS prefetch).  A two-group ping-pong
+// plain loop (0) at d = 64 (about 4% ahead of the pipeline) and d = 128
+// (where the pipeline's second score buffer leaves fewer registers for LDS
+// prefetch); at d = 72 the in-wave pipeline (2) is about 2% ahead at two
+// waves per SIMD but spills at three, where the plain loop runs.  A two-group ping-pong
 // (FA3-style, one group on MFMA while the other runs the softmax, two
 // barriers per tile) was measured slower on every head dim and is not kept.
 #ifndef DITANGO_SCHED
@@ -814,7 +826,8 @@ void partial_kernel(const PartialParams p) {
 
 template <int D, int WAVES, int NQT>
 hipError_t launch(PartialParams& p, hipStream_t stream) {
-  constexpr int sched = DITANGO_SCHED >= 0 ? DITANGO_SCHED : (D == 72 ? 2 : 0);
+  constexpr int sched =
+      DITANGO_SCHED >= 0 ? DITANGO_SCHED : (D == 72 && waves_per_simd<D, NQT, WAVES>() == 2 ? 2 : 0);
   constexpr int bc = DITANGO_BC;
   static_assert(sched == 0 || sched == 2, "loop schedules: 0 (plain) or 2 (software-pipelined)");
   if (p.grouped) {
@@ -840,6 +853,7 @@ int partial_rows_per_block(int d, int S) {
   const int wide = 4 * 2 * 32, narrow = 4 * 32;   // 8 or 4 column tiles per block
   (void)qpw;
   if (d == 64 && DITANGO_D64_WAVES_PER_SIMD > 2) return narrow;   // 4-wave blocks, three per CU
+  if (d == 72 && DITANGO_D72_WAVES_PER_SIMD > 2) return narrow;
   // 256 rows per block unless 128-row blocks waste clearly less of a ragged
   // partition (e.g. S = 549: 3 x 256 rows hold 71% useful work, 5 x 128 hold 86%).
   const long waste_w = (S + wide - 1) / wide * static_cast<long>(wide) - S;
