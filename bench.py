@@ -71,6 +71,13 @@ def fresh_flops(w, mask) -> float:
     return float(4.0 * w.d * w.H * (np.outer(lens, lens) * mask).sum())
 
 
+def token_reuse(w, fresh: float) -> float:
+    """Reuse weighted by work: the share of the step's 4*N^2*d*H dense score
+    FLOPs not computed fresh (equals the pair share unless partitions differ
+    in length)."""
+    return 1.0 - fresh / (4.0 * w.N * w.N * w.d * w.H)
+
+
 def merge_bytes(w) -> float:
     """Per row and head: read P states of d+1 floats, write one."""
     return float(w.H * w.N * (w.P + 1) * (w.d + 1) * 4)
@@ -129,6 +136,17 @@ def stored_traffic(kernel: str, workload: str, src_hash: str):
         return None
 
 
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, heads: int, steps: int):
     """fp64 oracle on `steps` steady-state steps of `heads` heads (the anchor
     step 0 runs untimed first)."""
@@ -158,6 +176,7 @@ def cpu_baseline(w, heads: int, steps: int):
             n += 1
     dense = 4.0 * w.N * w.N * w.d * heads
     return {"value": dense * n / timed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": host_cpu_model(),
             "sample": f"{w.name}: {n} steady-state steps (after an untimed anchor step) for {heads} of {w.H} "
                       f"heads, all {w.N} rows; fp64 NumPy oracle, {timed:.1f} s timed; effective TFLOP/s "
                       f"counts 4*N^2*d per sampled head and step"}
@@ -327,7 +346,17 @@ def main():
     step(0)                                         # anchor: all fresh
     for i in range(args.warmup):
         step(steady[i % len(steady)])
+    # one more anchor step (all fresh, inputs of step 0), timed on its own and
+    # reported apart from the steady-state steps; the cache it leaves is the
+    # one the first anchor left
+    anchor_ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    step(0, anchor_ev)
+    if g:
+        computed_log.pop()
     torch.cuda.synchronize()
+    anchor_rec = {"ms": round(anchor_ev[0].elapsed_time(anchor_ev[2]), 4),
+                  "partial_ms": round(anchor_ev[0].elapsed_time(anchor_ev[1]), 4),
+                  "merge_ms": round(anchor_ev[1].elapsed_time(anchor_ev[2]), 4)}
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     masks = []
@@ -421,6 +450,7 @@ def main():
         "config": {"workload": f"{w.name}: {w.F}x{w.Hh}x{w.W} = {w.N} tokens, H={w.H}, d={w.d}, P={w.P}, "
                                f"{mask_desc} mask", "tokens": w.N, "heads": w.H, "head_dim": w.d,
                    "partitions": w.P, "reuse_ratio": round(float(reuse), 4),
+                   "reuse_ratio_tokens": round(token_reuse(w, float(fresh)), 4),
                    "state_cache": ("per pair, window states only, plus a residual [H][N][d]" if wr else cache_desc),
                    "cache_bytes": cache_bytes,
                    "fresh_pairs_per_step": float(np.mean([m.sum() for m in masks])),
@@ -435,6 +465,7 @@ def main():
                       "hbm_frac": round(merge_gbs / PEAK_HBM_GBS, 4), "bytes": mb},
         },
     }
+    out["anchor_step"] = anchor_rec
     if compose_rec is not None:
         out["group_compose"] = compose_rec
     if not args.no_cpu_baseline and not g and not wr:

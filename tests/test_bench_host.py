@@ -45,3 +45,24 @@ def test_group_accounting_at_group_size_one_is_per_pair():
     flops, mbytes = bench.group_work(w, 1, computed)
     assert flops == bench.fresh_flops(w, m)
     assert mbytes == bench.merge_bytes(w)
+
+
+def test_token_weighted_reuse():
+    # equal partitions: the work-weighted reuse is the pair share
+    w = synth.get("image")
+    m = np.zeros((w.P, w.P), np.uint8)
+    np.fill_diagonal(m, 1)
+    m[0, 1] = 1
+    assert abs(bench.token_reuse(w, bench.fresh_flops(w, m)) - (1 - m.mean())) < 1e-12
+    # stress: the ragged last partition (531 of 549 tokens) carries less work
+    w = synth.get("stress")
+    m = np.zeros((w.P, w.P), np.uint8)
+    m[w.P - 1, w.P - 1] = 1
+    lens = np.array([min(w.S, w.N - p * w.S) for p in range(w.P)], float)
+    expect = 1 - lens[-1] ** 2 / w.N ** 2
+    assert abs(bench.token_reuse(w, bench.fresh_flops(w, m)) - expect) < 1e-12
+    assert bench.token_reuse(w, bench.fresh_flops(w, m)) > 1 - m.mean()
+
+
+def test_host_cpu_model_is_named():
+    assert isinstance(bench.host_cpu_model(), str) and bench.host_cpu_model()
