@@ -357,6 +357,9 @@ int ditango_sig_drift(const float* A, const float* B, int32_t H, int32_t P, int3
                       float* out, void* stream) {
   if (!A || !B || !out) return fail(DITANGO_EINVAL, "A, B and out must be non-NULL");
   if (H < 1 || d < 1) return fail(DITANGO_EINVAL, "H=%d and d=%d must be >= 1", H, d);
+  if (P < 1 || P > DITANGO_MAX_P) return fail(DITANGO_EINVAL, "P=%d outside 1..%d", P, DITANGO_MAX_P);
+  if (static_cast<int64_t>(H) * d > 0x7fffffff)
+    return fail(DITANGO_EINVAL, "H=%d x d=%d values per pair exceed 2^31 - 1", H, d);
   int rc = check_mask(select, P);
   if (rc) return rc;
   ditango::DriftParams dp;
@@ -454,8 +457,12 @@ int ditango_planner_plan(ditango_planner_t* pl, int32_t step, const float* drift
       const int n = group_members(pl, q, j, mem);
       if (n == 0) continue;
       const double grow = std::max(0.0, pl->D[q] - pl->Dc[q][j]);
+      // no growth predicts no error, and a member of zero importance adds
+      // none (also when its scale ratio is +inf)
       double ase = 0.0;
-      for (int i = 0; i < n; ++i) ase += pl->W[q][mem[i]] * pl->alpha[q][mem[i]] * grow;
+      if (grow > 0.0)
+        for (int i = 0; i < n; ++i)
+          if (pl->W[q][mem[i]] > 0.0) ase += pl->W[q][mem[i]] * pl->alpha[q][mem[i]] * grow;
       if (ase > pl->eps)
         for (int i = 0; i < n; ++i) mask_out[q * P + mem[i]] = 1;
     }
@@ -471,6 +478,18 @@ int ditango_planner_update(ditango_planner_t* pl, int32_t step, const uint8_t* m
   if ((rc = check_mask(mask, P))) return rc;
   if (pl->anchor && !W) return fail(DITANGO_EINVAL, "W must be non-NULL at an anchor step");
   if (step < 0) return fail(DITANGO_EINVAL, "step=%d must be >= 0", step);
+  if (pl->anchor) {
+    // Statistics are checked before anything changes: a NaN would leave the
+    // errors below without an order.  A drift may be +inf (a signature that
+    // was zero has moved).
+    for (size_t i = 0; i < static_cast<size_t>(H) * P * P; ++i)
+      if (!(W[i] >= 0.0f) || !std::isfinite(W[i]))
+        return fail(DITANGO_EINVAL, "W[%zu] = %g is not a finite importance >= 0", i, static_cast<double>(W[i]));
+    if (e && pl->n_anchors > 0)
+      for (int i = 0; i < P * P; ++i)
+        if (i / P != i % P && !(e[i] >= 0.0f))
+          return fail(DITANGO_EINVAL, "e[%d][%d] = %g is not a drift >= 0", i / P, i % P, static_cast<double>(e[i]));
+  }
   if (pl->anchor) {
     for (int q = 0; q < P; ++q)
       for (int k = 0; k < P; ++k) {
@@ -489,7 +508,9 @@ int ditango_planner_update(ditango_planner_t* pl, int32_t step, const uint8_t* m
           const int n = group_members(pl, q, j, mem);
           if (n == 0) continue;
           double s = 0.0;
-          for (int i = 0; i < n; ++i) s += pl->W[q][mem[i]] * static_cast<double>(e[q * P + mem[i]]);
+          // a pair of zero importance adds nothing, whatever its drift
+          for (int i = 0; i < n; ++i)
+            if (pl->W[q][mem[i]] > 0.0) s += pl->W[q][mem[i]] * static_cast<double>(e[q * P + mem[i]]);
           E.push_back(s);
         }
       std::sort(E.begin(), E.end());

@@ -283,6 +283,8 @@ int ditango_group_mask_build(int32_t P, int32_t g, int32_t n, uint8_t* mask_out)
  *   between anchors: ASE(q,G) = sum over members k of w(q,k) alpha(q,k)
  *   max(0, D(q,t) - Dc(q,G)); G is computed iff ASE > eps, and then
  *   Dc(q,G) = D(q,t).
+ * In E and ASE a member of zero importance adds nothing (also when its drift
+ * or alpha is +inf), and ASE is 0 while D(q,t) <= Dc(q,G).
  * Groups: G_j = {j g .. min((j+1) g, P) - 1} without q; empty ones skipped. */
 
 /* Per-pair statistics of the cache after a step's merge, on `stream`:
@@ -302,7 +304,8 @@ int ditango_pair_stats(const ditango_states_t* st, const float* LSE, const uint8
  * [H][P][P][d]: for the pairs with select[q][k] = 1 (host uint8 [P][P]),
  * out[q*P + k] = ||A - B|| / ||B|| over the pair's H*d values (0 when both
  * are 0, +inf when only B is); out is device fp32 [P][P], other entries
- * untouched.  Errors: EINVAL, EHIP. */
+ * untouched.  Errors: EINVAL (NULL A, B, out or select, H or d < 1, P
+ * outside 1..32, H*d >= 2^31, a select entry other than 0 or 1), EHIP. */
 int ditango_sig_drift(const float* A, const float* B, int32_t H, int32_t P, int32_t d, const uint8_t* select,
                       float* out, void* stream);
 
@@ -341,7 +344,10 @@ int ditango_planner_plan(ditango_planner_t* pl, int32_t step, const float* drift
  * after the step (ditango_pair_stats), and e, host fp32 [P][P] (diagonal not
  * read), each pair's signature drift against the signature it had before the
  * step (ditango_sig_drift; NULL at the first anchor); between anchors it reads
- * only the mask and W, e may be NULL.  Errors: EINVAL. */
+ * only the mask (W and e may be NULL).  Errors: EINVAL (an uninitialised
+ * planner, a bad mask, step < 0, W NULL at an anchor, a W entry that is not
+ * finite and >= 0, an off-diagonal e entry that is NaN or < 0; e may hold
+ * +inf); nothing is changed on an error. */
 int ditango_planner_update(ditango_planner_t* pl, int32_t step, const uint8_t* mask, const float* W,
                            const float* e);
 

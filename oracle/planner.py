@@ -40,11 +40,13 @@ supports; parity unpinned against the page for the decision rule itself):
 * between anchors the predicted error of member k of group G is
   alpha(q, k) * max(0, D(q, t) - D(q, t_c(G))), where D(q, t_c(G)) is the
   local drift recorded when G was last computed (0 right after an anchor);
-  ASE(q, G) = sum_k w(q, k) * that;
+  ASE(q, G) = sum_k w(q, k) * that (0 when D has not grown, and a member of
+  zero importance adds nothing, even with an infinite alpha);
 * groups are those of the grouped cache: G_j = {j g .. min((j+1) g, P) - 1}
   minus q; a group with no member is skipped;
 * eps: the errors corrected at the anchor are E(q, G) = sum_k w(q, k) e(q, k)
-  over all groups with members; with the target reuse fraction rho (the
+  over all groups with members (a member of zero importance adds nothing,
+  even when its drift is +inf: its state has no weight in the output); with the target reuse fraction rho (the
   share of groups reused, which sets the acceleration), eps is the
   ceil(rho n)-th smallest of the n values (-inf when that is 0), and a
   group is reused when ASE <= eps.
@@ -151,7 +153,9 @@ class AnchorPlanner:
                 if not mem:
                     continue
                 grow = max(0.0, self.D[q] - self.Dc[q, j])
-                ase = sum(self.W[q, k] * self.alpha[q, k] * grow for k in mem)
+                # no growth predicts no error; a member of zero importance adds
+                # none (also when its scale ratio is +inf)
+                ase = sum(self.W[q, k] * self.alpha[q, k] * grow for k in mem if self.W[q, k] > 0) if grow > 0 else 0.0
                 if ase > self.eps:
                     mask[q, mem] = 1
         return mask, False
@@ -175,14 +179,23 @@ class AnchorPlanner:
         P = self.P
         mask = np.asarray(mask, dtype=np.uint8)
         if self.anchor:
-            self.W = np.asarray(W, dtype=np.float64).copy()
+            W = np.asarray(W, dtype=np.float64)
+            if not (np.all(np.isfinite(W)) and np.all(W >= 0)):
+                raise ValueError("importance must be finite and >= 0")
+            if e is not None and self.n_anchors > 0:
+                off = ~np.eye(P, dtype=bool)
+                if not np.all(np.asarray(e, dtype=np.float64)[off] >= 0):   # NaN fails too; +inf is a drift
+                    raise ValueError("pair drifts must be >= 0")
+            self.W = W.copy()
             if e is not None and self.n_anchors > 0:
                 e = np.asarray(e, dtype=np.float64)
                 for q in range(P):
                     for k in range(P):
                         if k != q:
                             self.alpha[q, k] = e[q, k] / self.D[q] if self.D[q] > 0 else 0.0
-                E = [sum(self.W[q, k] * e[q, k] for k in group_members(P, self.g, q, j))
+                # Eq. 6 weights each state's error by its importance: a pair of
+                # zero importance adds nothing, even with an unbounded drift
+                E = [sum(self.W[q, k] * e[q, k] for k in group_members(P, self.g, q, j) if self.W[q, k] > 0)
                      for q in range(P) for j in range(self.m) if group_members(P, self.g, q, j)]
                 self.eps = reuse_threshold(E, self.rho)
             self.Dc[:] = 0.0

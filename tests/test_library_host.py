@@ -211,3 +211,23 @@ def test_step_checks_everything_before_work():
     assert step(fake, fake, fake, _u8(m1), 2, ctypes.byref(f.st), fake, fake, None, None) == lib.DITANGO_EINVAL
     assert step(fake, fake, fake, _u8(m1), 4, ctypes.byref(f.st), None, fake, None, None) == lib.DITANGO_EINVAL
     assert np.all(f.tc == 3)
+
+
+def test_sig_drift_argument_checks():
+    """Every refusal happens before a launch: P outside 1..32 (the pair list
+    holds 32 x 32 entries), H*d beyond 2^31 - 1, NULL tables, a bad select."""
+    drift = binding.lib.ditango_sig_drift
+    fake = ctypes.c_void_p(0x30000)
+    sel33 = np.ones((33, 33), np.uint8)
+    assert drift(fake, fake, 2, 33, 64, binding._u8(sel33), fake, None) == lib.DITANGO_EINVAL
+    assert "P=33" in binding.lib.ditango_last_error().decode()
+    sel = np.ones((4, 4), np.uint8)
+    assert drift(fake, fake, 2, 0, 64, binding._u8(sel), fake, None) == lib.DITANGO_EINVAL
+    assert drift(fake, fake, 1 << 16, 4, 1 << 15, binding._u8(sel), fake, None) == lib.DITANGO_EINVAL
+    assert drift(None, fake, 2, 4, 64, binding._u8(sel), fake, None) == lib.DITANGO_EINVAL
+    assert drift(fake, fake, 2, 4, 64, binding._u8(sel), None, None) == lib.DITANGO_EINVAL
+    assert drift(fake, fake, 0, 4, 64, binding._u8(sel), fake, None) == lib.DITANGO_EINVAL
+    bad = sel.copy()
+    bad[2, 3] = 7
+    assert drift(fake, fake, 2, 4, 64, binding._u8(bad), fake, None) == lib.DITANGO_EINVAL
+    assert drift(fake, fake, 2, 4, 64, None, fake, None) == lib.DITANGO_EINVAL

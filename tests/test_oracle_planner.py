@@ -186,3 +186,79 @@ def test_planner_rejects_bad_parameters():
             AnchorPlanner(*args)
     with pytest.raises(ValueError):
         AnchorPlanner(4, 2, 0.5, 0.1, warmup=1)
+
+
+def _zero_importance_case():
+    """P = 3, g = 1 (every other partition is a group of its own).  Pair (0, 2)
+    has zero importance and an infinite drift at the anchor (its cached
+    signature was zero)."""
+    W = np.array([[0.5, 0.5, 0.0], [0.3, 0.5, 0.2], [0.4, 0.1, 0.5]])
+    e = np.array([[0.0, 0.2, math.inf], [0.1, 0.0, 0.4], [0.3, 0.5, 0.0]])
+    return W, e
+
+
+def test_planner_zero_importance_adds_no_error():
+    W, e = _zero_importance_case()
+    pl = AnchorPlanner(3, 1, target_reuse=0.5, drift_max=10.0)
+    ones = np.ones((3, 3), np.uint8)
+    m, a = pl.plan_drift(0, np.zeros(3))
+    pl.update_drift(0, m, W, None)
+    m, a = pl.plan_drift(1, np.full(3, 0.5))
+    assert a
+    pl.update_drift(1, ones, W, e)
+    # E: q0 {1} .5*.2 = .1, {2} 0 (zero importance); q1 {0} .03, {2} .08; q2 {0} .12, {1} .05
+    # sorted 0 .03 .05 .08 .1 .12, rho = .5 -> the 3rd: .05
+    assert pl.eps == pytest.approx(0.05)
+    assert math.isinf(pl.alpha[0, 2]) and pl.alpha[0, 1] == pytest.approx(0.4)
+    # q0 drifts to .6: {1} .5 * .4 * .6 = .12 > .05 computed; {2} has zero importance: reused
+    m, a = pl.plan_drift(2, np.array([0.6, 0.0, 0.0]))
+    assert not a
+    exp = np.eye(3, dtype=np.uint8)
+    exp[0, 1] = 1
+    assert (m == exp).all()
+
+
+def test_planner_no_growth_with_infinite_alpha():
+    """rho = 0 computes every group: also one whose alpha is +inf while its
+    local drift has not grown (no growth predicts no error, 0 > -inf)."""
+    W, e = _zero_importance_case()
+    W = np.full((3, 3), 1 / 3)
+    pl = AnchorPlanner(3, 1, target_reuse=0.0, drift_max=10.0)
+    m, _ = pl.plan_drift(0, np.zeros(3))
+    pl.update_drift(0, m, W, None)
+    m, _ = pl.plan_drift(1, np.full(3, 0.5))
+    pl.update_drift(1, m, W, e)
+    assert pl.eps == -math.inf and math.isinf(pl.alpha[0, 2])
+    m, a = pl.plan_drift(2, np.zeros(3))
+    assert not a and m.all()
+
+
+@pytest.mark.parametrize("what", ["W", "e"])
+def test_planner_rejects_nan_statistics(what):
+    W, e = _zero_importance_case()
+    pl = AnchorPlanner(3, 1, target_reuse=0.5, drift_max=10.0)
+    m, _ = pl.plan_drift(0, np.zeros(3))
+    pl.update_drift(0, m, W, None)
+    m, _ = pl.plan_drift(1, np.full(3, 0.5))
+    if what == "W":
+        W = W.copy()
+        W[1, 2] = math.nan
+    else:
+        e = e.copy()
+        e[2, 0] = math.nan
+    with pytest.raises(ValueError):
+        pl.update_drift(1, m, W, e)
+    assert pl.n_anchors == 1
+
+
+def test_planner_zero_importance_member_at_rho_zero():
+    """rho = 0 (eps = -inf) computes every group, also one whose only member
+    has zero importance and an infinite alpha: its ASE is 0, not 0 * inf."""
+    W, e = _zero_importance_case()
+    pl = AnchorPlanner(3, 1, target_reuse=0.0, drift_max=10.0)
+    m, _ = pl.plan_drift(0, np.zeros(3))
+    pl.update_drift(0, m, W, None)
+    m, _ = pl.plan_drift(1, np.full(3, 0.5))
+    pl.update_drift(1, m, W, e)
+    m, a = pl.plan_drift(2, np.array([0.6, 0.0, 0.0]))
+    assert not a and m.all()

@@ -127,3 +127,54 @@ def test_planner_rejects_bad_arguments():
     p.update(0, m, np.full((1, 4, 4), 0.25, np.float32))
     with pytest.raises(lib.DitangoError):
         p.plan(1, None)                               # drift is required after the first anchor
+
+
+def _zero_importance_inputs():
+    # importance per head (2 heads, same mean as the oracle pin's case)
+    Wm = np.array([[0.5, 0.5, 0.0], [0.3, 0.5, 0.2], [0.4, 0.1, 0.5]], np.float32)
+    e = np.array([[0.0, 0.2, np.inf], [0.1, 0.0, 0.4], [0.3, 0.5, 0.0]], np.float32)
+    return np.stack([Wm, Wm]), e
+
+
+@pytest.mark.parametrize("rho", [0.0, 0.5, 1.0])
+def test_library_planner_zero_importance_and_infinite_drift(rho):
+    W, e = _zero_importance_inputs()
+    cpp = lib.Planner(3, 1, 2, rho, 10.0)
+    orc = AnchorPlanner(3, 1, rho, 10.0)
+    for t, D in enumerate([None, [0.5] * 3, [0.6, 0.0, 0.0], [0.0] * 3, [0.9, 0.7, 0.2]]):
+        Dv = None if D is None else np.array(D, np.float32)
+        m_c, a_c = cpp.plan(t, Dv)
+        m_o, a_o = orc.plan_drift(t, Dv if Dv is not None else np.zeros(3))
+        assert a_c == a_o and (m_c == m_o).all(), (t, m_c, m_o)
+        if a_c:
+            cpp.update(t, m_c, W, None if t == 0 else e)
+            orc.update_drift(t, m_c, W.mean(axis=0).astype(np.float64), None if t == 0 else e)
+        else:
+            cpp.update(t, m_c)
+            orc.update_drift(t, m_c, None, None)
+        assert cpp.pl.eps == orc.eps or (math.isinf(cpp.pl.eps) and cpp.pl.eps == orc.eps)
+
+
+@pytest.mark.parametrize("what", ["W", "e", "e_negative"])
+def test_library_planner_rejects_nan_statistics_unchanged(what):
+    W, e = _zero_importance_inputs()
+    p = lib.Planner(3, 1, 2, 0.5, 10.0)
+    m, _ = p.plan(0, None)
+    p.update(0, m, W)
+    m, a = p.plan(1, np.full(3, 0.5, np.float32))
+    assert a
+    if what == "W":
+        W = W.copy()
+        W[1, 0, 2] = np.nan
+    elif what == "e":
+        e = e.copy()
+        e[2, 0] = np.nan
+    else:
+        e = e.copy()
+        e[1, 2] = -0.5
+    before = bytes(p.pl)
+    with pytest.raises(lib.DitangoError):
+        p.update(1, m, W, e)
+    assert bytes(p.pl) == before                      # nothing changed
+    p.update(1, m, *_zero_importance_inputs())        # valid statistics are still taken
+    assert p.pl.n_anchors == 2
