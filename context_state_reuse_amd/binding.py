@@ -176,6 +176,17 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _torch_stream(stream):
+    """The torch stream for `stream` (None: torch's current one), so that the
+    binding's own torch work (fills, copies) is ordered with the launches."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream)
+    return stream
+
+
 def make_shape(H: int, N: int, d: int, P: int, scale: float | None = None) -> ditango_shape_t:
     return ditango_shape_t(H, N, d, P, float(1.0 / np.sqrt(d) if scale is None else scale))
 
@@ -276,7 +287,8 @@ def ditango_pair_stats(cache: StateCache, LSE, select, W=None, SIG=None, stream=
     if want_w and W is None:
         W = torch.empty((cache.H, cache.P, cache.P), dtype=torch.float32, device=dev)
     if SIG is None:
-        SIG = torch.zeros((cache.H, cache.P, cache.P, cache.d), dtype=torch.float32, device=dev)
+        with torch.cuda.stream(_torch_stream(stream)):   # the fill precedes the kernel on its stream
+            SIG = torch.zeros((cache.H, cache.P, cache.P, cache.d), dtype=torch.float32, device=dev)
     checks = [(SIG, (cache.H, cache.P, cache.P, cache.d), "SIG")]
     if want_w:
         checks += [(LSE, (cache.H, cache.N), "LSE"), (W, (cache.H, cache.P, cache.P), "W")]
@@ -296,7 +308,8 @@ def ditango_sig_drift(A, B, select, out=None, stream=None):
     H, P, _, d = A.shape
     m = _mask(select, P)
     if out is None:
-        out = torch.zeros((P, P), dtype=torch.float32, device=A.device)
+        with torch.cuda.stream(_torch_stream(stream)):   # the fill precedes the kernel on its stream
+            out = torch.zeros((P, P), dtype=torch.float32, device=A.device)
     for t, shp, nm in ((A, (H, P, P, d), "A"), (B, (H, P, P, d), "B"), (out, (P, P), "out")):
         if not (t.is_cuda and t.dtype == torch.float32 and t.is_contiguous() and tuple(t.shape) == shp):
             raise ValueError(f"{nm} must be a contiguous float32 device tensor of shape {shp}")
@@ -375,11 +388,20 @@ class PlannedSteps:
         self.DR = torch.zeros((P, P), dtype=torch.float32, device=dev)
         self.O = torch.empty((H, cache.N, d), dtype=torch.float32, device=dev)
         self.LSE = torch.zeros((H, cache.N), dtype=torch.float32, device=dev)
+        # the fills above are done before any step uses the tables, on any stream
+        torch.cuda.current_stream().synchronize()
         self.eye = np.eye(P, dtype=np.uint8)
         self.off = (1 - self.eye).astype(np.uint8)
 
     def step(self, t: int, Q, K, V, stream=None):
-        """Returns (mask, anchor, O, LSE); O and LSE are this object's buffers."""
+        """Returns (mask, anchor, O, LSE); O and LSE are this object's buffers.
+        Everything runs on `stream` (default: torch's current stream): the
+        launches and the table copies alike."""
+        import torch
+        with torch.cuda.stream(_torch_stream(stream)):
+            return self._step(t, Q, K, V, stream)
+
+    def _step(self, t: int, Q, K, V, stream):
         c, pl = self.cache, self.planner
         drift = None
         if pl.n_anchors:

@@ -207,3 +207,41 @@ def test_planned_full_size_image_on_sampled_rows():
             lerr = np.abs(outs[t][1][hi].astype(np.float64) - ref[t]["LSE"][h])
             assert err.max() <= TOL_O_MAX and err.mean() <= TOL_O_MEAN and lerr.max() <= TOL_LSE, \
                 f"step {t} head {h}: OUT {err.max():.3g}/{err.mean():.3g}, LSE {lerr.max():.3g}"
+
+
+def test_planned_steps_on_a_side_stream_match_the_current_stream():
+    """The same planned steps driven on a second (default-priority) stream:
+    every launch and every table copy of a step runs on that stream, so
+    masks and outputs are bit-identical to the run on the current stream
+    (all kernels here sum in a fixed order).  The statistics calls that
+    allocate their outputs are run on the side stream too."""
+    import torch
+
+    import context_state_reuse_amd as lib
+    w = _scaled("image", "image_plan_stream", 1, 57, 97, 2, steps=6)
+    side = torch.cuda.Stream()
+    runs = []
+    for stream in (None, side):
+        cache = lib.StateCache(w.H, w.N, w.d, w.P)
+        runner = lib.PlannedSteps(cache, lib.Planner(w.P, 2, w.H, target_reuse=0.6, drift_max=0.1))
+        inputs = synth.InputStream(w)
+        got = []
+        for t in range(w.steps):
+            qb, kb, vb = inputs.next()
+            Q, K, V = to_device(qb), to_device(kb), to_device(vb)
+            if stream is not None:
+                stream.wait_stream(torch.cuda.current_stream())    # inputs written on the current stream
+            mask, anchor, O, LSE = runner.step(t, Q, K, V, stream)
+            torch.cuda.synchronize()
+            got.append((mask.copy(), anchor, O.cpu().numpy().copy(), LSE.cpu().numpy().copy()))
+        if stream is not None:
+            _, sig = lib.ditango_pair_stats(cache, None, np.eye(w.P, dtype=np.uint8), stream=stream, want_w=False)
+            dr = lib.ditango_sig_drift(sig, sig, np.ones((w.P, w.P), np.uint8), stream=stream)
+            torch.cuda.synchronize()
+            assert (dr.cpu().numpy() == 0).all()
+        runs.append(got)
+        log(f"  [stream] run on {'side' if stream is not None else 'current'} stream: "
+            f"anchors {[t for t, g in enumerate(got) if g[1]]}")
+    for t, (a, b) in enumerate(zip(*runs)):
+        assert (a[0] == b[0]).all() and a[1] == b[1], f"step {t}: masks differ"
+        assert np.array_equal(a[2], b[2]) and np.array_equal(a[3], b[3]), f"step {t}: outputs differ"
