@@ -408,7 +408,7 @@ class PlannedSteps:
             ditango_attn_partial(Q, K, V, self.eye, c, stream)
             ditango_pair_stats(c, None, self.eye, None, self.SIG, stream, want_w=False)
             ditango_sig_drift(self.SIG, self.REF, self.eye, self.DR, stream)
-            drift = self.DR.diagonal().cpu().numpy()
+            drift = self.DR.cpu().numpy().diagonal().copy()   # P*P floats: no gather kernel
         mask, anchor = pl.plan(t, drift)
         if anchor and pl.n_anchors:
             self.OLD.copy_(self.SIG)
@@ -419,7 +419,12 @@ class PlannedSteps:
             ditango_attn_partial(Q, K, V, rest, c, stream)
         ditango_state_cache_update(c, mask, t)
         ditango_state_merge(c, self.O, self.LSE, stream)
-        ditango_pair_stats(c, self.LSE, mask, self.W, self.SIG, stream, want_w=anchor)
+        # signatures of the pairs computed after the plan (the local ones, when
+        # already refreshed above, are not read again); the importance of every
+        # pair at an anchor
+        refresh = rest if pl.n_anchors else mask
+        if anchor or rest.any():
+            ditango_pair_stats(c, self.LSE, refresh, self.W, self.SIG, stream, want_w=anchor)
         if anchor:
             e = None
             if pl.n_anchors:

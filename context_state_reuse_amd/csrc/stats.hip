@@ -10,9 +10,10 @@
 //                  the signature on which the planner measures how far a
 //                  state has drifted.
 // One block per (head, q, k) -- per selected pair only when W is not
-// wanted -- 256 threads; every sum is taken in a fixed
-// order (per-thread strided partial sums, then a fixed tree), so results do
-// not vary from run to run.  Reads the LSE of every slot and the OUT of the
+// wanted -- of 1024 threads, so that a step's few blocks (one per head and
+// local pair) keep enough loads in flight; every sum is taken in a fixed
+// order (per-thread strided partial sums over four interleaved
+// accumulators, then a fixed tree), so results do not vary from run to run.  Reads the LSE of every slot and the OUT of the
 // selected ones: a few per cent of one merge.
 
 #include <hip/hip_runtime.h>
@@ -24,14 +25,15 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;        // drift kernel
+constexpr int kStatsThreads = 1024;  // stats kernel
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void stats_kernel(const StatsParams p) {
+__global__ __launch_bounds__(kStatsThreads) void stats_kernel(const StatsParams p) {
   constexpr int C = D / 4;                  // 16-byte chunks per row
-  constexpr int RG = kThreads / C;          // rows summed in parallel
+  constexpr int RG = kStatsThreads / C;     // rows summed in parallel
   __shared__ f32x4 part[RG][C];
-  __shared__ float wpart[kThreads / 64];
+  __shared__ float wpart[kStatsThreads / 64];
 
   const int tid = threadIdx.x;
   const int n = p.W ? p.P * p.P : p.n_pairs;          // blocks per head
@@ -45,7 +47,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const StatsParams p) {
     const float* ls = p.LSE_slot + slot * p.S;
     const float* lm = p.LSE + static_cast<size_t>(h) * p.N + static_cast<size_t>(q) * p.S;
     float acc = 0.0f;
-    for (int r = tid; r < len_q; r += kThreads) acc += __expf(ls[r] - lm[r]);
+    for (int r = tid; r < len_q; r += kStatsThreads) acc += __expf(ls[r] - lm[r]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
     if ((tid & 63) == 0) wpart[tid >> 6] = acc;
@@ -53,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const StatsParams p) {
     if (tid == 0) {
       float s = 0.0f;
 #pragma unroll
-      for (int i = 0; i < kThreads / 64; ++i) s += wpart[i];
+      for (int i = 0; i < kStatsThreads / 64; ++i) s += wpart[i];
       p.W[slot] = s / static_cast<float>(len_q);
     }
   }
@@ -62,10 +64,19 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const StatsParams p) {
   if (!((p.sel[q] >> k) & 1u)) return;
   const float* o = p.O + slot * p.S * D;
   const int rg = tid / C, c = tid % C;
-  f32x4 a = {0.f, 0.f, 0.f, 0.f};
   if (rg < RG) {
-    for (int r = rg; r < len_q; r += RG) a += *reinterpret_cast<const f32x4*>(o + static_cast<size_t>(r) * D + 4 * c);
-    part[rg][c] = a;
+    // four independent accumulators: four loads in flight per thread
+    auto row = [&](int r) { return *reinterpret_cast<const f32x4*>(o + static_cast<size_t>(r) * D + 4 * c); };
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0, a3 = a0;
+    int r = rg;
+    for (; r + 3 * RG < len_q; r += 4 * RG) {
+      a0 += row(r);
+      a1 += row(r + RG);
+      a2 += row(r + 2 * RG);
+      a3 += row(r + 3 * RG);
+    }
+    for (; r < len_q; r += RG) a0 += row(r);
+    part[rg][c] = (a0 + a1) + (a2 + a3);
   }
   __syncthreads();
   if (tid < C) {
@@ -124,7 +135,7 @@ hipError_t launch_stats(const StatsParams& p, hipStream_t stream) {
   const int64_t blocks = static_cast<int64_t>(p.H) * (p.W ? p.P * p.P : p.n_pairs);
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kStatsThreads);
   switch (p.d) {
     case 64: hipLaunchKernelGGL(stats_kernel<64>, grid, block, 0, stream, p); break;
     case 72: hipLaunchKernelGGL(stats_kernel<72>, grid, block, 0, stream, p); break;
