@@ -465,6 +465,10 @@ def main():
                       "hbm_frac": round(merge_gbs / PEAK_HBM_GBS, 4), "bytes": mb},
         },
     }
+    # HBM fraction of the whole step: the merge's bytes plus the fresh states
+    # stored, over the step time
+    out["step_hbm"] = {"bytes": float(mb + sb),
+                       "frac": round((mb + sb) / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     out["anchor_step"] = anchor_rec
     if compose_rec is not None:
         out["group_compose"] = compose_rec
