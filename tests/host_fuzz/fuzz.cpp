@@ -7,7 +7,31 @@
 #include <random>
 #include <vector>
 #include "ditango.h"
-namespace ditango { extern long g_partial, g_merge, g_stats, g_drift; }
+namespace ditango {
+extern long g_partial, g_merge, g_stats, g_drift;
+extern int g_last_n, g_last_blocks, g_last_qtiles;
+extern uint16_t g_last_pairs[DITANGO_MAX_P * DITANGO_MAX_P];
+}
+
+// The per-pair work list of the last launch holds exactly the fresh pairs
+// of `mask`, once each, and the grid is heads x pairs x query tiles.
+static void check_work_list(const ditango_states_t& st, const uint8_t* mask) {
+  const int P = st.shape.P;
+  std::vector<int> seen(P * P, 0);
+  int fresh = 0;
+  for (int i = 0; i < P * P; ++i) fresh += mask[i] == 1;
+  bool ok = ditango::g_last_n == fresh;
+  for (int i = 0; ok && i < ditango::g_last_n; ++i) {
+    const int id = ditango::g_last_pairs[i];
+    ok = id < P * P && mask[id] == 1 && seen[id]++ == 0;
+  }
+  ok = ok && static_cast<long long>(ditango::g_last_blocks) ==
+                 static_cast<long long>(st.shape.H) * fresh * ditango::g_last_qtiles;
+  if (!ok) {
+    fprintf(stderr, "work list does not match the mask (P=%d, fresh=%d, listed=%d)\n", P, fresh, ditango::g_last_n);
+    abort();
+  }
+}
 
 static std::mt19937_64 rng(12345);
 static int ri(int a, int b) { return std::uniform_int_distribution<int>(a, b)(rng); }
@@ -72,7 +96,15 @@ int main() {
       for (int i = 0; i < P * P; ++i) m[i] = t == 0 ? 1 : (ri(0, 30) ? ri(0, 1) : 2);
       for (int q = 0; q < P; ++q) m[q * P + q] = m[q * P + q] ? m[q * P + q] : (ri(0, 4) ? 1 : 0);
       std::vector<uint8_t> reused(P * P);
-      ++calls; oks += ditango_attn_partial(fake(0x300000), fake(0x400000), fake(0x500000), m.data(), &st, nullptr) == 0;
+      ditango::g_last_n = -1;
+      int prc = ditango_attn_partial(fake(0x300000), fake(0x400000), fake(0x500000), m.data(), &st, nullptr);
+      ++calls; oks += prc == 0;
+      if (prc == 0 && ditango::g_last_n >= 0) check_work_list(st, m.data());
+      if (prc == 0) {   // no launch only when nothing is fresh
+        bool any = false;
+        for (int i = 0; i < P * P; ++i) any = any || m[i];
+        if (any != (ditango::g_last_n >= 0)) { fprintf(stderr, "launch presence does not match the mask\n"); abort(); }
+      }
       ++calls; oks += ditango_state_cache_update(&st, m.data(), ri(0, 4) ? t : ri(-2, 10), reused.data()) == 0;
       ++calls; oks += ditango_state_merge(&st, fake(0x600000), fake(0x700000), nullptr) == 0;
       ++calls; oks += ditango_step(fake(0x300000), fake(0x400000), fake(0x500000), m.data(), t + 10, &st, fake(0x600000),

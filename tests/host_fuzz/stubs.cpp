@@ -8,6 +8,9 @@
 namespace ditango {
 int partial_rows_per_block(int d, int S) { (void)d; return S > 300 ? 256 : 128; }
 long g_partial = 0, g_merge = 0, g_stats = 0, g_drift = 0;
+// the last per-pair work list, for the driver to compare with its mask
+int g_last_n = -1, g_last_blocks = -1, g_last_qtiles = -1;
+uint16_t g_last_pairs[DITANGO_MAX_P * DITANGO_MAX_P];
 hipError_t launch_partial(PartialParams& p, int rows, hipStream_t) {
   REQUIRE(p.n_pairs >= 1 && p.n_pairs <= DITANGO_MAX_P * DITANGO_MAX_P);
   REQUIRE(p.P >= 1 && p.P <= DITANGO_MAX_P && p.S >= 1 && p.N >= p.P);
@@ -16,6 +19,12 @@ hipError_t launch_partial(PartialParams& p, int rows, hipStream_t) {
   for (int i = 0; i < p.n_pairs; ++i) {
     if (!p.grouped) REQUIRE(p.pairs[i] < p.P * p.P);
     else { int q = p.pairs[i] >> 6, s = p.pairs[i] & 63; REQUIRE(q < p.P && s < DITANGO_MAX_SLOTS && p.gO[s] && p.gLSE[s]); }
+  }
+  if (!p.grouped) {
+    g_last_n = p.n_pairs;
+    g_last_blocks = p.n_blocks;
+    g_last_qtiles = p.q_tiles;
+    for (int i = 0; i < p.n_pairs; ++i) g_last_pairs[i] = p.pairs[i];
   }
   ++g_partial; return hipSuccess;
 }

@@ -231,3 +231,32 @@ def test_sig_drift_argument_checks():
     bad[2, 3] = 7
     assert drift(fake, fake, 2, 4, 64, binding._u8(bad), fake, None) == lib.DITANGO_EINVAL
     assert drift(fake, fake, 2, 4, 64, None, fake, None) == lib.DITANGO_EINVAL
+
+
+def test_evicted_pair_is_refused_until_computed_again():
+    """A caller that drops a cached state (t_c set back to -1, e.g. to free
+    memory) cannot reuse it: the next step that marks it REUSE is refused
+    before any launch, and a step that computes it fresh restores it."""
+    f = _FakeStates(P=4)
+    upd = binding.lib.ditango_state_cache_update
+    fake = ctypes.c_void_p(0x30000)
+    ones = np.ones((4, 4), np.uint8)
+    assert upd(ctypes.byref(f.st), _u8(ones), 0, None) == 0          # anchor
+    m1 = radius_mask(4, 1)
+    assert upd(ctypes.byref(f.st), _u8(m1), 1, None) == 0
+    f.tc[0 * 4 + 3] = -1                                              # evict pair (0, 3), reused by m1
+    for call in (lambda: binding.lib.ditango_attn_partial(fake, fake, fake, _u8(m1), ctypes.byref(f.st), None),
+                 lambda: binding.lib.ditango_step(fake, fake, fake, _u8(m1), 2, ctypes.byref(f.st), fake, fake,
+                                                  None, None),
+                 lambda: binding.lib.ditango_state_merge(ctypes.byref(f.st), fake, fake, None)):
+        assert call() == lib.DITANGO_ENOCACHE
+        assert "(q=0, k=3)" in binding.lib.ditango_last_error().decode()
+    tc_before = f.tc.copy()
+    assert upd(ctypes.byref(f.st), _u8(m1), 2, None) == lib.DITANGO_EINVAL
+    assert np.array_equal(f.tc, tc_before)                            # a refused commit changes nothing
+    # computing the pair again makes the cache whole
+    m2 = m1.copy()
+    m2[0, 3] = 1
+    assert upd(ctypes.byref(f.st), _u8(m2), 2, None) == 0
+    assert f.tc[3] == 2 and (f.tc >= 0).all()
+    assert upd(ctypes.byref(f.st), _u8(m1), 3, None) == 0
