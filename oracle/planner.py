@@ -146,7 +146,21 @@ class AnchorPlanner:
         self.anchor = t < self.warmup or self.n_anchors == 0 or not float(np.max(self.D)) <= self.drift_max
         if self.anchor:
             return np.ones((P, P), dtype=np.uint8), True
+        ase = self.predicted_errors()
         mask = np.eye(P, dtype=np.uint8)
+        for q in range(P):
+            for j in range(self.m):
+                mem = group_members(P, self.g, q, j)
+                if mem and ase[q, j] > self.eps:
+                    mask[q, mem] = 1
+        return mask, False
+
+    def predicted_errors(self) -> np.ndarray:
+        """ASE of every group [P][m] from the current local drifts (NaN for a
+        group without members): importance times the scale ratio times the
+        local drift's growth since the group was last computed."""
+        P = self.P
+        ase = np.full((P, self.m), np.nan)
         for q in range(P):
             for j in range(self.m):
                 mem = group_members(P, self.g, q, j)
@@ -155,10 +169,9 @@ class AnchorPlanner:
                 grow = max(0.0, self.D[q] - self.Dc[q, j])
                 # no growth predicts no error; a member of zero importance adds
                 # none (also when its scale ratio is +inf)
-                ase = sum(self.W[q, k] * self.alpha[q, k] * grow for k in mem if self.W[q, k] > 0) if grow > 0 else 0.0
-                if ase > self.eps:
-                    mask[q, mem] = 1
-        return mask, False
+                ase[q, j] = sum(self.W[q, k] * self.alpha[q, k] * grow for k in mem if self.W[q, k] > 0) \
+                    if grow > 0 else 0.0
+        return ase
 
     def update(self, t: int, mask, W_heads, sig_new, sig_old=None) -> None:
         P = self.P

@@ -84,3 +84,27 @@ def test_random_mask_small_by_hand():
         want[q, q] = 1
         want[q, c[rng.next() % 3]] = 1
     assert np.array_equal(random_mask(4, 2, 77), want)
+
+
+def test_random_mask_several_swaps_by_hand():
+    """Rows whose draws are the published SplitMix64 check values (golden
+    file), with two and three swaps per row, worked by hand:
+
+    seed 0, P = 5, n = 3 (draws o0..o3; candidates of row q are [k != q]):
+      row 0: c = [1, 2, 3, 4]; o0 mod 4 = 3 -> swap c[0], c[3] -> [4, 2, 3, 1];
+             o1 mod 3 = 0 -> j = 1, no swap; fresh = {0} + {4, 2}
+      row 1: c = [0, 2, 3, 4]; o2 mod 4 = 3 -> [4, 2, 3, 0];
+             o3 mod 3 = 1 -> j = 2 -> swap c[1], c[2] -> [4, 3, 2, 0];
+             fresh = {1} + {4, 3}
+    seed 1234567, P = 5, n = 4 (draws d0..d2):
+      row 0: c = [1, 2, 3, 4]; d0 mod 4 = 1 -> [2, 1, 3, 4];
+             d1 mod 3 = 1 -> j = 2 -> [2, 3, 1, 4]; d2 mod 2 = 1 -> j = 3 ->
+             [2, 3, 4, 1]; fresh = {0} + {2, 3, 4}
+    A modulus of P-1 at every swap, a dropped "+ i", or taking c[1..n-1]
+    changes at least one of these rows.
+    """
+    m = random_mask(5, 3, 0)
+    assert np.flatnonzero(m[0]).tolist() == [0, 2, 4]
+    assert np.flatnonzero(m[1]).tolist() == [1, 3, 4]
+    m = random_mask(5, 4, 1234567)
+    assert np.flatnonzero(m[0]).tolist() == [0, 2, 3, 4]
