@@ -44,7 +44,7 @@ EXPORTED = ("ditango_states_bytes", "ditango_states_init", "ditango_attn_partial
             "ditango_last_error", "ditango_version",
             "ditango_group_slots", "ditango_gstates_slot_bytes", "ditango_gstates_init",
             "ditango_group_attn_partial", "ditango_group_cache_update", "ditango_group_merge",
-            "ditango_group_compose", "ditango_group_reset", "ditango_group_mask_build",
+            "ditango_group_compose", "ditango_group_fit", "ditango_group_reset", "ditango_group_mask_build",
             "ditango_window_residual_merge", "ditango_step", "ditango_pair_stats", "ditango_sig_drift",
             "ditango_planner_init", "ditango_planner_plan", "ditango_planner_update")
 
@@ -104,7 +104,7 @@ def _load():
     lib.ditango_state_merge.restype = ctypes.c_int
     lib.ditango_state_merge.argtypes = [ctypes.POINTER(ditango_states_t), vp, vp, vp]
     lib.ditango_mask_build.restype = ctypes.c_int
-    lib.ditango_mask_build.argtypes = [i32, i32, i32, ctypes.c_uint64, u8p]
+    lib.ditango_mask_build.argtypes = [i32, i32, i32, ctypes.c_uint64, i32, u8p]
     lib.ditango_last_error.restype = ctypes.c_char_p
     lib.ditango_last_error.argtypes = []
     lib.ditango_version.restype = ctypes.c_int32
@@ -126,6 +126,8 @@ def _load():
     lib.ditango_group_merge.argtypes = [gst, vp, vp, vp]
     lib.ditango_group_compose.restype = ctypes.c_int
     lib.ditango_group_compose.argtypes = [gst, i32, vp]
+    lib.ditango_group_fit.restype = ctypes.c_int
+    lib.ditango_group_fit.argtypes = [gst, ctypes.c_size_t, i32, vp, ctypes.POINTER(ctypes.c_int32)]
     lib.ditango_group_reset.restype = ctypes.c_int
     lib.ditango_group_reset.argtypes = [gst, ptab, ptab]
     lib.ditango_group_mask_build.restype = ctypes.c_int
@@ -459,10 +461,12 @@ def ditango_window_residual_merge(cache: StateCache, window, mode: int, R, O=Non
     return O, LSE
 
 
-def ditango_mask_build(policy, P: int, n: int = 0, seed: int = 0) -> np.ndarray:
+def ditango_mask_build(policy, P: int, n: int = 0, seed: int = 0, step: int = 1) -> np.ndarray:
+    """Mask of step `step` (0: the all-fresh anchor) under `policy`; the
+    random policy draws with seed + step."""
     pol = MASK_POLICIES[policy] if isinstance(policy, str) else int(policy)
     out = np.zeros((P, P), dtype=np.uint8) if 1 <= P <= DITANGO_MAX_P else np.zeros(1, dtype=np.uint8)
-    _check(lib.ditango_mask_build(pol, int(P), int(n), ctypes.c_uint64(seed & ((1 << 64) - 1)), _u8(out)))
+    _check(lib.ditango_mask_build(pol, int(P), int(n), ctypes.c_uint64(seed & ((1 << 64) - 1)), int(step), _u8(out)))
     return out
 
 
@@ -472,9 +476,7 @@ def ditango_version() -> int:
 
 def workload_mask(w, t: int) -> np.ndarray:
     """Mask of step t of a workload, built by the library (step 0: all fresh)."""
-    if t == 0:
-        return ditango_mask_build("all", w.P)
-    return ditango_mask_build(w.policy, w.P, w.n_fresh, 1000 * w.cfg_id + t)
+    return ditango_mask_build(w.policy, w.P, w.n_fresh, 1000 * w.cfg_id, t)
 
 
 # ------------------------------------------------------------ grouped cache
@@ -578,6 +580,20 @@ class GroupedStateCache:
             # the released buffers are read by the queued group merges
             torch.cuda.synchronize()
             del self.O[n:], self.LSE[n:]
+
+    def fit(self, budget_bytes: int, k: int = 2, stream=None) -> int:
+        """Memory trigger of Dynamic Group State Compose: merge groups k at a
+        time while the cache's slot memory exceeds budget_bytes; frees the
+        released slots.  Returns the number of merges."""
+        import torch
+        merges = ctypes.c_int32(0)
+        _check(lib.ditango_group_fit(ctypes.byref(self.st), ctypes.c_size_t(int(budget_bytes)), int(k),
+                                     _stream(stream), ctypes.byref(merges)))
+        n = self.n_slots
+        if len(self.O) > n:
+            torch.cuda.synchronize()
+            del self.O[n:], self.LSE[n:]
+        return int(merges.value)
 
     def reset(self) -> None:
         """Back to the original group size with every slot empty (before an anchor step)."""

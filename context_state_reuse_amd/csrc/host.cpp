@@ -54,8 +54,10 @@ int check_shape(const ditango_shape_t* s, int32_t* S_out) {
   if (!(s->scale > 0.0f) || !std::isfinite(s->scale))
     return fail(DITANGO_EINVAL, "scale must be finite and > 0");
   if (s->N < s->P) return fail(DITANGO_EINVAL, "N=%d < P=%d leaves an empty partition", s->N, s->P);
-  if (static_cast<int64_t>(s->N) * s->d > (int64_t{1} << 30))
-    return fail(DITANGO_EINVAL, "N=%d x d=%d exceeds 2^30 elements per head", s->N, s->d);
+  // K/V of one head are addressed through buffer descriptors with 32-bit
+  // byte offsets: N * d * 2 bytes must stay below 2^31.
+  if (static_cast<int64_t>(s->N) * s->d >= (int64_t{1} << 30))
+    return fail(DITANGO_EINVAL, "N=%d x d=%d must stay below 2^30 elements per head", s->N, s->d);
   const int64_t S = (static_cast<int64_t>(s->N) + s->P - 1) / s->P;
   if (static_cast<int64_t>(s->P - 1) * S >= s->N)
     return fail(DITANGO_EINVAL, "N=%d, P=%d: partitions of %lld tokens leave the last one empty",
@@ -184,7 +186,7 @@ extern "C" {
 
 const char* ditango_last_error(void) { return g_err.c_str(); }
 
-int32_t ditango_version(void) { return 3; }
+int32_t ditango_version(void) { return 4; }
 
 size_t ditango_states_bytes(const ditango_shape_t* shape, size_t* o_bytes, size_t* lse_bytes) {
   int32_t S = 0;
@@ -804,6 +806,31 @@ int ditango_group_compose(ditango_gstates_t* st, int32_t k, void* stream) {
   return ok();
 }
 
+int ditango_group_fit(ditango_gstates_t* st, size_t budget_bytes, int32_t k, void* stream, int32_t* merges_out) {
+  if (merges_out) *merges_out = 0;
+  int ns = 0;
+  int rc = check_gstates(st, &ns);
+  if (rc) return rc;
+  if (k < 2) return fail(DITANGO_EINVAL, "merge factor k=%d must be >= 2", k);
+  const size_t slot_bytes = ditango_gstates_slot_bytes(&st->shape, nullptr, nullptr);
+  const int P = st->shape.P;
+  // Merges needed: group sizes g, k g, k^2 g, ... until the slot memory fits.
+  // The coarsest grouping (one group of all P partitions) has 2 slots.
+  int n = 0;
+  for (int64_t g = st->g;; g *= k, ++n) {
+    const int64_t slots = 1 + (P + g - 1) / g;
+    if (static_cast<size_t>(slots) * slot_bytes <= budget_bytes) break;
+    if (g >= P)
+      return fail(DITANGO_EINVAL, "the state cache needs %zu bytes at least (2 slots of %zu), above the budget of %zu",
+                  2 * slot_bytes, slot_bytes, budget_bytes);
+  }
+  for (int i = 0; i < n; ++i) {
+    if ((rc = ditango_group_compose(st, k, stream))) return rc;
+    if (merges_out) *merges_out = i + 1;
+  }
+  return ok();
+}
+
 int ditango_group_reset(ditango_gstates_t* st, float* const* O, float* const* LSE) {
   if (!st) return fail(DITANGO_EINVAL, "states is NULL");
   int32_t S = 0;
@@ -846,55 +873,52 @@ int ditango_group_mask_build(int32_t P, int32_t g, int32_t n, uint8_t* mask_out)
   return ok();
 }
 
-int ditango_mask_build(int32_t policy, int32_t P, int32_t n, uint64_t seed, uint8_t* mask_out) {
+int ditango_mask_build(int32_t policy, int32_t P, int32_t n, uint64_t seed, int32_t step, uint8_t* mask_out) {
   if (!mask_out) return fail(DITANGO_EINVAL, "mask_out is NULL");
   if (P < 1 || P > DITANGO_MAX_P) return fail(DITANGO_EINVAL, "P=%d outside 1..%d", P, DITANGO_MAX_P);
-  std::memset(mask_out, 0, static_cast<size_t>(P) * P);
-  switch (policy) {
-    case DITANGO_MASK_ALL:
-      std::memset(mask_out, 1, static_cast<size_t>(P) * P);
-      return ok();
-    case DITANGO_MASK_NONE:
-      return ok();
-    case DITANGO_MASK_RADIUS:
-      if (n < 0) return fail(DITANGO_EINVAL, "radius n=%d must be >= 0", n);
-      for (int q = 0; q < P; ++q)
-        for (int k = 0; k < P; ++k) mask_out[q * P + k] = (q - k <= n && k - q <= n) ? 1 : 0;
-      return ok();
-    case DITANGO_MASK_NEAREST:
-      if (n < 1 || n > P) return fail(DITANGO_EINVAL, "nearest n=%d outside 1..P", n);
-      for (int q = 0; q < P; ++q) {
-        // walk outward from q: distance 0, then for each distance the lower
-        // index first (ties go to the lower k)
-        int taken = 0;
-        for (int dist = 0; taken < n; ++dist) {
-          if (q - dist >= 0 && taken < n) { mask_out[q * P + (q - dist)] = 1; ++taken; }
-          if (dist > 0 && q + dist < P && taken < n) { mask_out[q * P + (q + dist)] = 1; ++taken; }
-        }
-      }
-      return ok();
-    case DITANGO_MASK_RANDOM: {
-      if (n < 1 || n > P) return fail(DITANGO_EINVAL, "random n=%d outside 1..P", n);
-      SplitMix64 rng{seed};
-      std::vector<int> c;
-      for (int q = 0; q < P; ++q) {
-        c.clear();
-        for (int k = 0; k < P; ++k)
-          if (k != q) c.push_back(k);
-        for (int i = 0; i < n - 1; ++i) {
-          const int j = i + static_cast<int>(rng.next() % static_cast<uint64_t>(P - 1 - i));
-          const int t = c[i];
-          c[i] = c[j];
-          c[j] = t;
-        }
-        mask_out[q * P + q] = 1;
-        for (int i = 0; i < n - 1; ++i) mask_out[q * P + c[i]] = 1;
-      }
-      return ok();
-    }
-    default:
-      return fail(DITANGO_EINVAL, "unknown mask policy %d", policy);
+  if (step < 0) return fail(DITANGO_EINVAL, "step=%d must be >= 0", step);
+  if (policy < DITANGO_MASK_ALL || policy > DITANGO_MASK_RANDOM)
+    return fail(DITANGO_EINVAL, "unknown mask policy %d", policy);
+  // The count n matters from step 1 on (step 0 is the all-fresh anchor).
+  if (step > 0) {
+    if (policy == DITANGO_MASK_RADIUS && n < 0) return fail(DITANGO_EINVAL, "radius n=%d must be >= 0", n);
+    if ((policy == DITANGO_MASK_NEAREST || policy == DITANGO_MASK_RANDOM) && (n < 1 || n > P))
+      return fail(DITANGO_EINVAL, "%s n=%d outside 1..P", policy == DITANGO_MASK_NEAREST ? "nearest" : "random", n);
   }
+  // Step 0 is an anchor step: every pair computes.
+  const int pol = step == 0 ? DITANGO_MASK_ALL : policy;
+  std::memset(mask_out, pol == DITANGO_MASK_ALL ? 1 : 0, static_cast<size_t>(P) * P);
+  if (pol == DITANGO_MASK_RADIUS) {
+    for (int q = 0; q < P; ++q)
+      for (int k = 0; k < P; ++k) mask_out[q * P + k] = (q - k <= n && k - q <= n) ? 1 : 0;
+  } else if (pol == DITANGO_MASK_NEAREST) {
+    for (int q = 0; q < P; ++q) {
+      // walk outward from q: distance 0, then for each distance the lower
+      // index first (ties go to the lower k)
+      int taken = 0;
+      for (int dist = 0; taken < n; ++dist) {
+        if (q - dist >= 0 && taken < n) { mask_out[q * P + (q - dist)] = 1; ++taken; }
+        if (dist > 0 && q + dist < P && taken < n) { mask_out[q * P + (q + dist)] = 1; ++taken; }
+      }
+    }
+  } else if (pol == DITANGO_MASK_RANDOM) {
+    SplitMix64 rng{seed + static_cast<uint64_t>(step)};
+    std::vector<int> c;
+    for (int q = 0; q < P; ++q) {
+      c.clear();
+      for (int k = 0; k < P; ++k)
+        if (k != q) c.push_back(k);
+      for (int i = 0; i < n - 1; ++i) {
+        const int j = i + static_cast<int>(rng.next() % static_cast<uint64_t>(P - 1 - i));
+        const int t = c[i];
+        c[i] = c[j];
+        c[j] = t;
+      }
+      mask_out[q * P + q] = 1;
+      for (int i = 0; i < n - 1; ++i) mask_out[q * P + c[i]] = 1;
+    }
+  }
+  return ok();
 }
 
 }  // extern "C"

@@ -53,7 +53,7 @@ extern "C" {
  * every partition must be non-empty (P * ceil(N/P) - N < ceil(N/P)). */
 typedef struct {
   int32_t H;      /* attention heads                                   */
-  int32_t N;      /* tokens in the flattened sequence; N * d <= 2^30   */
+  int32_t N;      /* tokens in the flattened sequence; N * d < 2^30    */
   int32_t d;      /* head dimension                                    */
   int32_t P;      /* partitions                                        */
   float   scale;  /* score scale applied to q.k, normally 1/sqrt(d)    */
@@ -124,24 +124,34 @@ int ditango_state_merge(const ditango_states_t* st, float* O, float* LSE, void* 
 int ditango_step(const void* Q, const void* K, const void* V, const uint8_t* mask, int32_t step,
                  ditango_states_t* st, float* O, float* LSE, uint8_t* reused_out, void* stream);
 
-/* Selection-mask builder for the locality policies used by the workloads
- * (state-selection section; locality of Fig. 5a).  Writes uint8 [P][P]:
- *   DITANGO_MASK_ALL      every pair fresh (an anchor step)
+/* Selection mask of denoising step `step` under one of the locality
+ * policies the workloads use (DiTango page, state-selection section: COMPUTE
+ * or REUSE per unit and step; the near partitions matter most, Fig. 5a;
+ * anchor-step section: an anchor step computes every unit).  Writes uint8
+ * [P][P] (row q = query partition, column k = KV partition, 1 = COMPUTE):
+ *   step 0                every pair fresh whatever the policy (the anchor
+ *                         step that fills the cache)
+ *   step >= 1:
+ *   DITANGO_MASK_ALL      every pair fresh
  *   DITANGO_MASK_NONE     every pair reused
  *   DITANGO_MASK_RADIUS   fresh iff |q - k| <= n
  *   DITANGO_MASK_NEAREST  per row q, the n partitions k with the smallest
  *                         |q - k|, ties to the lower k
  *   DITANGO_MASK_RANDOM   per row q, q plus n-1 distinct others drawn with
- *                         SplitMix64(seed): rows in order, candidates
- *                         c = [k != q] ascending, for i < n-1 swap c[i] with
- *                         c[i + next() % (P-1-i)], take c[0..n-2]
- * Errors: EINVAL (bad policy, P outside 1..32, n outside its range). */
+ *                         SplitMix64 seeded with seed + step: rows in order,
+ *                         candidates c = [k != q] ascending, for i < n-1 swap
+ *                         c[i] with c[i + next() % (P-1-i)], take c[0..n-2]
+ * `seed` is the workload's seed base (a workload with id c uses 1000 c), so a
+ * step's random mask depends on (workload, step) only.  The mask is owned by
+ * the caller.  Errors: EINVAL (NULL mask_out, bad policy, P outside 1..32,
+ * step < 0, or from step 1 on n outside its range for the policy). */
 #define DITANGO_MASK_ALL     0
 #define DITANGO_MASK_NONE    1
 #define DITANGO_MASK_RADIUS  2
 #define DITANGO_MASK_NEAREST 3
 #define DITANGO_MASK_RANDOM  4
-int ditango_mask_build(int32_t policy, int32_t P, int32_t n, uint64_t seed, uint8_t* mask_out);
+int ditango_mask_build(int32_t policy, int32_t P, int32_t n, uint64_t seed, int32_t step,
+                       uint8_t* mask_out);
 
 /* Window attention with residual sharing at partition granularity (the
  * DiTFastAttn page: window attention plus a cached full-minus-window
@@ -243,6 +253,19 @@ int ditango_group_merge(const ditango_gstates_t* st, float* O, float* LSE, void*
  * work), EHIP (a launch failed part-way: the slot contents are then
  * undefined and the caller should reset and recompute at an anchor step). */
 int ditango_group_compose(ditango_gstates_t* st, int32_t k, void* stream);
+
+/* The memory trigger of Dynamic Group State Compose (DiTango page, dynamic
+ * group state compose: when the cache's memory nears its limit, groups are
+ * merged, repeatedly if need be, until an anchor step restores g0).  The
+ * cache's device memory is (live slot count) x ditango_gstates_slot_bytes;
+ * while it exceeds budget_bytes, groups are merged k at a time, each merge
+ * as ditango_group_compose (k >= 2), enqueued on `stream`.  *merges_out (may
+ * be NULL) receives the number of merges done, 0 when the cache already
+ * fits.  The released slot buffers are the caller's to free once the stream
+ * has passed the call.  Errors: EINVAL before any merge (bad k, or even one
+ * group of all P partitions -- 2 slots -- exceeds the budget), ENOCACHE
+ * (a non-empty slot holds no state), EHIP as ditango_group_compose. */
+int ditango_group_fit(ditango_gstates_t* st, size_t budget_bytes, int32_t k, void* stream, int32_t* merges_out);
 
 /* Return to the original group size g0 before an anchor step: binds
  * ditango_group_slots(P, g0) slot buffers (kept ones may be passed again)

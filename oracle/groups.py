@@ -48,6 +48,30 @@ def n_slots(P: int, g: int) -> int:
     return 1 + n_groups(P, g)
 
 
+def slot_bytes(H: int, N: int, P: int, d: int) -> int:
+    """Device bytes of one slot of the grouped cache: fp32 OUT [H][P][S][d]
+    plus LSE [H][P][S] (the layout the library allocates per slot)."""
+    S = -(-N // P)
+    return 4 * H * P * S * (d + 1)
+
+
+def merges_to_fit(P: int, g: int, k: int, bytes_per_slot: int, budget: int) -> int:
+    """Dynamic Group State Compose, memory trigger (DiTango page, dynamic
+    group state compose: groups are merged, repeatedly if need be, once the
+    cache's memory nears its limit): the number of merges by k after which
+    the cache, n_slots(P, g) slots of bytes_per_slot each, fits the budget.
+    Raises ValueError when one group of all P partitions does not fit."""
+    if k < 2:
+        raise ValueError("merge factor must be >= 2")
+    n = 0
+    while n_slots(P, g) * bytes_per_slot > budget:
+        if g >= P:
+            raise ValueError("the cache does not fit the budget even as one group")
+        g *= k
+        n += 1
+    return n
+
+
 def slot_members(P: int, g: int, q: int, s: int) -> list[int]:
     """KV partitions whose composed state slot s of query partition q holds."""
     if s == 0:
@@ -167,6 +191,14 @@ class GroupedStateReuseOracle:
             lses[h] = np.concatenate(l_parts, axis=0)
         self.tc[dec == 1] = t
         return {"O": outs, "LSE": lses, "fresh": fresh, "computed": dec, "tc": self.tc.copy()}
+
+    def fit_memory(self, budget: int, k: int, bytes_per_slot: int) -> int:
+        """Merge groups k at a time while the cache exceeds the budget;
+        returns the number of merges (Dynamic Group State Compose)."""
+        n = merges_to_fit(self.P, self.g, k, bytes_per_slot, budget)
+        for _ in range(n):
+            self.compose_groups(k)
+        return n
 
     def compose_groups(self, k: int):
         """Dynamic Group State Compose: group size g -> k g, composing cached states."""

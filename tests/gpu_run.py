@@ -51,10 +51,12 @@ def run_steps(w, masks=None, steps=None, on_step=None, label=""):
     return cache
 
 
-def run_group_steps(w, g, masks=None, steps=None, compose_at=None, on_step=None, label=""):
+def run_group_steps(w, g, masks=None, steps=None, compose_at=None, on_step=None, label="", budget_at=None):
     """Run the grouped-cache path of the library over the steps of workload w.
 
     compose_at: optional {t: k}: merge groups by k right before step t.
+    budget_at: optional {t: bytes}: right before step t, merge groups by 2
+    while the cache exceeds that many bytes (the memory trigger).
     on_step(t, mask, computed, cache, O, LSE) is called after each step.
     """
     import torch
@@ -74,6 +76,10 @@ def run_group_steps(w, g, masks=None, steps=None, compose_at=None, on_step=None,
         if compose_at and t in compose_at:
             cache.compose(compose_at[t])
             log(f"  [{label or w.name}] before step {t}: groups merged to g={cache.g}, {cache.n_slots} slots")
+        if budget_at and t in budget_at:
+            n = cache.fit(budget_at[t], 2)
+            log(f"  [{label or w.name}] before step {t}: budget {budget_at[t]} B, {n} merge(s), g={cache.g}, "
+                f"{cache.device_bytes} B")
         mask = lib.workload_mask(w, t) if masks is None or t not in masks else np.asarray(masks[t], np.uint8)
         lib.ditango_group_attn_partial(Q, K, V, mask, cache)
         computed = lib.ditango_group_cache_update(cache, mask, t)

@@ -51,7 +51,7 @@ int main() {
   // masks
   for (int it = 0; it < 20000; ++it) {
     int pol = ri(-1, 5), P = ri(-1, 34), n = ri(-2, 36);
-    oks += ditango_mask_build(pol, P, n, rng(), m.data()) == 0; ++calls;
+    oks += ditango_mask_build(pol, P, n, rng(), static_cast<int32_t>(rng() % 12) - 1, m.data()) == 0; ++calls;
     oks += ditango_group_mask_build(P, ri(-1, 36), n, m.data()) == 0; ++calls;
     ditango_group_slots(P, ri(-2, 40));
   }
@@ -83,6 +83,8 @@ int main() {
   const int dims[] = {64, 72, 128, 65};
   for (int it = 0; it < 3000; ++it) {
     ditango_shape_t sh = {ri(0, 3), ri(0, 3000), dims[ri(0, 3)], ri(0, 33), ri(0, 20) ? 0.125f : wild()};
+    // now and then a sequence at the 32-bit K/V offset limit (N * d around 2^30)
+    if (ri(0, 9) == 0) sh.N = (1 << 30) / sh.d + ri(-2, 1);
     ditango_states_t st;
     std::memset(&st, 0, sizeof st);
     std::vector<int32_t> tc(40 * 40, 7);
@@ -138,6 +140,12 @@ int main() {
       ++calls; oks += ditango_group_cache_update(&st, m.data(), t, comp.data()) == 0;
       ++calls; oks += ditango_group_merge(&st, fake(0x600000), fake(0x700000), nullptr) == 0;
       if (ri(0, 3) == 0) { ++calls; oks += ditango_group_compose(&st, ri(0, 5), nullptr) == 0; }
+      if (ri(0, 3) == 0) {
+        const size_t sb = ditango_gstates_slot_bytes(&st.shape, nullptr, nullptr);
+        int32_t merges = -1;
+        ++calls; oks += ditango_group_fit(&st, sb * static_cast<size_t>(ri(0, 34)), ri(0, 5), nullptr,
+                                          ri(0, 5) ? &merges : nullptr) == 0;
+      }
       if (ri(0, 7) == 0) { ++calls; oks += ditango_group_reset(&st, O.data(), L.data()) == 0; }
     }
   }

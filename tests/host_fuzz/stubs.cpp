@@ -6,7 +6,13 @@
 #include "internal.h"
 #define REQUIRE(c) do { if (!(c)) { fprintf(stderr, "contract violated: %s (%s:%d)\n", #c, __FILE__, __LINE__); abort(); } } while (0)
 namespace ditango {
-int partial_rows_per_block(int d, int S) { (void)d; return S > 300 ? 256 : 128; }
+// same rule as the kernels': 128 rows for d = 64 and 72; d = 128 picks 256
+// or 128 by the waste of the last query tile
+int partial_rows_per_block(int d, int S) {
+  if (d != 128) return 128;
+  const long ww = (S + 255) / 256 * 256L - S, wn = (S + 127) / 128 * 128L - S;
+  return wn * 10 + S < ww * 10 ? 128 : 256;
+}
 long g_partial = 0, g_merge = 0, g_stats = 0, g_drift = 0;
 // the last per-pair work list, for the driver to compare with its mask
 int g_last_n = -1, g_last_blocks = -1, g_last_qtiles = -1;
@@ -14,7 +20,10 @@ uint16_t g_last_pairs[DITANGO_MAX_P * DITANGO_MAX_P];
 hipError_t launch_partial(PartialParams& p, int rows, hipStream_t) {
   REQUIRE(p.n_pairs >= 1 && p.n_pairs <= DITANGO_MAX_P * DITANGO_MAX_P);
   REQUIRE(p.P >= 1 && p.P <= DITANGO_MAX_P && p.S >= 1 && p.N >= p.P);
+  REQUIRE(rows == (p.d == 128 ? rows : 128) && (rows == 128 || rows == 256));
   REQUIRE(p.q_tiles == (p.S + rows - 1) / rows);
+  // K/V byte offsets of one head fit the 32-bit buffer descriptors
+  REQUIRE(static_cast<long long>(p.N) * p.d * 2 < (1LL << 31));
   REQUIRE(static_cast<long long>(p.n_blocks) == static_cast<long long>(p.H) * p.n_pairs * p.q_tiles);
   for (int i = 0; i < p.n_pairs; ++i) {
     if (!p.grouped) REQUIRE(p.pairs[i] < p.P * p.P);

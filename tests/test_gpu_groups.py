@@ -21,8 +21,9 @@ from test_gpu_parity import _sample_rows, _scaled, check_state
 pytestmark = pytest.mark.gpu
 
 
-def _oracle_steps(w, g, masks, steps, compose_at, rows=None, heads=None):
+def _oracle_steps(w, g, masks, steps, compose_at, rows=None, heads=None, budget_at=None):
     from synth import InputStream, bf16_bits_to_f64
+    from oracle.groups import slot_bytes
     heads = list(range(w.H)) if heads is None else heads
     orc = GroupedStateReuseOracle(w.N, w.P, w.d, g, rows=rows)
     stream = InputStream(w, heads)
@@ -31,6 +32,8 @@ def _oracle_steps(w, g, masks, steps, compose_at, rows=None, heads=None):
         qb, kb, vb = stream.next()
         if compose_at and t in compose_at:
             orc.compose_groups(compose_at[t])
+        if budget_at and t in budget_at:
+            orc.fit_memory(budget_at[t], 2, slot_bytes(w.H, w.N, w.P, w.d))
         m = masks[t] if masks and t in masks else step_mask(w, t)
         x = {h: (bf16_bits_to_f64(qb[i]), bf16_bits_to_f64(kb[i]), bf16_bits_to_f64(vb[i]))
              for i, h in enumerate(heads)}
@@ -38,9 +41,9 @@ def _oracle_steps(w, g, masks, steps, compose_at, rows=None, heads=None):
     return out, orc
 
 
-def _compare(w, g, masks=None, steps=None, compose_at=None, rows=None, heads=None, label=None):
+def _compare(w, g, masks=None, steps=None, compose_at=None, rows=None, heads=None, label=None, budget_at=None):
     steps = w.steps if steps is None else steps
-    ref, orc = _oracle_steps(w, g, masks, steps, compose_at, rows, heads)
+    ref, orc = _oracle_steps(w, g, masks, steps, compose_at, rows, heads, budget_at)
     heads = list(range(w.H)) if heads is None else heads
     rows_all = orc.rows
     import torch
@@ -79,7 +82,8 @@ def _compare(w, g, masks=None, steps=None, compose_at=None, rows=None, heads=Non
             check_state(Oc[hi, rows_all], Lc[hi, rows_all], res["O"][h], res["LSE"][h],
                         f"{label} step {t} head {h} merged")
 
-    run_group_steps(w, g, masks=masks, steps=steps, compose_at=compose_at, on_step=check, label=label)
+    run_group_steps(w, g, masks=masks, steps=steps, compose_at=compose_at, on_step=check, label=label,
+                    budget_at=budget_at)
     log(f"  {label}: worst slot state OUT max {worst[0]:.2e}, mean {worst[1]:.2e}, LSE {worst[2]:.2e}")
 
 
@@ -106,6 +110,19 @@ def test_group_merges_match_oracle():
     masks = {0: all_fresh(8), 1: (rng.random((8, 8)) < 0.4).astype(np.uint8), 2: all_reuse(8),
              3: all_reuse(8), 4: (rng.random((8, 8)) < 0.3).astype(np.uint8), 5: all_reuse(8)}
     _compare(w, 1, masks=masks, compose_at={2: 2, 4: 2}, label="merges")
+
+
+def test_memory_budget_merges_match_oracle():
+    """The memory trigger: a budget that lets the cache start at g = 1 (9
+    slots), then one that forces a merge to g = 2 (5 slots), then one that
+    forces two more (g = 8, 2 slots), with reuse across the merges."""
+    from oracle.groups import slot_bytes
+    w = synth.get("video_100").scaled(name="budget_p8", F=3, Hh=13, W=21, H=2, P=8, steps=6)
+    sb = slot_bytes(w.H, w.N, w.P, w.d)
+    rng = np.random.default_rng(5)
+    masks = {0: all_fresh(8), 1: (rng.random((8, 8)) < 0.4).astype(np.uint8), 2: all_reuse(8),
+             3: (rng.random((8, 8)) < 0.3).astype(np.uint8), 4: all_reuse(8), 5: all_reuse(8)}
+    _compare(w, 1, masks=masks, budget_at={0: 9 * sb, 2: 5 * sb, 4: 2 * sb}, label="budget")
 
 
 def test_group_aligned_masks_match_oracle():

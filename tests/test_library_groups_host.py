@@ -152,3 +152,20 @@ def test_group_mask_builder_rejects(args):
     with pytest.raises(lib.DitangoError) as e:
         lib.ditango_group_mask_build(*args)
     assert e.value.code == lib.DITANGO_EINVAL
+
+
+def test_memory_trigger_host_checks():
+    """ditango_group_fit: nothing to do when the cache fits, EINVAL before
+    any work when not even one group fits or k < 2, ENOCACHE when a merge is
+    needed over empty slots (all before any launch, so no GPU is used)."""
+    f = _FakeG(P=4, g=2)                       # 1 + 2 slots
+    sb = binding.lib.ditango_gstates_slot_bytes(ctypes.byref(f.st.shape), None, None)
+    n = ctypes.c_int32(-1)
+    fit = binding.lib.ditango_group_fit
+    assert fit(ctypes.byref(f.st), 3 * sb, 2, None, ctypes.byref(n)) == 0 and n.value == 0 and f.st.g == 2
+    assert fit(ctypes.byref(f.st), 2 * sb - 1, 2, None, ctypes.byref(n)) == lib.DITANGO_EINVAL and n.value == 0
+    assert "budget" in binding.lib.ditango_last_error().decode()
+    assert fit(ctypes.byref(f.st), 3 * sb, 1, None, ctypes.byref(n)) == lib.DITANGO_EINVAL
+    assert fit(ctypes.byref(f.st), 2 * sb, 2, None, ctypes.byref(n)) == lib.DITANGO_ENOCACHE and n.value == 0
+    assert f.st.g == 2
+    assert fit(ctypes.byref(f.st), 3 * sb, 2, None, None) == 0          # merges_out may be NULL

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_struct_layout():
-    assert lib.ditango_version() == 3
+    assert lib.ditango_version() == 4
     assert ctypes.sizeof(binding.ditango_shape_t) == 20
     assert binding.ditango_states_t.O.offset == 24 and ctypes.sizeof(binding.ditango_states_t) == 48
 
@@ -64,7 +64,7 @@ def test_mask_builder_policies_sweep():
         for n in range(1, P + 1):
             assert np.array_equal(lib.ditango_mask_build("nearest", P, n), nearest_mask(P, n))
             for seed in (0, 1, 12345, 2**63 + 7):
-                assert np.array_equal(lib.ditango_mask_build("random", P, n, seed), random_mask(P, n, seed))
+                assert np.array_equal(lib.ditango_mask_build("random", P, n, seed, 1), random_mask(P, n, seed + 1))
         assert lib.ditango_mask_build("all", P).sum() == P * P
         assert lib.ditango_mask_build("none", P).sum() == 0
 
@@ -77,9 +77,21 @@ def test_mask_builder_rejects(args):
     assert e.value.code == lib.DITANGO_EINVAL
 
 
+def test_mask_builder_step0_is_anchor_for_every_policy():
+    # step 0 is all fresh whatever the policy and its count; the seed is
+    # seed + step from step 1 on
+    for pol, n in (("radius", 0), ("nearest", 9), ("random", 0), ("none", 0), ("all", 0)):
+        assert lib.ditango_mask_build(pol, 8, n, 5, 0).sum() == 64
+    assert np.array_equal(lib.ditango_mask_build("random", 8, 3, 1000, 4), random_mask(8, 3, 1004))
+    with pytest.raises(lib.DitangoError):
+        lib.ditango_mask_build("nearest", 8, 2, 0, -1)
+    with pytest.raises(lib.DitangoError):
+        lib.ditango_mask_build(9, 8, 2, 0, 0)
+
+
 @pytest.mark.parametrize("H,N,d,P", [(1, 10, 96, 2), (1, 10, 64, 0), (1, 10, 64, 33), (0, 10, 64, 2),
-                                     (1, 3, 64, 4), (1, 10, 64, 6), (1, 2**30 // 128 + 1, 128, 8),
-                                     (1, 2**30 // 72 + 1, 72, 8)])
+                                     (1, 3, 64, 4), (1, 10, 64, 6), (1, 2**30 // 128, 128, 8),
+                                     (1, 2**30 // 64, 64, 8), (1, 2**30 // 72 + 1, 72, 8)])
 def test_shape_rejected(H, N, d, P):
     ob = ctypes.c_size_t(0)
     assert binding.lib.ditango_states_bytes(ctypes.byref(lib.make_shape(H, N, d, P)), ctypes.byref(ob), None) == 0
@@ -87,10 +99,13 @@ def test_shape_rejected(H, N, d, P):
 
 
 def test_shape_at_the_size_limit_accepted():
-    # K/V of one head are addressed with 32-bit byte offsets: N * d <= 2^30
+    # K/V of one head are addressed with 32-bit byte offsets: N * d < 2^30
+    # (N * d = 2^30 exactly is rejected above)
     ob = ctypes.c_size_t(0)
-    assert binding.lib.ditango_states_bytes(ctypes.byref(lib.make_shape(1, 2**30 // 128, 128, 8)),
-                                            ctypes.byref(ob), None) > 0
+    for N, d in ((2**30 // 128 - 1, 128), (2**30 // 64 - 1, 64), (2**30 // 72, 72)):
+        assert N * d < 2**30
+        assert binding.lib.ditango_states_bytes(ctypes.byref(lib.make_shape(1, N, d, 8)),
+                                                ctypes.byref(ob), None) > 0
 
 
 class _FakeStates:

@@ -237,3 +237,47 @@ def test_nearest_groups_mask_is_group_aligned(P, g, n):
             chosen += vals == {1}
         live = sum(1 for s in range(1, n_slots(P, g)) if slot_members(P, g, q, s))
         assert chosen == min(n, live)
+
+
+def test_memory_trigger_merge_counts():
+    """Merges by k needed to fit a budget: the cache holds 1 + ceil(P / g)
+    slots, so for P = 32 and g = 1, 2, 4, 8, 16, 32 it holds 33, 17, 9, 5,
+    3, 2 slots (counted by hand)."""
+    from oracle.groups import merges_to_fit, n_slots
+    assert [n_slots(32, g) for g in (1, 2, 4, 8, 16, 32)] == [33, 17, 9, 5, 3, 2]
+    B = 1000
+    want = {33: 0, 32: 1, 17: 1, 16: 2, 9: 2, 8: 3, 5: 3, 4: 4, 3: 4, 2: 5}
+    for slots, n in want.items():
+        assert merges_to_fit(32, 1, 2, B, slots * B) == n, slots
+    assert merges_to_fit(32, 1, 4, B, 9 * B) == 1          # g = 4 in one merge by 4
+    assert merges_to_fit(32, 1, 4, B, 8 * B) == 2          # then g = 16: 3 slots
+    assert merges_to_fit(8, 3, 2, B, 3 * B) == 1           # g = 3 -> 6: 1 + 2 slots
+    with pytest.raises(ValueError):
+        merges_to_fit(32, 1, 2, B, 2 * B - 1)              # not even one group fits
+    from oracle.groups import slot_bytes
+    assert slot_bytes(2, 10, 4, 64) == 4 * 2 * 4 * 3 * 65  # S = ceil(10 / 4) = 3
+
+
+def test_memory_trigger_merges_like_explicit_compose():
+    """fit_memory performs exactly the merges it counts: the same cache as
+    explicit compose_groups calls, and an all-reuse step after it returns
+    the output of the step before (merging only recomposes cached states)."""
+    from oracle.groups import GroupedStateReuseOracle, merges_to_fit
+    from oracle.masks import all_fresh, all_reuse
+    rng = np.random.default_rng(3)
+    N, P, d = 60, 8, 8
+    x = {0: tuple(rng.standard_normal((N, d)) for _ in range(3))}
+    a = GroupedStateReuseOracle(N, P, d, 1)
+    b = GroupedStateReuseOracle(N, P, d, 1)
+    r0 = a.step(0, all_fresh(P), x)
+    b.step(0, all_fresh(P), x)
+    assert merges_to_fit(P, 1, 2, 10, 30) == 2              # 9 slots -> 5 -> 3
+    assert a.fit_memory(30, 2, 10) == 2 and a.g == 4
+    b.compose_groups(2)
+    b.compose_groups(2)
+    assert b.g == 4 and np.array_equal(a.tc, b.tc)
+    for key in b.cache:
+        assert np.array_equal(a.cache[key][0], b.cache[key][0])
+    r1 = a.step(1, all_reuse(P), x)
+    assert np.abs(r1["O"][0] - r0["O"][0]).max() < 1e-12
+    assert a.fit_memory(30, 2, 10) == 0                     # already fits
