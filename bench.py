@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "effective attention TFLOP/s and ms/denoise-step at given reuse ratio, 1 GPU"
-DEFAULT_WORKLOAD = "image"
+DEFAULT_WORKLOAD = "long"
 
 
 def parse():
@@ -42,8 +42,7 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     help="image | video_100 | video_50 | video_25 | long | stress | tiny")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the oracle sample (0: auto)")
-    ap.add_argument("--cpu-steps", type=int, default=0, help="timed steady-state steps of the oracle (0: auto)")
+    ap.add_argument("--cpu-steps", type=int, default=0, help="timed steady-state steps of the oracle sample (0: auto, about 12 s)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--group", type=int, default=0,
@@ -147,39 +146,106 @@ def host_cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(w, heads: int, steps: int):
-    """fp64 oracle on `steps` steady-state steps of `heads` heads (the anchor
-    step 0 runs untimed first)."""
-    from oracle.reuse import StateReuseOracle
-    from oracle.masks import step_mask
+BLAS_THREAD_VARS = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS")
+ORACLE_CORE_FLOPS = 1.5e10    # fp64 oracle FLOP/s per core with single-threaded BLAS (measured, conservative)
+MAX_ORACLE_WORKERS = 16       # the host share of one GPU
+
+
+def _oracle_worker(conn, wname: str, heads: list, stride: int) -> None:
+    """One oracle process: its heads, every `stride`-th query row, stepped by
+    the parent (inputs and mask prepared untimed, then the step on "go")."""
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    hs = list(range(heads))
-    stream = synth.InputStream(w, hs)
-    orc = StateReuseOracle(w.N, w.P, w.d)
-    timed = 0.0
-    n = 0
-    for t in range(1 + steps):
-        tt = 1 + (t - 1) % max(w.steps - 1, 1) if t else 0
+    from oracle.masks import step_mask
+    from oracle.reuse import StateReuseOracle
+    w = synth.get(wname)
+    rows = None if stride == 1 else np.arange(0, w.N, stride)
+    orc = StateReuseOracle(w.N, w.P, w.d, rows=rows)
+    stream = synth.InputStream(w, heads)
+    while True:
+        msg = conn.recv()
+        if msg is None:
+            break
+        t, tt = msg
         if t == 0 or tt > stream.t:
             qb, kb, vb = stream.next()
         inp = {h: (synth.bf16_bits_to_f64(qb[i]), synth.bf16_bits_to_f64(kb[i]), synth.bf16_bits_to_f64(vb[i]))
-               for i, h in enumerate(hs)}
-        t0 = time.perf_counter()
-        orc.step(t, step_mask(w, tt), inp)
-        if t:
-            timed += time.perf_counter() - t0
-            n += 1
-    dense = 4.0 * w.N * w.N * w.d * heads
-    return {"value": dense * n / timed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+               for i, h in enumerate(heads)}
+        mask = step_mask(w, tt)
+        conn.send("ready")
+        conn.recv()
+        orc.step(t, mask, inp)
+        conn.send("done")
+    conn.close()
+
+
+def cpu_baseline(w, fresh_per_step: float, target_s: float = 12.0, steps: int = 0):
+    """The fp64 oracle on the host cores, one process per core with
+    single-threaded BLAS, heads spread over the processes, stepped in lock-step
+    by this process: an untimed anchor step (all fresh), then timed
+    steady-state steps cycling over t = 1 .. steps-1.  The sample is one head
+    per process and every r-th query row (the oracle's own row subset, exact
+    for those rows), r chosen so that about `target_s` seconds are timed.
+    Run before the GPU is touched: the workers are started as fresh
+    interpreters."""
+    import multiprocessing as mp
+    cores = max(1, min(MAX_ORACLE_WORKERS, len(os.sched_getaffinity(0)), w.H))
+    heads = list(range(cores))
+    per_head_step = fresh_per_step / w.H                  # FLOP, all rows
+    n_steps = steps or 3
+    stride = max(1, int(np.ceil(per_head_step * n_steps / (ORACLE_CORE_FLOPS * target_s))))
+    if stride == 1 and not steps:
+        n_steps = int(min(12, max(3, target_s * ORACLE_CORE_FLOPS / max(per_head_step, 1.0))))
+    ctx = mp.get_context("spawn")
+    saved = {k: os.environ.get(k) for k in BLAS_THREAD_VARS}
+    for k in BLAS_THREAD_VARS:
+        os.environ[k] = "1"
+    procs, conns = [], []
+    try:
+        for h in heads:
+            a, b = ctx.Pipe()
+            p = ctx.Process(target=_oracle_worker, args=(b, w.name, [h], stride), daemon=True)
+            p.start()
+            procs.append(p)
+            conns.append(a)
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    timed, times = 0.0, []
+    try:
+        for t in range(1 + n_steps):
+            tt = 1 + (t - 1) % max(w.steps - 1, 1) if t else 0
+            for c in conns:
+                c.send((t, tt))
+            for c in conns:
+                assert c.recv() == "ready"
+            t0 = time.perf_counter()
+            for c in conns:
+                c.send("go")
+            for c in conns:
+                assert c.recv() == "done"
+            if t:
+                times.append(time.perf_counter() - t0)
+        timed = float(sum(times))
+    finally:
+        for c in conns:
+            try:
+                c.send(None)
+            except (BrokenPipeError, OSError):
+                pass
+        for p in procs:
+            p.join(timeout=30)
+    n_rows = len(range(0, w.N, stride))
+    dense = 4.0 * n_rows * w.N * w.d * len(heads)         # dense-equivalent FLOPs of one sample step
+    return {"value": dense * len(times) / timed / 1e12, "unit": "TFLOP/s", "cores": len(procs), "kind": "oracle",
             "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": host_cpu_model(),
-            "sample": f"{w.name}: {n} steady-state steps (after an untimed anchor step) for {heads} of {w.H} "
-                      f"heads, all {w.N} rows; fp64 NumPy oracle, {timed:.1f} s timed; effective TFLOP/s "
-                      f"counts 4*N^2*d per sampled head and step"}
+            "ms_per_sample_step": round(1e3 * timed / len(times), 1),
+            "sample": f"{w.name}: {len(procs)} processes (single-threaded BLAS), one head each ({len(heads)} of "
+                      f"{w.H} heads), {'every query row' if stride == 1 else f'every {stride}th query row'} ({n_rows} of {w.N}); an untimed all-fresh anchor "
+                      f"step, then {len(times)} steady-state steps timed in lock-step, {timed:.1f} s; fp64 NumPy "
+                      f"oracle; effective TFLOP/s counts 4*rows*N*d per sampled head and step"}
 
 
 def planner_run(args, w, lib, torch, dev):
@@ -250,6 +316,16 @@ def main():
         print("bench.py measures one GPU: the path runs all P partitions on one device and has no "
               "multi-GPU mode; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    # The oracle's timing runs first, before anything touches the GPU: its
+    # worker processes start as fresh interpreters.
+    cpu_rec = None
+    if not (args.no_cpu_baseline or args.group or args.window_residual or args.planner):
+        import synth
+        from oracle.masks import step_mask
+        w0 = synth.get(args.workload)
+        fresh0 = float(np.mean([fresh_flops(w0, step_mask(w0, t)) for t in (range(1, w0.steps) or [0])]))
+        cpu_rec = cpu_baseline(w0, fresh0, steps=args.cpu_steps)
 
     import torch
 
@@ -472,13 +548,8 @@ def main():
     out["anchor_step"] = anchor_rec
     if compose_rec is not None:
         out["group_compose"] = compose_rec
-    if not args.no_cpu_baseline and not g and not wr:
-        # about 12 s of timed oracle work: the oracle sustains roughly 7e10
-        # fp64 FLOP/s on the fresh pairs of a step (measured on the image sample)
-        steps = args.cpu_steps or 3
-        per_head_step = fresh / w.H / 7e10
-        heads = args.cpu_heads or int(max(1, min(w.H, round(12.0 / (steps * per_head_step)))))
-        out["cpu_baseline"] = cpu_baseline(w, heads, steps)
+    if cpu_rec is not None:
+        out["cpu_baseline"] = cpu_rec
     print(json.dumps(out), flush=True)
 
 
