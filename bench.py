@@ -147,7 +147,7 @@ def host_cpu_model() -> str:
 
 
 BLAS_THREAD_VARS = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS")
-ORACLE_CORE_FLOPS = 1.5e10    # fp64 oracle FLOP/s per core with single-threaded BLAS (measured, conservative)
+ORACLE_CORE_FLOPS = 4.5e10    # fp64 oracle FLOP/s per core, single-threaded BLAS (EPYC host of the GPU machine, long sample)
 MAX_ORACLE_WORKERS = 16       # the host share of one GPU
 
 
@@ -178,7 +178,7 @@ def _oracle_worker(conn, wname: str, heads: list, stride: int) -> None:
     conn.close()
 
 
-def cpu_baseline(w, fresh_per_step: float, target_s: float = 12.0, steps: int = 0):
+def cpu_baseline(w, fresh_per_step: float, target_s: float = 15.0, steps: int = 0):
     """The fp64 oracle on the host cores, one process per core with
     single-threaded BLAS, heads spread over the processes, stepped in lock-step
     by this process: an untimed anchor step (all fresh), then timed

@@ -245,3 +245,92 @@ def test_planned_steps_on_a_side_stream_match_the_current_stream():
     for t, (a, b) in enumerate(zip(*runs)):
         assert (a[0] == b[0]).all() and a[1] == b[1], f"step {t}: masks differ"
         assert np.array_equal(a[2], b[2]) and np.array_equal(a[3], b[3]), f"step {t}: outputs differ"
+
+
+def test_oracle_planner_on_oracle_statistics_picks_the_same_masks():
+    """End to end: the library's planner, fed the GPU's fp32 statistics,
+    against the oracle planner fed the oracle's own fp64 statistics (local
+    signatures of the step's fresh local states, importance from the merged
+    LSE, signatures of every pair before and after an anchor step), step by
+    step on the same inputs.  Every decision must agree -- the anchor flag,
+    and per (query partition, group) compute or reuse -- except a decision
+    within MARGIN (relative) of its threshold: a predicted group error within
+    MARGIN of eps, or the largest local drift within MARGIN of the anchor
+    bound, which fp32 statistics may flip legitimately (right after an
+    anchor the group whose error sets eps sits on it by construction).  The
+    oracle then follows the library's mask, so both runs keep the same
+    cache.  The exempt decisions are counted and bounded."""
+    import torch
+
+    import context_state_reuse_amd as lib
+    from oracle.planner import AnchorPlanner
+    from oracle.state import partial_state, partition_bounds
+    from synth import bf16_bits_to_f64
+
+    MARGIN = 0.05
+    w = _scaled("image", "image_plan_e2e", 1, 57, 97, 2, steps=12)
+    g, rho, dmax = 2, 0.6, 0.1
+    cache = lib.StateCache(w.H, w.N, w.d, w.P)
+    runner = lib.PlannedSteps(cache, lib.Planner(w.P, g, w.H, target_reuse=rho, drift_max=dmax))
+    orc = StateReuseOracle(w.N, w.P, w.d)
+    opl = AnchorPlanner(w.P, g, rho, dmax)
+    bounds = partition_bounds(w.N, w.P)
+    stream = synth.InputStream(w)
+
+    def cache_sigs():
+        sig = np.zeros((w.H, w.P, w.P, w.d))
+        for (h, q, k), (o, _) in orc.cache.items():
+            sig[h, q, k] = pair_signature(o)
+        return sig
+
+    compared, exempt, selective = 0, 0, 0
+    for t in range(w.steps):
+        qb, kb, vb = stream.next()
+        mask_l, anchor_l, _, _ = runner.step(t, to_device(qb), to_device(kb), to_device(vb))
+        torch.cuda.synchronize()
+        x = {h: (bf16_bits_to_f64(qb[h]), bf16_bits_to_f64(kb[h]), bf16_bits_to_f64(vb[h])) for h in range(w.H)}
+        sig_local = np.zeros((w.H, w.P, w.P, w.d))
+        if opl.n_anchors:
+            for h, (Qh, Kh, Vh) in x.items():
+                for q, (lo, hi) in enumerate(bounds):
+                    sig_local[h, q, q] = pair_signature(partial_state(Qh[lo:hi], Kh[lo:hi], Vh[lo:hi], orc.scale)[0])
+        mask_o, anchor_o = opl.plan(t, sig_local)
+        near_anchor = bool(opl.n_anchors and t >= opl.warmup
+                           and abs(float(np.max(opl.D)) - dmax) <= MARGIN * dmax)
+        if near_anchor:
+            exempt += 1
+        else:
+            compared += 1
+            assert anchor_o == anchor_l, f"step {t}: anchor {anchor_l} on the GPU, {anchor_o} in the oracle"
+        n_exempt_groups = 0
+        if not anchor_o and not anchor_l:
+            ase = opl.predicted_errors()
+            for q in range(w.P):
+                for j in range(opl.m):
+                    mem = group_members(w.P, g, q, j)
+                    if not mem:
+                        continue
+                    if abs(ase[q, j] - opl.eps) <= MARGIN * max(abs(opl.eps), 1e-12):
+                        n_exempt_groups += 1
+                        continue
+                    compared += 1
+                    assert mask_l[q, mem].tolist() == mask_o[q, mem].tolist(), \
+                        f"step {t}: group {j} of query partition {q}: GPU {mask_l[q, mem]}, oracle {mask_o[q, mem]}"
+            assert np.array_equal(np.diag(mask_l), np.ones(w.P, np.uint8))
+        exempt += n_exempt_groups
+        selective += not anchor_l
+        opl.anchor = bool(anchor_l)
+        mask = mask_l.copy()
+        sig_old = cache_sigs() if opl.anchor and opl.n_anchors else None
+        res = orc.step(t, mask, x)
+        W = np.zeros((w.H, w.P, w.P))
+        for h in range(w.H):
+            lm = [res["LSE"][h][lo:hi] for lo, hi in bounds]
+            W[h] = pair_weights([[orc.cache[(h, q, k)][1] for k in range(w.P)] for q in range(w.P)], lm)
+        opl.update(t, mask, W, cache_sigs(), sig_old)
+        log(f"  [{w.name}] step {t}: anchor {anchor_l}, fresh {int(mask_l.sum())}/{w.P * w.P}, "
+            f"{n_exempt_groups} group decision(s) near eps{', anchor decision near the bound' if near_anchor else ''}")
+    log(f"  [{w.name}] planner decisions: {compared} compared and equal, {exempt} near a threshold; "
+        f"{selective} selective steps")
+    assert selective >= 3, "the run must exercise selective steps"
+    assert exempt * 5 <= compared + exempt, f"{exempt} of {compared + exempt} decisions near a threshold"
