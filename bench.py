@@ -3,7 +3,10 @@
 One step = one denoising step of one attention layer through the whole hot
 path: build the step's selection mask, fresh partial attention for every
 COMPUTE pair (states written into the cache), cache metadata update, and the
-LSE-weighted merge of all P states per row.  Inputs of every step are
+LSE-weighted merge of all P states per row.  With the per-pair cache the
+partial attention and the merge run as one fused launch (ditango_step);
+--separate runs them as two launches (ditango_attn_partial, then
+ditango_state_merge) and times each.  Inputs of every step are
 resident in HBM before timing; the anchor step (all fresh) runs untimed first,
 then warm-up and timed steps cycle over the workload's steady-state steps
 t = 1 .. steps-1 with their masks.
@@ -52,6 +55,8 @@ def parse():
     ap.add_argument("--window-residual", action="store_true",
                     help="window attention with residual sharing: the anchor step computes every pair and caches "
                          "full-minus-window outputs; steady steps compute the window pairs (nearest partitions) only")
+    ap.add_argument("--separate", action="store_true",
+                    help="per-pair cache: partial attention and merge as two launches instead of the fused step")
     ap.add_argument("--planner", action="store_true",
                     help="anchor-guided planner picks each step's mask (per-pair cache); extra measurement")
     ap.add_argument("--plan-steps", type=int, default=16, help="denoising steps of the planned run")
@@ -147,7 +152,7 @@ def host_cpu_model() -> str:
 
 
 BLAS_THREAD_VARS = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS")
-ORACLE_CORE_FLOPS = 4.5e10    # fp64 oracle FLOP/s per core, single-threaded BLAS (EPYC host of the GPU machine, long sample)
+ORACLE_CORE_FLOPS = 4.5e10    # fp64 oracle FLOP/s per core, single-threaded BLAS (measured on a 16-core EPYC host, long sample)
 MAX_ORACLE_WORKERS = 16       # the host share of one GPU
 
 
@@ -380,11 +385,20 @@ def main():
         mask_of = lambda t: lib.workload_mask(w, t)
         mask_desc = f"{w.policy}-{w.n_fresh}"
 
+    fused = not (g or wr or args.separate)
+
     def step(t: int, events=None):
         mask = mask_of(t)
         Q, K, V = qkv[t]
         if events is not None:
             events[0].record()
+        if fused:
+            lib.ditango_step(Q, K, V, mask, step_no[0], cache, O, LSE)
+            if events is not None:
+                events[1].record()
+                events[2].record()
+            step_no[0] += 1
+            return mask
         if g:
             lib.ditango_group_attn_partial(Q, K, V, mask, cache)
         else:
@@ -430,9 +444,10 @@ def main():
     if g:
         computed_log.pop()
     torch.cuda.synchronize()
-    anchor_rec = {"ms": round(anchor_ev[0].elapsed_time(anchor_ev[2]), 4),
-                  "partial_ms": round(anchor_ev[0].elapsed_time(anchor_ev[1]), 4),
-                  "merge_ms": round(anchor_ev[1].elapsed_time(anchor_ev[2]), 4)}
+    anchor_rec = {"ms": round(anchor_ev[0].elapsed_time(anchor_ev[2]), 4)}
+    if not fused:
+        anchor_rec.update(partial_ms=round(anchor_ev[0].elapsed_time(anchor_ev[1]), 4),
+                          merge_ms=round(anchor_ev[1].elapsed_time(anchor_ev[2]), 4))
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     masks = []
@@ -467,7 +482,7 @@ def main():
             mb = float(4.0 * w.H * (lens * (wmask.sum(axis=1) * (w.d + 1) + w.d + (w.d + 1))).sum())
 
     partial_tflops = fresh / (t_partial * 1e-3) / 1e12
-    merge_gbs = mb / (t_merge * 1e-3) / 1e9
+    merge_gbs = mb / (t_merge * 1e-3) / 1e9 if t_merge > 0 else 0.0
     src = source_hash("partial.hip")
     cache_desc = (f"grouped, g={g}: {cache.n_slots} slots per query partition" if g
                   else "per pair: P slots per query partition")
@@ -495,7 +510,15 @@ def main():
                        "bytes": cbytes, "gbs": round(cbytes / (ms * 1e-3) / 1e9, 1),
                        "cache_bytes_before": before, "cache_bytes_after": cache.device_bytes}
 
-    if t_partial >= t_merge:
+    if fused:
+        roof = {"kernel": "step_kernel", "bound": "mfma", "achieved": round(partial_tflops, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(partial_tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": stored_traffic("step", w.name, src),
+                "avg_launch_ms": round(float(t_partial), 4),
+                "algorithmic_per_launch": f"{fresh:.4e} FLOP (4*len_q*len_k*d per fresh pair and head); the same "
+                                          f"launch moves {mb + sb:.4e} B of states (P*(d+1)*4 read + (d+1)*4 "
+                                          f"written per row and head, (d+1)*4 per fresh pair row stored)"}
+    elif t_partial >= t_merge:
         roof = {"kernel": "partial_kernel", "bound": "mfma", "achieved": round(partial_tflops, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(partial_tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": None if (g or wr) else stored_traffic("partial", w.name, src),
@@ -533,13 +556,19 @@ def main():
                    **({"computed_slots_per_step": float(np.mean([c.sum() for c in computed_log]))} if g else {}),
                    "parallelism": "none (all partitions on one GPU)"},
         "roofline": roof,
-        "kernels": {
+        "kernels": ({
+            "step": {"ms": round(float(t_partial), 4), "tflops": round(partial_tflops, 2),
+                     "mfma_frac": round(partial_tflops / PEAK_BF16_TFLOPS, 4), "fresh_flop": fresh,
+                     "state_bytes": float(mb + sb),
+                     "gbs": round((mb + sb) / (t_partial * 1e-3) / 1e9, 1),
+                     "hbm_frac": round((mb + sb) / (t_partial * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        } if fused else {
             "partial": {"ms": round(float(t_partial), 4), "tflops": round(partial_tflops, 2),
                         "mfma_frac": round(partial_tflops / PEAK_BF16_TFLOPS, 4), "fresh_flop": fresh,
                         "state_store_bytes": sb},
             "merge": {"ms": round(float(t_merge), 4), "gbs": round(merge_gbs, 1),
                       "hbm_frac": round(merge_gbs / PEAK_HBM_GBS, 4), "bytes": mb},
-        },
+        }),
     }
     # HBM fraction of the whole step: the merge's bytes plus the fresh states
     # stored, over the step time

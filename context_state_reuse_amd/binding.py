@@ -45,7 +45,8 @@ EXPORTED = ("ditango_states_bytes", "ditango_states_init", "ditango_attn_partial
             "ditango_group_slots", "ditango_gstates_slot_bytes", "ditango_gstates_init",
             "ditango_group_attn_partial", "ditango_group_cache_update", "ditango_group_merge",
             "ditango_group_compose", "ditango_group_fit", "ditango_group_reset", "ditango_group_mask_build",
-            "ditango_window_residual_merge", "ditango_step", "ditango_pair_stats", "ditango_sig_drift",
+            "ditango_window_residual_merge", "ditango_step", "ditango_attn_partial_merge",
+            "ditango_pair_stats", "ditango_sig_drift",
             "ditango_planner_init", "ditango_planner_plan", "ditango_planner_update")
 
 
@@ -134,6 +135,8 @@ def _load():
     lib.ditango_group_mask_build.argtypes = [i32, i32, i32, u8p]
     lib.ditango_step.restype = ctypes.c_int
     lib.ditango_step.argtypes = [vp, vp, vp, u8p, i32, ctypes.POINTER(ditango_states_t), vp, vp, u8p, vp]
+    lib.ditango_attn_partial_merge.restype = ctypes.c_int
+    lib.ditango_attn_partial_merge.argtypes = [vp, vp, vp, u8p, ctypes.POINTER(ditango_states_t), vp, vp, vp]
     lib.ditango_pair_stats.restype = ctypes.c_int
     lib.ditango_pair_stats.argtypes = [ctypes.POINTER(ditango_states_t), vp, u8p, vp, vp, vp]
     plp, f32p = ctypes.POINTER(ditango_planner_t), ctypes.POINTER(ctypes.c_float)
@@ -276,6 +279,24 @@ def ditango_step(Q, K, V, mask, step: int, cache: StateCache, O=None, LSE=None, 
                             ctypes.byref(cache.st), ctypes.c_void_p(O.data_ptr()), ctypes.c_void_p(LSE.data_ptr()),
                             _u8(reused), _stream(stream)))
     return O, LSE, reused
+
+
+def ditango_attn_partial_merge(Q, K, V, mask, cache: StateCache, O=None, LSE=None, stream=None):
+    """Fresh partial attention of the COMPUTE pairs and the composition of
+    every row in one launch (t_c unchanged).  Returns (O, LSE)."""
+    import torch
+    m = _mask(mask, cache.P)
+    if O is None:
+        O = torch.empty((cache.H, cache.N, cache.d), dtype=torch.float32, device=cache.O.device)
+    if LSE is None:
+        LSE = torch.empty((cache.H, cache.N), dtype=torch.float32, device=cache.O.device)
+    for t, shp, nm in ((O, (cache.H, cache.N, cache.d), "O"), (LSE, (cache.H, cache.N), "LSE")):
+        if not (t.is_cuda and t.dtype == torch.float32 and t.is_contiguous() and tuple(t.shape) == shp):
+            raise ValueError(f"{nm} must be a contiguous float32 device tensor of shape {shp}")
+    _check(lib.ditango_attn_partial_merge(_qkv(Q, cache, "Q"), _qkv(K, cache, "K"), _qkv(V, cache, "V"), _u8(m),
+                                          ctypes.byref(cache.st), ctypes.c_void_p(O.data_ptr()),
+                                          ctypes.c_void_p(LSE.data_ptr()), _stream(stream)))
+    return O, LSE
 
 
 def ditango_pair_stats(cache: StateCache, LSE, select, W=None, SIG=None, stream=None, want_w=True):

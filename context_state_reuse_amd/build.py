@@ -32,8 +32,11 @@ def _hipcc() -> str:
 
 
 def _flags() -> list[str]:
-    # -fno-honor-nans: the kernels never produce NaN, and without it every max
-    # of MFMA results is preceded by a NaN-quieting canonicalize.
+    # -fno-honor-nans: from finite inputs no kernel makes a NaN (masked keys
+    # score -FLT_MAX rather than -inf and every softmax row holds at least one
+    # key), so NaN handling is dead code; without the flag every max of MFMA
+    # results is preceded by a NaN-quieting canonicalize.  Inputs that hold
+    # NaN or infinity give unspecified outputs.
     # -amdgpu-mfma-vgpr-form: MFMA results land in VGPRs, where the softmax
     # reads them, instead of AGPRs that need copies.
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,

@@ -536,6 +536,60 @@ int ditango_planner_update(ditango_planner_t* pl, int32_t step, const uint8_t* m
   return ok();
 }
 
+// The fused launch of a step: checks, then one step_kernel launch (fresh
+// pairs per query-partition row, states stored, rows composed).
+static int launch_fused_step(const void* Q, const void* K, const void* V, const uint8_t* mask,
+                             const ditango_states_t* st, float* O, float* LSE, void* stream) {
+  const int P = st->shape.P;
+  ditango::StepParams sp;
+  std::memset(&sp, 0, sizeof sp);
+  for (int q = 0; q < P; ++q) {
+    int n = 0;
+    for (int k = 0; k < P; ++k)
+      if (mask[q * P + k]) sp.fresh[q][n++] = static_cast<uint8_t>(k);
+    sp.nf[q] = static_cast<uint8_t>(n);
+  }
+  sp.Q = static_cast<const __bf16*>(Q);
+  sp.K = static_cast<const __bf16*>(K);
+  sp.V = static_cast<const __bf16*>(V);
+  sp.O = st->O;
+  sp.LSE = st->LSE;
+  sp.Oout = O;
+  sp.LSEout = LSE;
+  sp.H = st->shape.H;
+  sp.N = st->shape.N;
+  sp.P = P;
+  sp.S = st->S;
+  sp.d = st->shape.d;
+  sp.scale_log2 = st->shape.scale * 1.4426950408889634f;
+  const int rows = ditango::partial_rows_per_block(sp.d, sp.S);
+  sp.q_tiles = (sp.S + rows - 1) / rows;
+  const int64_t blocks = static_cast<int64_t>(sp.H) * P * sp.q_tiles;
+  if (blocks > 0x7fffffff) return fail(DITANGO_EINVAL, "grid of %lld blocks is too large", (long long)blocks);
+  sp.n_blocks = static_cast<int32_t>(blocks);
+  hipError_t e = ditango::launch_step(sp, rows, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DITANGO_EHIP, "step kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int ditango_attn_partial_merge(const void* Q, const void* K, const void* V, const uint8_t* mask,
+                               ditango_states_t* st, float* O, float* LSE, void* stream) {
+  int rc = check_states(st);
+  if (rc) return rc;
+  const int P = st->shape.P;
+  if ((rc = check_mask(mask, P))) return rc;
+  if (!Q || !K || !V) return fail(DITANGO_EINVAL, "Q, K and V must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(Q) | reinterpret_cast<uintptr_t>(K) | reinterpret_cast<uintptr_t>(V)) & 15u)
+    return fail(DITANGO_EINVAL, "Q, K and V must be 16-byte aligned");
+  if (!O || !LSE) return fail(DITANGO_EINVAL, "O and LSE must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(O) | reinterpret_cast<uintptr_t>(LSE)) & 15u)
+    return fail(DITANGO_EINVAL, "O and LSE must be 16-byte aligned");
+  for (int i = 0; i < P * P; ++i)
+    if (!mask[i] && st->tc[i] < 0)
+      return fail(DITANGO_ENOCACHE, "pair (q=%d, k=%d) is marked REUSE but was never computed", i / P, i % P);
+  return launch_fused_step(Q, K, V, mask, st, O, LSE, stream);
+}
+
 int ditango_step(const void* Q, const void* K, const void* V, const uint8_t* mask, int32_t step,
                  ditango_states_t* st, float* O, float* LSE, uint8_t* reused_out, void* stream) {
   int rc = check_states(st);
@@ -553,11 +607,13 @@ int ditango_step(const void* Q, const void* K, const void* V, const uint8_t* mas
     if (!mask[i] && st->tc[i] < 0)
       return fail(DITANGO_ENOCACHE, "pair (q=%d, k=%d) is marked REUSE but was never computed", i / P, i % P);
   }
-  // After the checks above the three calls cannot fail on their arguments;
-  // only a launch error remains, reported as EHIP.
-  if ((rc = ditango_attn_partial(Q, K, V, mask, st, stream))) return rc;
-  if ((rc = ditango_state_cache_update(st, mask, step, reused_out))) return rc;
-  return ditango_state_merge(st, O, LSE, stream);
+  if (!Q || !K || !V) return fail(DITANGO_EINVAL, "Q, K and V must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(Q) | reinterpret_cast<uintptr_t>(K) | reinterpret_cast<uintptr_t>(V)) & 15u)
+    return fail(DITANGO_EINVAL, "Q, K and V must be 16-byte aligned");
+  // After the checks above only a launch error remains, reported as EHIP
+  // before t_c changes.
+  if ((rc = launch_fused_step(Q, K, V, mask, st, O, LSE, stream))) return rc;
+  return ditango_state_cache_update(st, mask, step, reused_out);
 }
 
 int ditango_window_residual_merge(const ditango_states_t* st, const uint8_t* window, int32_t mode, float* R,

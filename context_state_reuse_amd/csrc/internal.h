@@ -38,6 +38,28 @@ struct PartialParams {
   uint16_t pairs[DITANGO_MAX_P * DITANGO_MAX_P];  // work items (see above)
 };
 
+// Launch parameters of the fused step kernel (per-pair cache): one block per
+// (head, query partition q, query-row tile).  The block computes the fresh
+// pairs (q, fresh[q][i]), i < nf[q], one after the other over the same
+// query rows, stores each state into its cache slot, and then composes
+// (Eq. 4) the P states of its rows -- fresh and cached alike -- into the
+// output O [H][N][d], LSE [H][N].
+struct StepParams {
+  const __bf16* Q;          // [H][N][d]
+  const __bf16* K;
+  const __bf16* V;
+  float* O;                 // per-pair cache [H][P*P][S][d]
+  float* LSE;               // per-pair cache [H][P*P][S]
+  float* Oout;              // [H][N][d]
+  float* LSEout;            // [H][N]
+  int32_t H, N, P, S, d;
+  float scale_log2;
+  int32_t q_tiles;          // query tiles per partition
+  int32_t n_blocks;         // H * P * q_tiles
+  uint8_t nf[DITANGO_MAX_P];
+  uint8_t fresh[DITANGO_MAX_P][DITANGO_MAX_P];
+};
+
 // Composition (Eq. 4) of n_in states per row.  State k of the rows of
 // (head h, query partition q) starts at in_O[k] + (h*in_hs + q*in_qs)*S*d
 // (LSE: in_L[k] + (h*in_hs + q*in_qs)*S); it takes part when bit k of
@@ -106,6 +128,7 @@ int partial_rows_per_block(int d, int S);
 
 // Enqueue kernels; return hipSuccess or the launch error.
 hipError_t launch_partial(PartialParams& p, int rows_per_block, hipStream_t stream);
+hipError_t launch_step(StepParams& p, int rows_per_block, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_stats(const StatsParams& p, hipStream_t stream);
 hipError_t launch_drift(const DriftParams& p, hipStream_t stream);

@@ -278,6 +278,238 @@ constexpr int waves_per_simd() {
   return D == 128 ? 2 : 3;
 }
 
+// Per-lane map of a block's direct tile loads, fixed for the kernel.  Round
+// i of a tile covers LDS chunk positions [(i*WAVES + wave)*64, +64) (lane L
+// writes position +L); the global source offsets are swizzled as the LDS
+// layout requires.  V positions past column d (the d = 72 ones/zero chunks)
+// are not loaded.
+template <int D, int WAVES>
+struct TileLoadMap {
+  using G = Geometry<D>;
+  static constexpr int kGroupsK = kTile * G::kcpr / 64;            // 64-chunk groups per K tile
+  static constexpr int kGroupsV = kTile * G::vcpr / 64;
+  static constexpr int kRoundsK = (kGroupsK + WAVES - 1) / WAVES;  // groups per wave (the last may idle)
+  static constexpr int kRoundsV = (kGroupsV + WAVES - 1) / WAVES;
+  static_assert(kTile * G::kcpr % 64 == 0 && kTile * G::vcpr % 64 == 0, "tiles must split into 64-chunk groups");
+  int krow_of[kRoundsK], kgoff[kRoundsK], vrow_of[kRoundsV], vgoff[kRoundsV];
+  int swave;
+  __device__ TileLoadMap(int wave, int lane) {
+    swave = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+    for (int i = 0; i < kRoundsK; ++i) {
+      const int idx = min((i * WAVES + wave) * 64 + lane, kTile * G::kcpr - 1);
+      const int r = idx / G::kcpr, pos = idx % G::kcpr;
+      krow_of[i] = r;
+      kgoff[i] = r * D + ((pos ^ G::kswz(r)) << 3);
+    }
+#pragma unroll
+    for (int i = 0; i < kRoundsV; ++i) {
+      const int idx = min((i * WAVES + wave) * 64 + lane, kTile * G::vcpr - 1);
+      const int r = idx / G::vcpr, pos = idx % G::vcpr;
+      vrow_of[i] = r;
+      vgoff[i] = pos < D / 8 ? r * D + ((pos ^ G::vswz(r)) << 3) : -1;   // -1: spare chunk, not loaded
+    }
+  }
+};
+
+// d = 72: the contraction pad 72..79 of a tile's last K row reads past the
+// tile: zeros there.  V chunks D/8 .. vcpr-1 of every row: 1.0 at column D,
+// zeros after (the ones row of O^T); the tile loads never write them.
+template <int D, int kThreads>
+__device__ __attribute__((always_inline)) inline void init_lds_pads(int tid, __bf16* k_lds0, __bf16* k_lds1,
+                                                                    __bf16* v_lds0, __bf16* v_lds1) {
+  using G = Geometry<D>;
+  if constexpr (G::kpad > 0) {
+    if (tid < 2) *reinterpret_cast<u32x4*>(&(tid == 0 ? k_lds0 : k_lds1)[kTile * G::KS]) = u32x4{0u, 0u, 0u, 0u};
+  }
+  if constexpr (G::ones_row) {
+    constexpr int padc = G::vcpr - D / 8;
+    static_assert(D % 8 == 0 && padc >= 1, "ones column starts a spare chunk");
+    for (int i = tid; i < 2 * kTile * padc; i += kThreads) {
+      const int j = i % (kTile * padc);
+      const int r = j / padc, c = D / 8 + j % padc;
+      const u32x4 val = {c == D / 8 ? 0x3f80u : 0u, 0u, 0u, 0u};   // bf16 1.0 in element 0
+      *reinterpret_cast<u32x4*>(&(i < kTile * padc ? v_lds0 : v_lds1)[r * G::VS + c * 8]) = val;
+    }
+  }
+}
+
+// Q^T operand of this lane's query row (row `row` of the partition, clamped
+// to its last row) and an empty state.
+template <int D>
+__device__ __attribute__((always_inline)) inline void load_q(WaveState<D>& w, const __bf16* Qh, int row, int len_q,
+                                                             int hw) {
+  using G = Geometry<D>;
+  const __bf16* qrow = Qh + static_cast<size_t>(min(row, len_q - 1)) * D;
+#pragma unroll
+  for (int s = 0; s < G::kSteps; ++s) {
+    const int dim = s * 16 + hw * 8;
+    if (dim < D) {
+      w.qf[s] = *reinterpret_cast<const bf16x8*>(qrow + dim);
+    } else {
+      w.qf[s] = bf16x8{};
+    }
+  }
+}
+
+template <int D>
+__device__ __attribute__((always_inline)) inline void reset_state(WaveState<D>& w) {
+  using G = Geometry<D>;
+#pragma unroll
+  for (int v = 0; v < G::vTiles; ++v) w.oacc[v] = f32x16{};
+  w.m_run = -__builtin_inff();
+  w.l_run = 0.0f;
+  w.lr_run = 0.0f;
+}
+
+// Attention of the block's query rows (Q^T in w.qf, state reset) over one
+// key range: the concatenated key index j < len_k lives at row k0 + j of
+// Kh0 / Vh0 (the head's K and V), or k0 + j + S once j >= len0 (a gap over
+// the query partition when it sits strictly inside a group; len0 = len_k
+// otherwise).  Per 64-key tile: scores -> softmax -> PV, one barrier; tile
+// kt lives in buffer pair kt & 1 and the next tile is fetched into the other
+// pair; the last (possibly ragged) tile is peeled so only it carries the key
+// mask.  Every LDS read of the range is done when it returns (the caller
+// meets the other waves before reusing the buffers).
+template <int D, int WAVES, bool GAP>
+__device__ __attribute__((always_inline)) inline void attend_keys(
+    WaveState<D>& w, const __bf16* Kh0, const __bf16* Vh0, int N, int S, int k0, int len_k, int len0,
+    __bf16* k_lds0, __bf16* k_lds1, __bf16* v_lds0, __bf16* v_lds1, const TileLoadMap<D, WAVES>& map,
+    const OperandOffsets<D>& off, int hw, float sl2) {
+  using G = Geometry<D>;
+  using M = TileLoadMap<D, WAVES>;
+  const __bf16* Kh = Kh0 + static_cast<size_t>(k0) * D;
+  const __bf16* Vh = Vh0 + static_cast<size_t>(k0) * D;
+  const int n_tiles = (len_k + kTile - 1) / kTile;
+  // A tile that straddles the gap maps each LDS row to its token on its own,
+  // through a descriptor over the range's keys from k0 to the end of the
+  // sequence (< 2^31 bytes).  Every other tile gets a descriptor of its own,
+  // based at the tile's first key and ending at the last key of its
+  // contiguous run (scalar arithmetic): a lane's offset is its fixed in-tile
+  // offset and rows past the end read zeros (their scores are masked).
+  const uint32_t kv_bytes = static_cast<uint32_t>(N - k0) * (D * 2u);
+  const __amdgpu_buffer_rsrc_t krsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(Kh), 0, static_cast<int>(kv_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(Vh), 0, static_cast<int>(kv_bytes), 0x00020000);
+  auto tile_load = [&](const __bf16* base, __amdgpu_buffer_rsrc_t whole, int kt, int elem, int r, __bf16* dst)
+                       __attribute__((always_inline)) {
+    const int t0 = kt * kTile;
+    if constexpr (!GAP) {
+      (void)whole;
+      (void)r;
+      tile_load_lds<D>(base, t0, len_k, elem, dst);
+    } else {
+      if (t0 + kTile <= len0 || t0 >= len0 || len0 == len_k) {   // one side of the gap (block-uniform)
+        const bool after = t0 >= len0 && len0 != len_k;
+        tile_load_lds<D>(base, t0 + (after ? S : 0), after ? len_k + S : len0, elem, dst);
+      } else {
+        int j = min(t0 + r, len_k - 1);
+        j += j >= len0 ? S : 0;
+        const int src = j * D + (elem - r * D);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(whole, (__attribute__((address_space(3))) void*)dst, 16, src * 2,
+                                                 0, 0, 0);
+      }
+    }
+  };
+  // Start fetching K tile kt into kdst and V tile kt into vdst; land() waits
+  // for this wave's loads and meets the other waves, after which every
+  // wave's part of the tiles is visible.
+  auto fetch = [&](int kt, __bf16* kdst, __bf16* vdst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < M::kRoundsK; ++i) {
+      if (M::kGroupsK % WAVES != 0 && i * WAVES + map.swave >= M::kGroupsK) break;   // wave-uniform
+      tile_load(Kh, krsrc, kt, map.kgoff[i], map.krow_of[i], kdst + (i * WAVES + map.swave) * 64 * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < M::kRoundsV; ++i) {
+      if (M::kGroupsV % WAVES != 0 && i * WAVES + map.swave >= M::kGroupsV) break;   // wave-uniform
+      if (G::vcpr == D / 8 || map.vgoff[i] >= 0)
+        tile_load(Vh, vrsrc, kt, map.vgoff[i], map.vrow_of[i], vdst + (i * WAVES + map.swave) * 64 * 8);
+    }
+  };
+  auto land = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have landed
+    __syncthreads();
+  };
+  // Buffer pair B (0 or 1) as compile-time pointers.
+  auto kb_ = [&](auto B) __attribute__((always_inline)) -> __bf16* { if constexpr (decltype(B)::value == 0) return k_lds0; else return k_lds1; };
+  auto vb_ = [&](auto B) __attribute__((always_inline)) -> __bf16* { if constexpr (decltype(B)::value == 0) return v_lds0; else return v_lds1; };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  auto full_tile = [&](auto B, int kt) __attribute__((always_inline)) {
+    using NB = std::integral_constant<int, 1 - decltype(B)::value>;
+    fetch(kt + 1, kb_(NB{}), vb_(NB{}));
+    tile_scores<D>(w, kb_(B), off);
+    tile_softmax<false, D>(w, kTile, hw, sl2);
+    tile_pv<D>(w, vb_(B), off);
+    land();
+  };
+  auto last_tile = [&](auto B, int kt) __attribute__((always_inline)) {
+    tile_scores<D>(w, kb_(B), off);
+    tile_softmax<true, D>(w, len_k - kt * kTile, hw, sl2);
+    tile_pv<D>(w, vb_(B), off);
+  };
+  fetch(0, k_lds0, v_lds0);
+  land();
+  int kt = 0;
+  for (; kt + 2 < n_tiles; kt += 2) {
+    full_tile(B0{}, kt);
+    full_tile(B1{}, kt + 1);
+  }
+  if (kt + 1 < n_tiles) {
+    full_tile(B0{}, kt);
+    last_tile(B1{}, kt + 1);
+  } else {
+    last_tile(B0{}, kt);
+  }
+}
+
+// OUT = O / l_rounded, LSE = ln2 * (m + log2 l) of this lane's query row
+// `row` into a state's rows at obase / lbase (rows at or past len_q are not
+// stored).
+template <int D>
+__device__ __attribute__((always_inline)) inline void store_state(const WaveState<D>& w, float* obase, float* lbase,
+                                                                  int row, int len_q, int hw, int l32) {
+  using G = Geometry<D>;
+  const float l_tot = w.l_run + xor32(w.l_run);
+  float lr_tot;
+  if constexpr (G::ones_row) {
+    // O^T row D sits in tile D/32, element 4*((D%32)/8) of the lanes of
+    // half-wave 0 (D % 8 == 0); broadcast it to the query's other half.
+    static_assert(D % 8 == 0, "ones row must start a 4-row group of half-wave 0");
+    lr_tot = __shfl(w.oacc[D / 32][4 * ((D % 32) / 8)], l32);
+  } else {
+    lr_tot = w.lr_run + xor32(w.lr_run);
+  }
+  const float inv = 1.0f / lr_tot;
+  if (row < len_q) {
+    float* orow = obase + static_cast<size_t>(row) * D;
+#pragma unroll
+    for (int v = 0; v < G::vTiles; ++v)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dim = v * 32 + 8 * g + 4 * hw;
+        if (dim < D) {
+          const f32x4 o = {w.oacc[v][4 * g] * inv, w.oacc[v][4 * g + 1] * inv, w.oacc[v][4 * g + 2] * inv,
+                           w.oacc[v][4 * g + 3] * inv};
+          *reinterpret_cast<f32x4*>(orow + dim) = o;
+        }
+      }
+    if (hw == 0) lbase[row] = (w.m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+  }
+}
+
+// XCD-aware block order: blocks are dealt round-robin to the 8 XCDs; remap
+// so each XCD runs a contiguous range of work items (items sharing K/V then
+// share its L2).
+__device__ __attribute__((always_inline)) inline int xcd_item(int nb) {
+  const int b = blockIdx.x;
+  const int xcd = b & 7;
+  const int per = nb >> 3, rem = nb & 7;
+  return xcd * per + (xcd < rem ? xcd : rem) + (b >> 3);
+}
+
 template <int D, int WAVES, bool GROUPED>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
                           amdgpu_waves_per_eu(waves_per_simd<D>(), waves_per_simd<D>())))
@@ -301,22 +533,15 @@ void partial_kernel(const PartialParams p) {
   const int hw = lane >> 5;   // half-wave
   const int l32 = lane & 31;
 
-  // Blocks are dealt round-robin to the 8 XCDs; remap so each XCD runs a
-  // contiguous range of work items (items sharing K/V then share its L2).
-  const int nb = p.n_blocks;
-  const int b = blockIdx.x;
-  const int xcd = b & 7;
-  const int per = nb >> 3, rem = nb & 7;
-  const int item = xcd * per + (xcd < rem ? xcd : rem) + (b >> 3);
-
+  const int item = xcd_item(p.n_blocks);
   const int qt = item % p.q_tiles;
   const int rest = item / p.q_tiles;
   const int pi = rest % p.n_pairs;
   const int h = rest / p.n_pairs;
   const int it = p.pairs[pi];
-  // Keys of the item: the concatenated key index j < len_k lives at token
-  // k0 + j, or k0 + j + S once j >= len0 (a gap over query partition q when
-  // it sits strictly inside a group; len0 = len_k otherwise).
+  // Keys of the item: k0 .. k0 + len_k, with a gap of S tokens over query
+  // partition q at concatenated index len0 when it sits strictly inside a
+  // group (len0 = len_k otherwise).
   int qp, k0, len_k, len0;
   float* obase;   // OUT row 0 of this item's state
   float* lbase;   // LSE row 0
@@ -355,197 +580,183 @@ void partial_kernel(const PartialParams p) {
   const int q0 = qp * p.S;
   const int len_q = min(p.S, p.N - q0);
   const size_t head = static_cast<size_t>(h) * p.N * D;
-  const __bf16* Qh = p.Q + head + static_cast<size_t>(q0) * D;
-  const __bf16* Kh = p.K + head + static_cast<size_t>(k0) * D;
-  const __bf16* Vh = p.V + head + static_cast<size_t>(k0) * D;
-  const float sl2 = p.scale_log2;
   const int row0 = qt * BR + wave * 32 + l32;     // this lane's query row
 
   WaveState<D> w;
-  {
-    const __bf16* qrow = Qh + static_cast<size_t>(min(row0, len_q - 1)) * D;
-#pragma unroll
-    for (int s = 0; s < G::kSteps; ++s) {
-      const int dim = s * 16 + hw * 8;
-      if (dim < D) {
-        w.qf[s] = *reinterpret_cast<const bf16x8*>(qrow + dim);
-      } else {
-        w.qf[s] = bf16x8{};
-      }
-    }
-#pragma unroll
-    for (int v = 0; v < G::vTiles; ++v) w.oacc[v] = f32x16{};
-    w.m_run = -__builtin_inff();
-    w.l_run = 0.0f;
-    w.lr_run = 0.0f;
-  }
-
-  // d = 72: the contraction pad 72..79 of a tile's last K row reads past the
-  // tile: zeros there.  V chunks D/8 .. vcpr-1 of every row: 1.0 at column
-  // D, zeros after (the ones row of O^T); the tile loads never write them.
-  if constexpr (G::kpad > 0) {
-    if (tid < 2) *reinterpret_cast<u32x4*>(&(tid == 0 ? k_lds0 : k_lds1)[kTile * G::KS]) = u32x4{0u, 0u, 0u, 0u};
-  }
-  if constexpr (G::ones_row) {
-    constexpr int padc = G::vcpr - D / 8;
-    static_assert(D % 8 == 0 && padc >= 1, "ones column starts a spare chunk");
-    for (int i = tid; i < 2 * kTile * padc; i += kThreads) {
-      const int j = i % (kTile * padc);
-      const int r = j / padc, c = D / 8 + j % padc;
-      const u32x4 val = {c == D / 8 ? 0x3f80u : 0u, 0u, 0u, 0u};   // bf16 1.0 in element 0
-      *reinterpret_cast<u32x4*>(&(i < kTile * padc ? v_lds0 : v_lds1)[r * G::VS + c * 8]) = val;
-    }
-  }
-
-  const int n_tiles = (len_k + kTile - 1) / kTile;
-
-  // Tile loads.  Round i of a tile covers LDS chunk positions
-  // [(i*WAVES + wave)*64, +64) (lane L writes position +L); per-lane element
-  // offsets of the global source (swizzled) are fixed for the kernel.  V
-  // positions past column d (the d = 72 ones/zero chunks) are not loaded.
-  constexpr int kGroupsK = kTile * G::kcpr / 64;            // 64-chunk groups per K tile
-  constexpr int kGroupsV = kTile * G::vcpr / 64;
-  constexpr int kRoundsK = (kGroupsK + WAVES - 1) / WAVES;  // groups per wave (the last may idle)
-  constexpr int kRoundsV = (kGroupsV + WAVES - 1) / WAVES;
-  static_assert(kTile * G::kcpr % 64 == 0 && kTile * G::vcpr % 64 == 0, "tiles must split into 64-chunk groups");
-  const int swave = __builtin_amdgcn_readfirstlane(wave);
-  int krow_of[kRoundsK], kgoff[kRoundsK], vrow_of[kRoundsV], vgoff[kRoundsV];
-#pragma unroll
-  for (int i = 0; i < kRoundsK; ++i) {
-    const int idx = min((i * WAVES + wave) * 64 + lane, kTile * G::kcpr - 1);
-    const int r = idx / G::kcpr, pos = idx % G::kcpr;
-    krow_of[i] = r;
-    kgoff[i] = r * D + ((pos ^ G::kswz(r)) << 3);
-  }
-#pragma unroll
-  for (int i = 0; i < kRoundsV; ++i) {
-    const int idx = min((i * WAVES + wave) * 64 + lane, kTile * G::vcpr - 1);
-    const int r = idx / G::vcpr, pos = idx % G::vcpr;
-    vrow_of[i] = r;
-    vgoff[i] = pos < D / 8 ? r * D + ((pos ^ G::vswz(r)) << 3) : -1;   // -1: spare chunk, not loaded
-  }
-  // A grouped item's tile that straddles the gap over q maps each LDS row to
-  // its token on its own, through a descriptor over the item's whole key
-  // range (from token k0 to the end of the sequence, < 2^31 bytes).  Every
-  // other tile gets a descriptor of its own, based at the tile's first key
-  // and ending at the last key of its contiguous run (scalar arithmetic): a
-  // lane's offset is its fixed in-tile offset and rows past the end read
-  // zeros (their scores are masked).
-  const uint32_t kv_bytes = static_cast<uint32_t>(p.N - k0) * (D * 2u);
-  const __amdgpu_buffer_rsrc_t krsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(Kh), 0, static_cast<int>(kv_bytes), 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(Vh), 0, static_cast<int>(kv_bytes), 0x00020000);
-  auto tile_load = [&](const __bf16* base, __amdgpu_buffer_rsrc_t whole, int kt, int elem, int r, __bf16* dst)
-                       __attribute__((always_inline)) {
-    const int t0 = kt * kTile;
-    if constexpr (!GROUPED) {
-      (void)whole;
-      (void)r;
-      tile_load_lds<D>(base, t0, len_k, elem, dst);
-    } else {
-      if (t0 + kTile <= len0 || t0 >= len0 || len0 == len_k) {   // one side of the gap (block-uniform)
-        const bool after = t0 >= len0 && len0 != len_k;
-        tile_load_lds<D>(base, t0 + (after ? p.S : 0), after ? len_k + p.S : len0, elem, dst);
-      } else {
-        int j = min(t0 + r, len_k - 1);
-        j += j >= len0 ? p.S : 0;
-        const int src = j * D + (elem - r * D);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(whole, (__attribute__((address_space(3))) void*)dst, 16, src * 2,
-                                                 0, 0, 0);
-      }
-    }
-  };
-  // Start fetching K tile kt into kdst and V tile kt into vdst; land() waits
-  // for this wave's loads and meets the other waves, after which every
-  // wave's part of the tiles is visible.
-  auto fetch = [&](int kt, __bf16* kdst, __bf16* vdst) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < kRoundsK; ++i) {
-      if (kGroupsK % WAVES != 0 && i * WAVES + swave >= kGroupsK) break;   // wave-uniform
-      tile_load(Kh, krsrc, kt, kgoff[i], krow_of[i], kdst + (i * WAVES + swave) * 64 * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < kRoundsV; ++i) {
-      if (kGroupsV % WAVES != 0 && i * WAVES + swave >= kGroupsV) break;   // wave-uniform
-      if (G::vcpr == D / 8 || vgoff[i] >= 0)
-        tile_load(Vh, vrsrc, kt, vgoff[i], vrow_of[i], vdst + (i * WAVES + swave) * 64 * 8);
-    }
-  };
-  auto land = [&]() __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have landed
-    __syncthreads();
-  };
-
+  load_q<D>(w, p.Q + head + static_cast<size_t>(q0) * D, row0, len_q, hw);
+  reset_state<D>(w);
+  init_lds_pads<D, kThreads>(tid, k_lds0, k_lds1, v_lds0, v_lds1);
+  const TileLoadMap<D, WAVES> map(wave, lane);
   // ds_read_b64_tr_b16 addressing for the V^T operand: in each 16-lane group
   // lane 4r+c supplies key row r, dims 4c..4c+3 of the group's 16 dims, and
   // receives dim (lane % 16) of the four rows.
-  const int tr_r = (lane & 15) >> 2;
-  const int tr_dim = ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
-  const OperandOffsets<D> off(l32, hw, tr_r, tr_dim);
-  // Buffer pair B (0 or 1) as compile-time pointers.
-  auto kb_ = [&](auto B) __attribute__((always_inline)) -> __bf16* { if constexpr (decltype(B)::value == 0) return k_lds0; else return k_lds1; };
-  auto vb_ = [&](auto B) __attribute__((always_inline)) -> __bf16* { if constexpr (decltype(B)::value == 0) return v_lds0; else return v_lds1; };
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
+  const OperandOffsets<D> off(l32, hw, (lane & 15) >> 2, ((lane >> 4) & 1) * 16 + 4 * (lane & 3));
+  attend_keys<D, WAVES, GROUPED>(w, p.K + head, p.V + head, p.N, p.S, k0, len_k, len0, k_lds0, k_lds1, v_lds0,
+                                 v_lds1, map, off, hw, p.scale_log2);
+  store_state<D>(w, obase, lbase, row0, len_q, hw, l32);
+}
 
-  // Per tile: scores -> softmax -> PV, one barrier.  Tile kt lives in buffer
-  // pair kt & 1; the next tile is fetched into the other pair.  The last
-  // (possibly ragged) tile is peeled so only it carries the key mask.
-  auto full_tile = [&](auto B, int kt) __attribute__((always_inline)) {
-    using NB = std::integral_constant<int, 1 - decltype(B)::value>;
-    fetch(kt + 1, kb_(NB{}), vb_(NB{}));
-    tile_scores<D>(w, kb_(B), off);
-    tile_softmax<false, D>(w, kTile, hw, sl2);
-    tile_pv<D>(w, vb_(B), off);
-    land();
-  };
-  auto last_tile = [&](auto B, int kt) __attribute__((always_inline)) {
-    tile_scores<D>(w, kb_(B), off);
-    tile_softmax<true, D>(w, len_k - kt * kTile, hw, sl2);
-    tile_pv<D>(w, vb_(B), off);
-  };
-  fetch(0, k_lds0, v_lds0);
-  land();
-  int kt = 0;
-  for (; kt + 2 < n_tiles; kt += 2) {
-    full_tile(B0{}, kt);
-    full_tile(B1{}, kt + 1);
+// Composition (Eq. 4) of the P pair states of this wave's rows r0 .. r0 +
+// nv - 1 of query partition q, head h, into the output: m = max_k LSE_k,
+// w_k = exp(LSE_k - m) / sum_k exp(LSE_k - m), OUT = sum_k w_k OUT_k,
+// LSE = m + log sum.  Lane l owns row l % 32 and the states k = 2i + l / 32,
+// so all P LSE loads of a row are in flight at once and the weights stay in
+// registers.  The rows' OUT values of a state are
+// nv*d contiguous floats, streamed with 16-byte non-temporal loads,
+// lane-consecutive (chunk c = lane + 64 j holds row c / (d/4)); a lane takes
+// its chunk's weight from the lane that owns the row and the state's parity.
+// The fresh states among them were written by this wave (the caller has
+// fenced those stores).
+template <int D>
+__device__ __attribute__((always_inline)) inline void merge_rows(const StepParams& p, int h, int q, int r0, int nv,
+                                                                 int lane) {
+  constexpr int CPR = D / 4;                       // 16-byte chunks per row
+  constexpr int J = (32 * CPR + 63) / 64;          // chunks per lane for 32 rows
+  constexpr int KH = DITANGO_MAX_P / 2;            // states per half-wave
+  constexpr float kLog2e = 1.4426950408889634f;
+  const int P = p.P, S = p.S;
+  const int hw = lane >> 5;
+  r0 = __builtin_amdgcn_readfirstlane(r0);         // uniform per wave: keeps the descriptors scalar
+  nv = __builtin_amdgcn_readfirstlane(nv);
+  const size_t slot0 = static_cast<size_t>(h) * P * P + static_cast<size_t>(q) * P;   // slot of pair (q, 0)
+  const float* Ls = p.LSE + slot0 * S + r0 + min(lane & 31, nv - 1);
+  const float* Os = p.O + (slot0 * S + r0) * D;
+  float wk[KH];
+#pragma unroll
+  for (int i = 0; i < KH; ++i) {
+    const int k = 2 * i + hw;
+    wk[i] = k < P ? Ls[static_cast<size_t>(k) * S] : 0.0f;
   }
-  if (kt + 1 < n_tiles) {
-    full_tile(B0{}, kt);
-    last_tile(B1{}, kt + 1);
-  } else {
-    last_tile(B0{}, kt);
+  float m = hw < P ? wk[0] : kMaskScore;          // half-wave 0 always holds state 0
+#pragma unroll
+  for (int i = 1; i < KH; ++i)
+    if (2 * i + hw < P) m = fmaxf(m, wk[i]);
+  m = fmaxf(m, xor32(m));
+  float zh = 0.0f;
+#pragma unroll
+  for (int i = 0; i < KH; ++i) {
+    wk[i] = 2 * i + hw < P ? __builtin_amdgcn_exp2f((wk[i] - m) * kLog2e) : 0.0f;
+    zh += wk[i];
   }
+  const float z = zh + xor32(zh);
+  const float invz = 1.0f / z;
+#pragma unroll
+  for (int i = 0; i < KH; ++i) wk[i] *= invz;
 
-  // Epilogue: OUT = O / l_rounded, LSE = ln2 * (m + log2 l), into the slot.
-  const float l_tot = w.l_run + xor32(w.l_run);
-  float lr_tot;
-  if constexpr (G::ones_row) {
-    // O^T row D sits in tile D/32, element 4*((D%32)/8) of the lanes of
-    // half-wave 0 (D % 8 == 0); broadcast it to the query's other half.
-    static_assert(D % 8 == 0, "ones row must start a 4-row group of half-wave 0");
-    lr_tot = __shfl(w.oacc[D / 32][4 * ((D % 32) / 8)], l32);
-  } else {
-    lr_tot = w.lr_run + xor32(w.lr_run);
-  }
-  const float inv = 1.0f / lr_tot;
-  if (row0 < len_q) {
-    float* orow = obase + static_cast<size_t>(row0) * D;
+  int crow[J];
 #pragma unroll
-    for (int v = 0; v < G::vTiles; ++v)
+  for (int j = 0; j < J; ++j) crow[j] = min((lane + 64 * j) / CPR, 31);
+  f32x4 acc[J];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dim = v * 32 + 8 * g + 4 * hw;
-        if (dim < D) {
-          const f32x4 o = {w.oacc[v][4 * g] * inv, w.oacc[v][4 * g + 1] * inv, w.oacc[v][4 * g + 2] * inv,
-                           w.oacc[v][4 * g + 3] * inv};
-          *reinterpret_cast<f32x4*>(orow + dim) = o;
-        }
-      }
-    if (hw == 0) lbase[row0] = (w.m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+  for (int j = 0; j < J; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int valid = nv * CPR;                      // chunks of the valid rows
+  // Each state's rows are read through a buffer descriptor ending at the
+  // last valid row: chunks past it read as zeros (never stored), so the
+  // loads need no branches or clamps, and chunk j's offset is the lane's
+  // offset plus a constant.  Cache policy 2: non-temporal.
+  auto load_state = [&](f32x4(&o)[J], int k) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(Os + static_cast<size_t>(k) * S * D), 0, valid * 16, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      o[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + j * 1024, 0, 2));
+  };
+  auto accumulate = [&](const f32x4(&o)[J], float w, int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) acc[j] += __shfl(w, crow[j] + 32 * b) * o[j];
+  };
+  // States 2i (half-wave 0's weights) and 2i + 1 (half-wave 1's) per
+  // iteration, each state's loads issued one state ahead of its use; the
+  // weights shift down one register per iteration so the current pair's
+  // are always wk[0].
+  f32x4 oa[J], ob[J];
+  load_state(oa, 0);
+  // The scheduling barriers keep each load batch after the arithmetic that
+  // frees its registers, so the batch in flight stays in the same registers
+  // across the loop's back edge (no copy that would wait for it).
+#pragma nounroll
+  for (int i = 0; 2 * i < P; ++i) {
+    load_state(ob, min(2 * i + 1, P - 1));       // P odd: the last pair's second state has weight 0
+    __builtin_amdgcn_sched_barrier(0);
+    accumulate(oa, wk[0], 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_state(oa, min(2 * i + 2, P - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    accumulate(ob, wk[0], 1);
+#pragma unroll
+    for (int t = 0; t + 1 < KH; ++t) wk[t] = wk[t + 1];
   }
+  float* dst = p.Oout + (static_cast<size_t>(h) * p.N + static_cast<size_t>(q) * S + r0) * D;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int c = lane + 64 * j;
+    if (c < valid) __builtin_nontemporal_store(acc[j], reinterpret_cast<f32x4*>(dst + 4 * c));
+  }
+  if (hw == 0 && lane < nv)
+    p.LSEout[static_cast<size_t>(h) * p.N + static_cast<size_t>(q) * S + r0 + lane] =
+        m + __builtin_amdgcn_logf(z) * 0.69314718055994531f;
+}
+
+// The whole step of the per-pair cache for one (head, query partition,
+// row tile): the fresh pairs of the partition's row of the mask, one after
+// the other over the same query rows, each state stored into its slot; then
+// each wave composes its rows' P states (the fresh ones just stored and the
+// cached ones) into the output.  A block whose wave merges while others
+// still multiply keeps the CU's matrix cores busy with the next blocks'
+// work: the composition's HBM reads overlap the other blocks' MFMA work
+// instead of running as a pass of their own after it.
+template <int D, int WAVES>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
+                          amdgpu_waves_per_eu(waves_per_simd<D>(), waves_per_simd<D>())))
+void step_kernel(const StepParams p) {
+  using G = Geometry<D>;
+  constexpr int kThreads = 64 * WAVES;
+  constexpr int BR = 32 * WAVES;
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds0[kTile * G::KS + G::kpad];
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds1[kTile * G::KS + G::kpad];
+  __shared__ __attribute__((aligned(16))) __bf16 v_lds0[kTile * G::VS];
+  __shared__ __attribute__((aligned(16))) __bf16 v_lds1[kTile * G::VS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hw = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int item = xcd_item(p.n_blocks);
+  const int qt = item % p.q_tiles;
+  const int rest = item / p.q_tiles;
+  const int q = rest % p.P;
+  const int h = rest / p.P;
+  const int q0 = q * p.S;
+  const int len_q = min(p.S, p.N - q0);
+  const size_t head = static_cast<size_t>(h) * p.N * D;
+  const int wrow0 = qt * BR + wave * 32;          // this wave's first query row
+  const int row0 = wrow0 + l32;                   // this lane's query row
+  const int nf = p.nf[q];
+
+  if (nf > 0) {
+    WaveState<D> w;
+    load_q<D>(w, p.Q + head + static_cast<size_t>(q0) * D, row0, len_q, hw);
+    init_lds_pads<D, kThreads>(tid, k_lds0, k_lds1, v_lds0, v_lds1);
+    const TileLoadMap<D, WAVES> map(wave, lane);
+    const OperandOffsets<D> off(l32, hw, (lane & 15) >> 2, ((lane >> 4) & 1) * 16 + 4 * (lane & 3));
+    for (int i = 0; i < nf; ++i) {
+      if (i > 0) __syncthreads();   // every wave is done with the previous pair's tiles
+      const int k = p.fresh[q][i];
+      const int k0 = k * p.S;
+      const int len_k = min(p.S, p.N - k0);
+      reset_state<D>(w);
+      attend_keys<D, WAVES, false>(w, p.K + head, p.V + head, p.N, p.S, k0, len_k, len_k, k_lds0, k_lds1, v_lds0,
+                                   v_lds1, map, off, hw, p.scale_log2);
+      const size_t slot = static_cast<size_t>(h) * p.P * p.P + static_cast<size_t>(q) * p.P + k;
+      store_state<D>(w, p.O + slot * p.S * D, p.LSE + slot * p.S, row0, len_q, hw, l32);
+    }
+    // the wave's state stores complete before it reads them back
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+  }
+  const int nv = min(32, len_q - wrow0);
+  if (nv > 0) merge_rows<D>(p, h, q, wrow0, nv, lane);
 }
 
 template <int D, int WAVES>
@@ -555,6 +766,12 @@ hipError_t launch(PartialParams& p, hipStream_t stream) {
   } else {
     hipLaunchKernelGGL((partial_kernel<D, WAVES, false>), dim3(p.n_blocks), dim3(64 * WAVES), 0, stream, p);
   }
+  return hipGetLastError();
+}
+
+template <int D, int WAVES>
+hipError_t launch_step_d(StepParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((step_kernel<D, WAVES>), dim3(p.n_blocks), dim3(64 * WAVES), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -577,6 +794,20 @@ hipError_t launch_partial(PartialParams& p, int rows, hipStream_t stream) {
     case 72: return rows == 128 ? launch<72, 4>(p, stream) : hipErrorInvalidValue;
     case 128: return rows == 256 ? launch<128, 8>(p, stream) : rows == 128 ? launch<128, 4>(p, stream)
                                                                            : hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace ditango
+
+namespace ditango {
+
+hipError_t launch_step(StepParams& p, int rows, hipStream_t stream) {
+  switch (p.d) {
+    case 64: return rows == 128 ? launch_step_d<64, 4>(p, stream) : hipErrorInvalidValue;
+    case 72: return rows == 128 ? launch_step_d<72, 4>(p, stream) : hipErrorInvalidValue;
+    case 128: return rows == 256 ? launch_step_d<128, 8>(p, stream) : rows == 128 ? launch_step_d<128, 4>(p, stream)
+                                                                                  : hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }

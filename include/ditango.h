@@ -78,20 +78,29 @@ typedef struct {
   int32_t* tc;
 } ditango_states_t;
 
-/* Bytes the caller must allocate for the cache of `shape`: *o_bytes for O
- * and *lse_bytes for LSE (either pointer may be NULL).  Returns their sum, or
- * 0 if the shape is invalid (message in ditango_last_error()). */
+/* Bytes the caller must allocate for the cache of `shape` (the per-pair
+ * state cache of the attention-state section, Fig. 6: one (OUT, LSE) state
+ * per head and (query partition, KV partition) pair): *o_bytes for O
+ * = H*P*P*S*d*4 and *lse_bytes for LSE = H*P*P*S*4 (either pointer may be
+ * NULL).  Returns their sum, or 0 if the shape is invalid (message in
+ * ditango_last_error()).  No allocation, no device call. */
 size_t ditango_states_bytes(const ditango_shape_t* shape, size_t* o_bytes, size_t* lse_bytes);
 
-/* Bind caller-owned buffers to `st` and mark every pair empty (tc[] = -1).
- * O and LSE must be 16-byte aligned device pointers of the sizes above.
+/* Bind caller-owned buffers to `st` and mark every pair empty (tc[] = -1:
+ * no state cached yet, so the first step must compute every pair, as the
+ * anchor step of the anchor-steps section does).  O and LSE must be 16-byte
+ * aligned device pointers of the sizes above; tc a host array of P*P int32.
+ * Nothing is copied or allocated; the buffers stay the caller's.
  * Errors: DITANGO_EINVAL. */
 int ditango_states_init(ditango_states_t* st, const ditango_shape_t* shape,
                         float* O, float* LSE, int32_t* tc);
 
 /* Fresh partial attention for every pair with mask[q][k] = 1 (COMPUTE), on
- * every head: writes that pair's (OUT, LSE) over its slot, overwriting the
- * stale state.  Pairs with mask = 0 (REUSE) are not touched and no work is
+ * every head: the attention state of query partition q against KV partition
+ * k, OUT = softmax(scale * Q_q K_k^T) V_k and LSE = log sum exp of those
+ * scaled scores (attention-state section, the state definition before
+ * Eq. 4), written
+ * over the pair's slot, overwriting the stale state.  Pairs with mask = 0 (REUSE) are not touched and no work is
  * launched for them.  Computes with bf16 inputs, fp32 accumulation, fp32
  * softmax statistics; probabilities are rounded to bf16 before the product
  * with V.  Checks before launching anything that every REUSE pair holds a
@@ -115,12 +124,27 @@ int ditango_state_cache_update(ditango_states_t* st, const uint8_t* mask, int32_
  * else DITANGO_ENOCACHE.  Errors: EINVAL, ENOCACHE, EHIP. */
 int ditango_state_merge(const ditango_states_t* st, float* O, float* LSE, void* stream);
 
+/* The partial attention of the COMPUTE pairs and the composition (Eq. 4)
+ * of every row in one launch: what ditango_attn_partial followed by
+ * ditango_state_merge computes (the same fresh states, stored into the same
+ * slots; O and LSE [H][N][d], [H][N] as ditango_state_merge writes them, up
+ * to the rounding of the composition's sums), without t_c changes.  One
+ * block per (head, query partition, query-row tile) computes that row's
+ * fresh pairs one after the other and then composes the rows' P states, so
+ * the composition's memory traffic overlaps other blocks' matrix work
+ * (DiTango page, ring-based composed attention: partial states are composed
+ * as they are produced).  Every REUSE pair must hold a state (tc >= 0),
+ * else DITANGO_ENOCACHE before any launch.  Errors: EINVAL, ENOCACHE, EHIP. */
+int ditango_attn_partial_merge(const void* Q, const void* K, const void* V, const uint8_t* mask,
+                               ditango_states_t* st, float* O, float* LSE, void* stream);
+
 /* One denoising step of one layer (anchor steps included): the partial
  * attention of the COMPUTE pairs, the t_c update and the composition, i.e.
  * ditango_attn_partial, ditango_state_cache_update and ditango_state_merge
- * in that order on `stream`, with every check done before anything is
- * launched or any t_c changes.  reused_out as in ditango_state_cache_update
- * (may be NULL).  Errors: EINVAL, ENOCACHE, EHIP. */
+ * in that order, with every check done before anything is launched or any
+ * t_c changes.  The device work is one ditango_attn_partial_merge launch on
+ * `stream`.  reused_out as in ditango_state_cache_update (may be NULL).
+ * Errors: EINVAL, ENOCACHE, EHIP. */
 int ditango_step(const void* Q, const void* K, const void* V, const uint8_t* mask, int32_t step,
                  ditango_states_t* st, float* O, float* LSE, uint8_t* reused_out, void* stream);
 

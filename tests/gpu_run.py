@@ -18,10 +18,12 @@ def to_device(bits: np.ndarray):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda")
 
 
-def run_steps(w, masks=None, steps=None, on_step=None, label=""):
+def run_steps(w, masks=None, steps=None, on_step=None, label="", fused=False):
     """Run the library over the steps of workload w.
 
     masks: optional {t: mask}; default is the library's own mask builder.
+    fused: each step is one ditango_step call (the fused partial + merge
+    launch) instead of partial, t_c update and merge called one by one.
     on_step(t, mask, reused, cache, O, LSE) is called after each step
     (after a device synchronisation).
     """
@@ -40,11 +42,14 @@ def run_steps(w, masks=None, steps=None, on_step=None, label=""):
         Q, K, V = to_device(qb), to_device(kb), to_device(vb)
         del qb, kb, vb
         mask = lib.workload_mask(w, t) if masks is None or t not in masks else np.asarray(masks[t], np.uint8)
-        lib.ditango_attn_partial(Q, K, V, mask, cache)
-        reused = lib.ditango_state_cache_update(cache, mask, t)
-        lib.ditango_state_merge(cache, O, LSE)
+        if fused:
+            _, _, reused = lib.ditango_step(Q, K, V, mask, t, cache, O, LSE)
+        else:
+            lib.ditango_attn_partial(Q, K, V, mask, cache)
+            reused = lib.ditango_state_cache_update(cache, mask, t)
+            lib.ditango_state_merge(cache, O, LSE)
         torch.cuda.synchronize()
-        log(f"  [{label or w.name}] step {t}: fresh {int(mask.sum())}/{w.P * w.P} pairs, {time.time() - t0:.1f}s")
+        log(f"  [{label or w.name}{' fused' if fused else ''}] step {t}: fresh {int(mask.sum())}/{w.P * w.P} pairs, {time.time() - t0:.1f}s")
         if on_step is not None:
             on_step(t, mask, reused, cache, O, LSE)
         del Q, K, V

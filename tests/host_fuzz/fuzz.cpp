@@ -8,7 +8,7 @@
 #include <vector>
 #include "ditango.h"
 namespace ditango {
-extern long g_partial, g_merge, g_stats, g_drift;
+extern long g_partial, g_merge, g_stats, g_drift, g_step;
 extern int g_last_n, g_last_blocks, g_last_qtiles;
 extern uint16_t g_last_pairs[DITANGO_MAX_P * DITANGO_MAX_P];
 }
@@ -109,6 +109,9 @@ int main() {
       }
       ++calls; oks += ditango_state_cache_update(&st, m.data(), ri(0, 4) ? t : ri(-2, 10), reused.data()) == 0;
       ++calls; oks += ditango_state_merge(&st, fake(0x600000), fake(0x700000), nullptr) == 0;
+      ++calls; oks += ditango_attn_partial_merge(ri(0, 20) ? fake(0x300000) : nullptr, fake(0x400000), fake(0x500000),
+                                                 m.data(), &st, fake(0x600000), ri(0, 20) ? fake(0x700000) : nullptr,
+                                                 nullptr) == 0;
       ++calls; oks += ditango_step(fake(0x300000), fake(0x400000), fake(0x500000), m.data(), t + 10, &st, fake(0x600000),
                                    fake(0x700000), reused.data(), nullptr) == 0;
       ++calls; oks += ditango_window_residual_merge(&st, m.data(), ri(-1, 2), fake(0x800000), fake(0x600000),
@@ -149,7 +152,7 @@ int main() {
       if (ri(0, 7) == 0) { ++calls; oks += ditango_group_reset(&st, O.data(), L.data()) == 0; }
     }
   }
-  printf("calls %ld ok %ld; launches partial %ld merge %ld stats %ld drift %ld\n", calls, oks, ditango::g_partial,
+  printf("calls %ld ok %ld; launches step %ld partial %ld merge %ld stats %ld drift %ld\n", calls, oks, ditango::g_step, ditango::g_partial,
          ditango::g_merge, ditango::g_stats, ditango::g_drift);
   return 0;
 }

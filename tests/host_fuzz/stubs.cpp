@@ -37,6 +37,23 @@ hipError_t launch_partial(PartialParams& p, int rows, hipStream_t) {
   }
   ++g_partial; return hipSuccess;
 }
+long g_step = 0;
+hipError_t launch_step(StepParams& p, int rows, hipStream_t) {
+  REQUIRE(p.P >= 1 && p.P <= DITANGO_MAX_P && p.S >= 1 && p.N >= p.P && p.H >= 1);
+  REQUIRE(rows == partial_rows_per_block(p.d, p.S));
+  REQUIRE(p.q_tiles == (p.S + rows - 1) / rows);
+  REQUIRE(static_cast<long long>(p.n_blocks) == static_cast<long long>(p.H) * p.P * p.q_tiles);
+  REQUIRE(static_cast<long long>(p.N) * p.d * 2 < (1LL << 31));
+  for (int q = 0; q < p.P; ++q) {
+    REQUIRE(p.nf[q] <= p.P);
+    for (int i = 0; i < p.nf[q]; ++i) {
+      REQUIRE(p.fresh[q][i] < p.P);
+      if (i) REQUIRE(p.fresh[q][i] > p.fresh[q][i - 1]);
+    }
+  }
+  REQUIRE(p.O && p.LSE && p.Oout && p.LSEout);
+  ++g_step; return hipSuccess;
+}
 hipError_t launch_merge(const MergeParams& m, hipStream_t) {
   REQUIRE(m.n_in >= 1 && m.n_in <= DITANGO_MAX_SLOTS);
   for (int q = 0; q < m.P; ++q) {

@@ -5,6 +5,9 @@ Bar (bf16 inputs, fp32 accumulation): OUT max-abs <= 2e-2 and mean-abs
 output; the selection mask, the reused set and t_c bit-exact; reused cache
 slots bit-identical to what was written at their t_c.
 
+The reduced and edge workloads run twice: partial, t_c update and merge as
+three calls, and each step as one fused launch (ditango_step).
+
 Reduced workloads keep each workload's d, P, mask policy and value recipe at
 sizes the oracle finishes in seconds, with several key tiles, both query-tile
 widths and ragged last partitions; the full-size workloads are checked on
@@ -86,7 +89,9 @@ def _run_full_compare(w, masks=None, label=None):
             check_state(O[h].cpu().numpy(), LSE[h].cpu().numpy(), res["O"][h], res["LSE"][h],
                         f"{w.name} step {t} head {h} merged")
 
-    run_steps(w, masks=masks, on_step=check, label=label)
+    for fused in (False, True):       # three calls per step, then the fused step launch
+        snap.clear()
+        run_steps(w, masks=masks, on_step=check, label=label, fused=fused)
     log(f"  {label or w.name}: worst pair state OUT max {worst[0]:.2e}, mean {worst[1]:.2e}, LSE {worst[2]:.2e}")
 
 
