@@ -82,27 +82,37 @@ def token_reuse(w, fresh: float) -> float:
     return 1.0 - fresh / (4.0 * w.N * w.N * w.d * w.H)
 
 
+def state_row_bytes(d: int) -> int:
+    """One cached state row: d bf16 OUT values and an fp32 LSE."""
+    return 2 * d + 4
+
+
+def out_row_bytes(d: int) -> int:
+    """One composed output row: d fp32 OUT values and an fp32 LSE."""
+    return 4 * d + 4
+
+
 def merge_bytes(w) -> float:
-    """Per row and head: read P states of d+1 floats, write one."""
-    return float(w.H * w.N * (w.P + 1) * (w.d + 1) * 4)
+    """Per row and head: read P cached states, write one fp32 output row."""
+    return float(w.H * w.N * (w.P * state_row_bytes(w.d) + out_row_bytes(w.d)))
 
 
 def state_store_bytes(w, mask) -> float:
     lens = np.array([min(w.S, w.N - p * w.S) for p in range(w.P)], dtype=np.float64)
-    return float(w.H * (w.d + 1) * 4 * (lens[:, None] * mask).sum())
+    return float(w.H * state_row_bytes(w.d) * (lens[:, None] * mask).sum())
 
 
 def group_work(w, g, computed):
     """Fresh FLOPs (4 * len_q * keys * d per computed slot and head) and
-    merge bytes (live slots' d+1 floats read plus d+1 written per row and
-    head) of one grouped step."""
+    merge bytes (the live slots' state rows read plus one output row written
+    per row and head) of one grouped step."""
     from context_state_reuse_amd import group_slot_keys, group_slot_live
     lens = [min(w.S, w.N - q * w.S) for q in range(w.P)]
     ns = computed.shape[1]
     flops = sum(4.0 * w.d * w.H * lens[q] * group_slot_keys(w.N, w.P, g, q, s)
                 for q in range(w.P) for s in range(ns) if computed[q, s])
     live = [sum(1 for s in range(ns) if group_slot_live(w.P, g, q, s)) for q in range(w.P)]
-    mbytes = sum(4.0 * w.H * lens[q] * (w.d + 1) * (live[q] + 1) for q in range(w.P))
+    mbytes = sum(float(w.H * lens[q] * (live[q] * state_row_bytes(w.d) + out_row_bytes(w.d))) for q in range(w.P))
     return flops, mbytes
 
 
@@ -479,7 +489,8 @@ def main():
         if wr:
             # window step: the window states and the residual read, one output written
             lens = np.array([min(w.S, w.N - p * w.S) for p in range(w.P)], dtype=np.float64)
-            mb = float(4.0 * w.H * (lens * (wmask.sum(axis=1) * (w.d + 1) + w.d + (w.d + 1))).sum())
+            mb = float(w.H * (lens * (wmask.sum(axis=1) * state_row_bytes(w.d) + 4 * w.d
+                                      + out_row_bytes(w.d))).sum())
 
     partial_tflops = fresh / (t_partial * 1e-3) / 1e12
     merge_gbs = mb / (t_merge * 1e-3) / 1e9 if t_merge > 0 else 0.0
@@ -498,7 +509,7 @@ def main():
         for q in range(w.P):
             for i in range(m_new):
                 parts = sum(lib.group_slot_live(w.P, g, q, 1 + j) for j in range(k * i, min(k * i + k, m_old)))
-                cbytes += (parts + (1 if parts else 0)) * 4.0 * w.H * lens[q] * (w.d + 1)
+                cbytes += (parts + (1 if parts else 0)) * float(w.H * lens[q] * state_row_bytes(w.d))
         before = cache.device_bytes
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         torch.cuda.synchronize()
@@ -516,8 +527,8 @@ def main():
                 "traffic": stored_traffic("step", w.name, src),
                 "avg_launch_ms": round(float(t_partial), 4),
                 "algorithmic_per_launch": f"{fresh:.4e} FLOP (4*len_q*len_k*d per fresh pair and head); the same "
-                                          f"launch moves {mb + sb:.4e} B of states (P*(d+1)*4 read + (d+1)*4 "
-                                          f"written per row and head, (d+1)*4 per fresh pair row stored)"}
+                                          f"launch moves {mb + sb:.4e} B of states (P*(2d+4) read + (4d+4) "
+                                          f"written per row and head, 2d+4 per fresh pair row stored)"}
     elif t_partial >= t_merge:
         roof = {"kernel": "partial_kernel", "bound": "mfma", "achieved": round(partial_tflops, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(partial_tflops / PEAK_BF16_TFLOPS, 4),
@@ -530,7 +541,7 @@ def main():
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(merge_gbs / PEAK_HBM_GBS, 4),
                 "traffic": None if (g or wr) else stored_traffic("merge", w.name, source_hash("merge.hip")),
                 "avg_launch_ms": round(float(t_merge), 4),
-                "algorithmic_per_launch": f"{mb:.4e} B ({'live slots' if g else 'P'}*(d+1)*4 read + (d+1)*4 "
+                "algorithmic_per_launch": f"{mb:.4e} B ({'live slots' if g else 'P'}*(2d+4) read + (4d+4) "
                                           f"written per row and head)"}
 
     out = {

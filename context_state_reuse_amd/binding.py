@@ -204,15 +204,16 @@ def ditango_states_bytes(shape: ditango_shape_t) -> tuple[int, int]:
 
 
 class StateCache:
-    """The attention-state cache: device O/LSE slots (torch) and host t_c."""
+    """The attention-state cache: device O (bfloat16) / LSE (float32) slots
+    (torch) and host t_c."""
 
     def __init__(self, H: int, N: int, d: int, P: int, scale: float | None = None, device="cuda"):
         import torch
         self.shape = make_shape(H, N, d, P, scale)
         ob, lb = ditango_states_bytes(self.shape)
         S = -(-N // P)
-        assert ob == H * P * P * S * d * 4 and lb == H * P * P * S * 4
-        self.O = torch.empty((H, P * P, S, d), dtype=torch.float32, device=device)
+        assert ob == H * P * P * S * d * 2 and lb == H * P * P * S * 4
+        self.O = torch.empty((H, P * P, S, d), dtype=torch.bfloat16, device=device)
         self.LSE = torch.empty((H, P * P, S), dtype=torch.float32, device=device)
         self.tc = np.full(P * P, -1, dtype=np.int32)
         self.st = ditango_states_t()
@@ -565,7 +566,7 @@ class GroupedStateCache:
 
     def _slot_o(self):
         import torch
-        return torch.empty((self.H, self.P, self.S, self.d), dtype=torch.float32, device=self.device)
+        return torch.empty((self.H, self.P, self.S, self.d), dtype=torch.bfloat16, device=self.device)
 
     def _slot_l(self):
         import torch
@@ -585,7 +586,7 @@ class GroupedStateCache:
 
     @property
     def device_bytes(self) -> int:
-        return sum(t.numel() * 4 for t in self.O + self.LSE)
+        return sum(t.numel() * t.element_size() for t in self.O + self.LSE)
 
     def compose(self, k: int = 2, stream=None, after=None) -> None:
         """Dynamic Group State Compose: group size g -> k g; frees released slots.

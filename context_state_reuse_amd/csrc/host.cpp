@@ -141,7 +141,10 @@ int64_t slot_keys(int N, int P, int S, int g, int q, int s) {
 
 int& gtc(const ditango_gstates_t* st, int q, int s) { return st->tc[q * DITANGO_MAX_SLOTS + s]; }
 
-int check_slot_buffers(float* const* O, float* const* LSE, int n) {
+// Cached OUT values are bf16; the C ABI carries them as their bit patterns.
+__bf16* bf16_ptr(ditango_bf16_t* p) { return reinterpret_cast<__bf16*>(p); }
+
+int check_slot_buffers(ditango_bf16_t* const* O, float* const* LSE, int n) {
   if (!O || !LSE) return fail(DITANGO_EINVAL, "slot buffer tables are NULL");
   for (int s = 0; s < n; ++s) {
     if (!O[s] || !LSE[s]) return fail(DITANGO_EINVAL, "slot %d buffers are NULL", s);
@@ -186,13 +189,13 @@ extern "C" {
 
 const char* ditango_last_error(void) { return g_err.c_str(); }
 
-int32_t ditango_version(void) { return 4; }
+int32_t ditango_version(void) { return 5; }
 
 size_t ditango_states_bytes(const ditango_shape_t* shape, size_t* o_bytes, size_t* lse_bytes) {
   int32_t S = 0;
   if (check_shape(shape, &S)) return 0;
   const size_t slots = static_cast<size_t>(shape->H) * shape->P * shape->P;
-  const size_t ob = slots * S * shape->d * sizeof(float);
+  const size_t ob = slots * S * shape->d * sizeof(ditango_bf16_t);
   const size_t lb = slots * S * sizeof(float);
   if (o_bytes) *o_bytes = ob;
   if (lse_bytes) *lse_bytes = lb;
@@ -200,7 +203,7 @@ size_t ditango_states_bytes(const ditango_shape_t* shape, size_t* o_bytes, size_
   return ob + lb;
 }
 
-int ditango_states_init(ditango_states_t* st, const ditango_shape_t* shape, float* O, float* LSE,
+int ditango_states_init(ditango_states_t* st, const ditango_shape_t* shape, ditango_bf16_t* O, float* LSE,
                         int32_t* tc) {
   if (!st) return fail(DITANGO_EINVAL, "states is NULL");
   int32_t S = 0;
@@ -244,7 +247,7 @@ int ditango_attn_partial(const void* Q, const void* K, const void* V, const uint
   p.Q = static_cast<const __bf16*>(Q);
   p.K = static_cast<const __bf16*>(K);
   p.V = static_cast<const __bf16*>(V);
-  p.O = st->O;
+  p.O = bf16_ptr(st->O);
   p.LSE = st->LSE;
   p.H = st->shape.H;
   p.N = st->shape.N;
@@ -298,7 +301,7 @@ int ditango_state_merge(const ditango_states_t* st, float* O, float* LSE, void* 
   std::memset(&m, 0, sizeof m);
   const size_t slot_o = static_cast<size_t>(st->S) * st->shape.d;
   for (int k = 0; k < P; ++k) {
-    m.in_O[k] = st->O + k * slot_o;
+    m.in_O[k] = bf16_ptr(st->O) + k * slot_o;
     m.in_L[k] = st->LSE + static_cast<size_t>(k) * st->S;
   }
   for (int q = 0; q < P; ++q) m.live[q] = P == 32 ? 0xffffffffu : (1u << P) - 1u;
@@ -334,7 +337,7 @@ int ditango_pair_stats(const ditango_states_t* st, const float* LSE, const uint8
     if (st->tc[i] < 0) return fail(DITANGO_ENOCACHE, "pair (q=%d, k=%d) holds no state", i / P, i % P);
   ditango::StatsParams sp;
   std::memset(&sp, 0, sizeof sp);
-  sp.O = st->O;
+  sp.O = bf16_ptr(st->O);
   sp.LSE_slot = st->LSE;
   sp.LSE = LSE;
   sp.W = W;
@@ -552,7 +555,7 @@ static int launch_fused_step(const void* Q, const void* K, const void* V, const 
   sp.Q = static_cast<const __bf16*>(Q);
   sp.K = static_cast<const __bf16*>(K);
   sp.V = static_cast<const __bf16*>(V);
-  sp.O = st->O;
+  sp.O = bf16_ptr(st->O);
   sp.LSE = st->LSE;
   sp.Oout = O;
   sp.LSEout = LSE;
@@ -641,7 +644,7 @@ int ditango_window_residual_merge(const ditango_states_t* st, const uint8_t* win
         return fail(DITANGO_ENOCACHE, "pair (q=%d, k=%d) holds no state", q, k);
   const size_t slot_o = static_cast<size_t>(st->S) * st->shape.d;
   for (int k = 0; k < P; ++k) {
-    m.in_O[k] = st->O + k * slot_o;
+    m.in_O[k] = bf16_ptr(st->O) + k * slot_o;
     m.in_L[k] = st->LSE + static_cast<size_t>(k) * st->S;
   }
   m.in_hs = static_cast<int64_t>(P) * P;
@@ -669,13 +672,13 @@ size_t ditango_gstates_slot_bytes(const ditango_shape_t* shape, size_t* o_bytes,
   int32_t S = 0;
   if (check_shape(shape, &S)) return 0;
   const size_t rows = static_cast<size_t>(shape->H) * shape->P * S;
-  if (o_bytes) *o_bytes = rows * shape->d * sizeof(float);
+  if (o_bytes) *o_bytes = rows * shape->d * sizeof(ditango_bf16_t);
   if (lse_bytes) *lse_bytes = rows * sizeof(float);
   ok();
-  return rows * (shape->d + 1) * sizeof(float);
+  return rows * (shape->d * sizeof(ditango_bf16_t) + sizeof(float));
 }
 
-int ditango_gstates_init(ditango_gstates_t* st, const ditango_shape_t* shape, int32_t g, float* const* O,
+int ditango_gstates_init(ditango_gstates_t* st, const ditango_shape_t* shape, int32_t g, ditango_bf16_t* const* O,
                          float* const* LSE, int32_t* tc) {
   if (!st) return fail(DITANGO_EINVAL, "states is NULL");
   int32_t S = 0;
@@ -739,7 +742,7 @@ int ditango_group_attn_partial(const void* Q, const void* K, const void* V, cons
   p.grouped = 1;
   p.g = g;
   for (int s = 0; s < ns; ++s) {
-    p.gO[s] = st->O[s];
+    p.gO[s] = bf16_ptr(st->O[s]);
     p.gLSE[s] = st->LSE[s];
   }
   const int rows = ditango::partial_rows_per_block(p.d, p.S);
@@ -794,7 +797,7 @@ int ditango_group_merge(const ditango_gstates_t* st, float* O, float* LSE, void*
         m.live[q] |= 1u << s;
       }
   for (int s = 0; s < ns; ++s) {
-    m.in_O[s] = st->O[s];
+    m.in_O[s] = bf16_ptr(st->O[s]);
     m.in_L[s] = st->LSE[s];
   }
   m.out_hs = st->shape.N;
@@ -830,7 +833,7 @@ int ditango_group_compose(ditango_gstates_t* st, int32_t k, void* stream) {
     std::memset(&m, 0, sizeof m);
     bool any = false;
     for (int j = j0; j < j1; ++j) {
-      m.in_O[j - j0] = st->O[1 + j];
+      m.in_O[j - j0] = bf16_ptr(st->O[1 + j]);
       m.in_L[j - j0] = st->LSE[1 + j];
     }
     for (int q = 0; q < P; ++q) {
@@ -846,7 +849,7 @@ int ditango_group_compose(ditango_gstates_t* st, int32_t k, void* stream) {
     if (!any) continue;
     m.out_hs = static_cast<int64_t>(P) * st->S;
     m.out_qs = st->S;
-    m.O = st->O[1 + i];
+    m.Os = bf16_ptr(st->O[1 + i]);
     m.LSE = st->LSE[1 + i];
     hipError_t e = launch_group_merge(m, st, j1 - j0, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(DITANGO_EHIP, "group merge kernel launch: %s", hipGetErrorString(e));
@@ -887,7 +890,7 @@ int ditango_group_fit(ditango_gstates_t* st, size_t budget_bytes, int32_t k, voi
   return ok();
 }
 
-int ditango_group_reset(ditango_gstates_t* st, float* const* O, float* const* LSE) {
+int ditango_group_reset(ditango_gstates_t* st, ditango_bf16_t* const* O, float* const* LSE) {
   if (!st) return fail(DITANGO_EINVAL, "states is NULL");
   int32_t S = 0;
   int rc = check_shape(&st->shape, &S);

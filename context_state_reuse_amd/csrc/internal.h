@@ -24,7 +24,7 @@ struct PartialParams {
   const __bf16* Q;          // [H][N][d]
   const __bf16* K;          // [H][N][d]
   const __bf16* V;          // [H][N][d]
-  float* O;                 // per-pair cache [H][P*P][S][d]
+  __bf16* O;                // per-pair cache [H][P*P][S][d]
   float* LSE;               // per-pair cache [H][P*P][S]
   int32_t H, N, P, S, d;
   float scale_log2;         // scale * log2(e): scores in base-2 units
@@ -33,7 +33,7 @@ struct PartialParams {
   int32_t n_blocks;         // H * n_pairs * q_tiles
   int32_t grouped;          // 0: per-pair cache, 1: grouped cache
   int32_t g;                // group size (grouped)
-  float* gO[DITANGO_MAX_SLOTS];    // grouped: slot buffers [H][P][S][d]
+  __bf16* gO[DITANGO_MAX_SLOTS];   // grouped: slot buffers [H][P][S][d]
   float* gLSE[DITANGO_MAX_SLOTS];  // grouped: [H][P][S]
   uint16_t pairs[DITANGO_MAX_P * DITANGO_MAX_P];  // work items (see above)
 };
@@ -48,7 +48,7 @@ struct StepParams {
   const __bf16* Q;          // [H][N][d]
   const __bf16* K;
   const __bf16* V;
-  float* O;                 // per-pair cache [H][P*P][S][d]
+  __bf16* O;                // per-pair cache [H][P*P][S][d]
   float* LSE;               // per-pair cache [H][P*P][S]
   float* Oout;              // [H][N][d]
   float* LSEout;            // [H][N]
@@ -63,8 +63,9 @@ struct StepParams {
 // Composition (Eq. 4) of n_in states per row.  State k of the rows of
 // (head h, query partition q) starts at in_O[k] + (h*in_hs + q*in_qs)*S*d
 // (LSE: in_L[k] + (h*in_hs + q*in_qs)*S); it takes part when bit k of
-// live[q] is set.  Row r of (h, q) is written to O + (h*out_hs + q*out_qs
-// + r)*d and LSE + h*out_hs + q*out_qs + r.  A (h, q) with no live state is
+// live[q] is set.  Row r of (h, q) is written to O (or, for a group slot,
+// Os in bf16) + (h*out_hs + q*out_qs + r)*d and LSE + h*out_hs + q*out_qs
+// + r.  A (h, q) with no live state is
 // skipped.  The row merge of both caches and the in-place group merge of
 // the grouped cache are instances.
 //
@@ -72,7 +73,7 @@ struct StepParams {
 // O): res_mode 1 also writes res = OUT - (composition of the states in
 // wlive[q]); res_mode 2 adds res to OUT.
 struct MergeParams {
-  const float* in_O[DITANGO_MAX_SLOTS];
+  const __bf16* in_O[DITANGO_MAX_SLOTS];
   const float* in_L[DITANGO_MAX_SLOTS];
   uint32_t live[DITANGO_MAX_P];
   uint32_t wlive[DITANGO_MAX_P];
@@ -84,7 +85,8 @@ struct MergeParams {
   uint32_t wpos[DITANGO_MAX_P];
   int64_t in_hs, in_qs;     // in units of S rows
   int64_t out_hs, out_qs;   // in rows
-  float* O;
+  float* O;                 // fp32 output rows, or
+  __bf16* Os;               // bf16 output rows (a group slot) when not null
   float* LSE;
   float* res;
   int32_t res_mode;
@@ -99,7 +101,7 @@ struct MergeParams {
 // W == nullptr: importance not wanted; the grid then covers the selected
 // pairs only, listed in pairs[0 .. n_pairs).
 struct StatsParams {
-  const float* O;           // per-pair cache [H][P*P][S][d]
+  const __bf16* O;          // per-pair cache [H][P*P][S][d]
   const float* LSE_slot;    // [H][P*P][S]
   const float* LSE;         // merged [H][N]
   float* W;                 // [H][P][P] or nullptr

@@ -9,14 +9,15 @@
 // output is a group slot.  Where the states are and which take part come
 // from tables in the launch parameters.
 //
-// HBM-bound: per row and head it reads n*(d+1) floats and writes d+1.
-// A block owns R consecutive rows of one query partition of one head.
+// HBM-bound: per row and head it reads n states of d bf16 values and one
+// fp32 LSE each, and writes d fp32 values (bf16 for a group slot) and an
+// LSE.  A block owns R consecutive rows of one query partition of one head.
 //   1. one lane per (row, state) loads LSE_k, the row's lanes reduce max and
 //      sum with cross-lane shuffles, and the normalised weights go to LDS;
-//   2. for every state k the block streams the R*d contiguous floats of its
-//      rows with 16-byte loads -- all states' loads are issued before the
-//      first is used, about 32 per thread -- and accumulates w_k * OUT_k in
-//      registers;
+//   2. for every state k the block streams the R*d contiguous bf16 values of
+//      its rows in 16-byte chunks of 8 -- all states' loads are issued
+//      before the first is used -- and accumulates w_k * OUT_k in fp32
+//      registers (bf16 -> fp32 is exact);
 //   3. the R*d outputs are written contiguously.
 // R = 256 / PMAX keeps up to 32 independent loads in flight per thread; the
 // template chosen for a state count is in launch_d.  Each output element is written by the thread that read that
@@ -37,6 +38,8 @@ namespace ditango {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 
@@ -51,12 +54,38 @@ __device__ inline f32x4 load_stream(const float* p) {
   if constexpr (DITANGO_MERGE_NT) return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
   return *reinterpret_cast<const f32x4*>(p);
 }
+__device__ inline u32x4 load_stream(const __bf16* p) {
+  if constexpr (DITANGO_MERGE_NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return *reinterpret_cast<const u32x4*>(p);
+}
 __device__ inline void store_stream(float* p, f32x4 v) {
   if constexpr (DITANGO_MERGE_NT) {
     __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
   } else {
     *reinterpret_cast<f32x4*>(p) = v;
   }
+}
+__device__ inline void store_stream(__bf16* p, u32x4 v) {
+  if constexpr (DITANGO_MERGE_NT) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  } else {
+    *reinterpret_cast<u32x4*>(p) = v;
+  }
+}
+
+// The 8 bf16 values of a 16-byte chunk as fp32 (exact: the pattern in the
+// high half of a word), and back (round to nearest even).
+__device__ inline void unpack8(u32x4 u, f32x4& lo, f32x4& hi) {
+  lo = f32x4{__builtin_bit_cast(float, u.x << 16), __builtin_bit_cast(float, u.x & 0xffff0000u),
+             __builtin_bit_cast(float, u.y << 16), __builtin_bit_cast(float, u.y & 0xffff0000u)};
+  hi = f32x4{__builtin_bit_cast(float, u.z << 16), __builtin_bit_cast(float, u.z & 0xffff0000u),
+             __builtin_bit_cast(float, u.w << 16), __builtin_bit_cast(float, u.w & 0xffff0000u)};
+}
+__device__ inline u32x4 pack8(f32x4 lo, f32x4 hi) {
+  const bf16x2 a = {(__bf16)lo.x, (__bf16)lo.y}, b = {(__bf16)lo.z, (__bf16)lo.w};
+  const bf16x2 c = {(__bf16)hi.x, (__bf16)hi.y}, d = {(__bf16)hi.z, (__bf16)hi.w};
+  return u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+               __builtin_bit_cast(uint32_t, d)};
 }
 
 // COMPACT: lanes walk the compacted live list idx[q][0 .. cnt[q]) (one more
@@ -66,7 +95,8 @@ __device__ inline void store_stream(float* p, f32x4 v) {
 template <int D, int PMAX, int RES, bool COMPACT>
 __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p, int row_tiles) {
   constexpr int R = kThreads / PMAX;                  // rows per block
-  constexpr int CH = R * D / 4;                       // float4 chunks per state block
+  constexpr int CPR = D / 8;                          // 16-byte bf16 chunks per row
+  constexpr int CH = R * CPR;                         // chunks per state block
   constexpr int PER = (CH + kThreads - 1) / kThreads; // chunks per thread
   __shared__ float w_lds[R][PMAX];
   __shared__ float wr_lds[RES == 1 ? R : 1][PMAX];     // weights of res = OUT - OUT_window
@@ -90,7 +120,9 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p, in
   {
     const int r = tid / PMAX, k = tid % PMAX;
     const bool lv = k < cnt && ((live >> k) & 1u) && r < rows;
-    float l = lv ? p.in_L[state(k)][in_row0 + r] : -__builtin_inff();
+    // Lanes without a state take -FLT_MAX and weight 0, so no infinity or
+    // NaN arises even in rows past the end of the block's rows.
+    float l = lv ? p.in_L[state(k)][in_row0 + r] : -3.4028234663852886e38f;
     float m = l;
 #pragma unroll
     for (int off = 1; off < PMAX; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
@@ -98,41 +130,41 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p, in
     float z = e;
 #pragma unroll
     for (int off = 1; off < PMAX; off <<= 1) z += __shfl_xor(z, off);
-    w_lds[r][k] = e / z;
+    w_lds[r][k] = e / (z > 0.0f ? z : 1.0f);
     if constexpr (RES == 1) {
       const bool win = lv && (((COMPACT ? p.wpos[q] : p.wlive[q]) >> k) & 1u);
-      float mw = win ? l : -__builtin_inff();
+      float mw = win ? l : -3.4028234663852886e38f;
 #pragma unroll
       for (int off = 1; off < PMAX; off <<= 1) mw = fmaxf(mw, __shfl_xor(mw, off));
       const float ew = win ? __builtin_amdgcn_exp2f((l - mw) * 1.4426950408889634f) : 0.0f;
       float zw = ew;
 #pragma unroll
       for (int off = 1; off < PMAX; off <<= 1) zw += __shfl_xor(zw, off);
-      wr_lds[r][k] = e / z - ew / zw;
+      wr_lds[r][k] = e / (z > 0.0f ? z : 1.0f) - ew / (zw > 0.0f ? zw : 1.0f);
     }
     if (k == 0 && r < rows) p.LSE[out_row0 + r] = m + __builtin_amdgcn_logf(z) * 0.69314718055994531f;
   }
   __syncthreads();
 
   // 2. stream the states
-  const int valid = rows * (D / 4);
-  f32x4 acc[PER];
-  f32x4 racc[RES == 1 ? PER : 1];
-  f32x4 o[PMAX][PER];
+  const int valid = rows * CPR;
+  f32x4 acc[PER][2];
+  f32x4 racc[RES == 1 ? PER : 1][2];
+  u32x4 o[PMAX][PER];
 #pragma unroll
-  for (int j = 0; j < PER; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < PER; ++j) acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   if constexpr (RES == 1) {
 #pragma unroll
-    for (int j = 0; j < PER; ++j) racc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < PER; ++j) racc[j][0] = racc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int k = 0; k < PMAX; ++k) {
     if (k < cnt && ((live >> k) & 1u)) {
-      const float* src = p.in_O[state(k)] + in_row0 * D;
+      const __bf16* src = p.in_O[state(k)] + in_row0 * D;
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         const int c = tid + j * kThreads;
-        if (c < valid) o[k][j] = load_stream(src + 4 * c);
+        if (c < valid) o[k][j] = load_stream(src + 8 * c);
       }
     }
   }
@@ -143,23 +175,42 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p, in
       for (int j = 0; j < PER; ++j) {
         const int c = tid + j * kThreads;
         if (c < valid) {
-          acc[j] += w_lds[c / (D / 4)][k] * o[k][j];
-          if constexpr (RES == 1) racc[j] += wr_lds[c / (D / 4)][k] * o[k][j];
+          f32x4 lo, hi;
+          unpack8(o[k][j], lo, hi);
+          const float wt = w_lds[c / CPR][k];
+          acc[j][0] += wt * lo;
+          acc[j][1] += wt * hi;
+          if constexpr (RES == 1) {
+            const float wr = wr_lds[c / CPR][k];
+            racc[j][0] += wr * lo;
+            racc[j][1] += wr * hi;
+          }
         }
       }
     }
   }
 
   // 3. write
-  float* dst = p.O + out_row0 * D;
   float* rdst = p.res + out_row0 * D;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int c = tid + j * kThreads;
     if (c < valid) {
-      if constexpr (RES == 2) acc[j] += load_stream(rdst + 4 * c);
-      store_stream(dst + 4 * c, acc[j]);
-      if constexpr (RES == 1) store_stream(rdst + 4 * c, racc[j]);
+      if constexpr (RES == 2) {
+        acc[j][0] += load_stream(rdst + 8 * c);
+        acc[j][1] += load_stream(rdst + 8 * c + 4);
+      }
+      if (p.Os) {                                      // block-uniform: a group slot
+        store_stream(p.Os + out_row0 * D + 8 * c, pack8(acc[j][0], acc[j][1]));
+      } else {
+        float* dst = p.O + out_row0 * D;
+        store_stream(dst + 8 * c, acc[j][0]);
+        store_stream(dst + 8 * c + 4, acc[j][1]);
+      }
+      if constexpr (RES == 1) {
+        store_stream(rdst + 8 * c, racc[j][0]);
+        store_stream(rdst + 8 * c + 4, racc[j][1]);
+      }
     }
   }
 }

@@ -370,12 +370,15 @@ __device__ __attribute__((always_inline)) inline void reset_state(WaveState<D>& 
 // kt lives in buffer pair kt & 1 and the next tile is fetched into the other
 // pair; the last (possibly ragged) tile is peeled so only it carries the key
 // mask.  Every LDS read of the range is done when it returns (the caller
-// meets the other waves before reusing the buffers).
+// meets the other waves before reusing the buffers).  A wave whose 32 query
+// rows all lie past the end of a ragged partition (live = false) only loads
+// its share of the tiles and meets the barriers, leaving its SIMD to the
+// waves that have work.
 template <int D, int WAVES, bool GAP>
 __device__ __attribute__((always_inline)) inline void attend_keys(
     WaveState<D>& w, const __bf16* Kh0, const __bf16* Vh0, int N, int S, int k0, int len_k, int len0,
     __bf16* k_lds0, __bf16* k_lds1, __bf16* v_lds0, __bf16* v_lds1, const TileLoadMap<D, WAVES>& map,
-    const OperandOffsets<D>& off, int hw, float sl2) {
+    const OperandOffsets<D>& off, int hw, float sl2, bool live) {
   using G = Geometry<D>;
   using M = TileLoadMap<D, WAVES>;
   const __bf16* Kh = Kh0 + static_cast<size_t>(k0) * D;
@@ -440,15 +443,19 @@ __device__ __attribute__((always_inline)) inline void attend_keys(
   auto full_tile = [&](auto B, int kt) __attribute__((always_inline)) {
     using NB = std::integral_constant<int, 1 - decltype(B)::value>;
     fetch(kt + 1, kb_(NB{}), vb_(NB{}));
-    tile_scores<D>(w, kb_(B), off);
-    tile_softmax<false, D>(w, kTile, hw, sl2);
-    tile_pv<D>(w, vb_(B), off);
+    if (live) {
+      tile_scores<D>(w, kb_(B), off);
+      tile_softmax<false, D>(w, kTile, hw, sl2);
+      tile_pv<D>(w, vb_(B), off);
+    }
     land();
   };
   auto last_tile = [&](auto B, int kt) __attribute__((always_inline)) {
-    tile_scores<D>(w, kb_(B), off);
-    tile_softmax<true, D>(w, len_k - kt * kTile, hw, sl2);
-    tile_pv<D>(w, vb_(B), off);
+    if (live) {
+      tile_scores<D>(w, kb_(B), off);
+      tile_softmax<true, D>(w, len_k - kt * kTile, hw, sl2);
+      tile_pv<D>(w, vb_(B), off);
+    }
   };
   fetch(0, k_lds0, v_lds0);
   land();
@@ -465,11 +472,11 @@ __device__ __attribute__((always_inline)) inline void attend_keys(
   }
 }
 
-// OUT = O / l_rounded, LSE = ln2 * (m + log2 l) of this lane's query row
-// `row` into a state's rows at obase / lbase (rows at or past len_q are not
-// stored).
+// OUT = O / l_rounded (rounded to bf16), LSE = ln2 * (m + log2 l) of this
+// lane's query row `row` into a state's rows at obase / lbase (rows at or
+// past len_q are not stored).
 template <int D>
-__device__ __attribute__((always_inline)) inline void store_state(const WaveState<D>& w, float* obase, float* lbase,
+__device__ __attribute__((always_inline)) inline void store_state(const WaveState<D>& w, __bf16* obase, float* lbase,
                                                                   int row, int len_q, int hw, int l32) {
   using G = Geometry<D>;
   const float l_tot = w.l_run + xor32(w.l_run);
@@ -484,16 +491,17 @@ __device__ __attribute__((always_inline)) inline void store_state(const WaveStat
   }
   const float inv = 1.0f / lr_tot;
   if (row < len_q) {
-    float* orow = obase + static_cast<size_t>(row) * D;
+    __bf16* orow = obase + static_cast<size_t>(row) * D;
 #pragma unroll
     for (int v = 0; v < G::vTiles; ++v)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int dim = v * 32 + 8 * g + 4 * hw;
         if (dim < D) {
-          const f32x4 o = {w.oacc[v][4 * g] * inv, w.oacc[v][4 * g + 1] * inv, w.oacc[v][4 * g + 2] * inv,
-                           w.oacc[v][4 * g + 3] * inv};
-          *reinterpret_cast<f32x4*>(orow + dim) = o;
+          const bf16x2 lo = {(__bf16)(w.oacc[v][4 * g] * inv), (__bf16)(w.oacc[v][4 * g + 1] * inv)};
+          const bf16x2 hi = {(__bf16)(w.oacc[v][4 * g + 2] * inv), (__bf16)(w.oacc[v][4 * g + 3] * inv)};
+          const u32x2 o = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+          *reinterpret_cast<u32x2*>(orow + dim) = o;
         }
       }
     if (hw == 0) lbase[row] = (w.m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
@@ -543,7 +551,7 @@ void partial_kernel(const PartialParams p) {
   // partition q at concatenated index len0 when it sits strictly inside a
   // group (len0 = len_k otherwise).
   int qp, k0, len_k, len0;
-  float* obase;   // OUT row 0 of this item's state
+  __bf16* obase;  // OUT row 0 of this item's state
   float* lbase;   // LSE row 0
   if constexpr (!GROUPED) {
     qp = it / p.P;
@@ -581,6 +589,7 @@ void partial_kernel(const PartialParams p) {
   const int len_q = min(p.S, p.N - q0);
   const size_t head = static_cast<size_t>(h) * p.N * D;
   const int row0 = qt * BR + wave * 32 + l32;     // this lane's query row
+  const bool live = __builtin_amdgcn_readfirstlane(qt * BR + wave * 32) < len_q;   // any row of the wave
 
   WaveState<D> w;
   load_q<D>(w, p.Q + head + static_cast<size_t>(q0) * D, row0, len_q, hw);
@@ -592,7 +601,7 @@ void partial_kernel(const PartialParams p) {
   // receives dim (lane % 16) of the four rows.
   const OperandOffsets<D> off(l32, hw, (lane & 15) >> 2, ((lane >> 4) & 1) * 16 + 4 * (lane & 3));
   attend_keys<D, WAVES, GROUPED>(w, p.K + head, p.V + head, p.N, p.S, k0, len_k, len0, k_lds0, k_lds1, v_lds0,
-                                 v_lds1, map, off, hw, p.scale_log2);
+                                 v_lds1, map, off, hw, p.scale_log2, live);
   store_state<D>(w, obase, lbase, row0, len_q, hw, l32);
 }
 
@@ -601,16 +610,15 @@ void partial_kernel(const PartialParams p) {
 // w_k = exp(LSE_k - m) / sum_k exp(LSE_k - m), OUT = sum_k w_k OUT_k,
 // LSE = m + log sum.  Lane l owns row l % 32 and the states k = 2i + l / 32,
 // so all P LSE loads of a row are in flight at once and the weights stay in
-// registers.  The rows' OUT values of a state are
-// nv*d contiguous floats, streamed with 16-byte non-temporal loads,
-// lane-consecutive (chunk c = lane + 64 j holds row c / (d/4)); a lane takes
-// its chunk's weight from the lane that owns the row and the state's parity.
-// The fresh states among them were written by this wave (the caller has
-// fenced those stores).
+// registers.  The rows' bf16 OUT values of a state are nv*d contiguous
+// elements, streamed in 16-byte chunks of 8 (chunk c = lane + 64 j holds
+// row c / (d/8)), non-temporal; a lane takes its chunk's weight from the
+// lane that owns the row and the state's parity.  The fresh states among
+// them were written by this wave (the caller has fenced those stores).
 template <int D>
 __device__ __attribute__((always_inline)) inline void merge_rows(const StepParams& p, int h, int q, int r0, int nv,
                                                                  int lane) {
-  constexpr int CPR = D / 4;                       // 16-byte chunks per row
+  constexpr int CPR = D / 8;                       // 16-byte chunks per row
   constexpr int J = (32 * CPR + 63) / 64;          // chunks per lane for 32 rows
   constexpr int KH = DITANGO_MAX_P / 2;            // states per half-wave
   constexpr float kLog2e = 1.4426950408889634f;
@@ -620,7 +628,7 @@ __device__ __attribute__((always_inline)) inline void merge_rows(const StepParam
   nv = __builtin_amdgcn_readfirstlane(nv);
   const size_t slot0 = static_cast<size_t>(h) * P * P + static_cast<size_t>(q) * P;   // slot of pair (q, 0)
   const float* Ls = p.LSE + slot0 * S + r0 + min(lane & 31, nv - 1);
-  const float* Os = p.O + (slot0 * S + r0) * D;
+  const __bf16* Os = p.O + (slot0 * S + r0) * D;
   float wk[KH];
 #pragma unroll
   for (int i = 0; i < KH; ++i) {
@@ -646,34 +654,43 @@ __device__ __attribute__((always_inline)) inline void merge_rows(const StepParam
   int crow[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) crow[j] = min((lane + 64 * j) / CPR, 31);
-  f32x4 acc[J];
+  f32x4 acc[J][2];
 #pragma unroll
-  for (int j = 0; j < J; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < J; ++j) acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int valid = nv * CPR;                      // chunks of the valid rows
   // Each state's rows are read through a buffer descriptor ending at the
   // last valid row: chunks past it read as zeros (never stored), so the
   // loads need no branches or clamps, and chunk j's offset is the lane's
   // offset plus a constant.  Cache policy 2: non-temporal.
-  auto load_state = [&](f32x4(&o)[J], int k) __attribute__((always_inline)) {
+  auto load_state = [&](u32x4(&o)[J], int k) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(Os + static_cast<size_t>(k) * S * D), 0, valid * 16, 0x00020000);
+        const_cast<__bf16*>(Os + static_cast<size_t>(k) * S * D), 0, valid * 16, 0x00020000);
 #pragma unroll
     for (int j = 0; j < J; ++j)
-      o[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + j * 1024, 0, 2));
+      o[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + j * 1024, 0, 2));
   };
-  auto accumulate = [&](const f32x4(&o)[J], float w, int b) __attribute__((always_inline)) {
+  // bf16 -> fp32 is exact: the pattern in the high half of a word.
+  auto accumulate = [&](const u32x4(&o)[J], float w, int b) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < J; ++j) acc[j] += __shfl(w, crow[j] + 32 * b) * o[j];
+    for (int j = 0; j < J; ++j) {
+      const float wt = __shfl(w, crow[j] + 32 * b);
+      const f32x4 lo = {__builtin_bit_cast(float, o[j].x << 16), __builtin_bit_cast(float, o[j].x & 0xffff0000u),
+                        __builtin_bit_cast(float, o[j].y << 16), __builtin_bit_cast(float, o[j].y & 0xffff0000u)};
+      const f32x4 hi = {__builtin_bit_cast(float, o[j].z << 16), __builtin_bit_cast(float, o[j].z & 0xffff0000u),
+                        __builtin_bit_cast(float, o[j].w << 16), __builtin_bit_cast(float, o[j].w & 0xffff0000u)};
+      acc[j][0] += wt * lo;
+      acc[j][1] += wt * hi;
+    }
   };
   // States 2i (half-wave 0's weights) and 2i + 1 (half-wave 1's) per
   // iteration, each state's loads issued one state ahead of its use; the
   // weights shift down one register per iteration so the current pair's
-  // are always wk[0].
-  f32x4 oa[J], ob[J];
+  // are always wk[0].  The scheduling barriers keep each load batch after
+  // the arithmetic that frees its registers, so the batch in flight stays in
+  // the same registers across the loop's back edge (no copy that would wait
+  // for it).
+  u32x4 oa[J], ob[J];
   load_state(oa, 0);
-  // The scheduling barriers keep each load batch after the arithmetic that
-  // frees its registers, so the batch in flight stays in the same registers
-  // across the loop's back edge (no copy that would wait for it).
 #pragma nounroll
   for (int i = 0; 2 * i < P; ++i) {
     load_state(ob, min(2 * i + 1, P - 1));       // P odd: the last pair's second state has weight 0
@@ -690,7 +707,10 @@ __device__ __attribute__((always_inline)) inline void merge_rows(const StepParam
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int c = lane + 64 * j;
-    if (c < valid) __builtin_nontemporal_store(acc[j], reinterpret_cast<f32x4*>(dst + 4 * c));
+    if (c < valid) {
+      __builtin_nontemporal_store(acc[j][0], reinterpret_cast<f32x4*>(dst + 8 * c));
+      __builtin_nontemporal_store(acc[j][1], reinterpret_cast<f32x4*>(dst + 8 * c + 4));
+    }
   }
   if (hw == 0 && lane < nv)
     p.LSEout[static_cast<size_t>(h) * p.N + static_cast<size_t>(q) * S + r0 + lane] =
@@ -733,6 +753,7 @@ void step_kernel(const StepParams p) {
   const size_t head = static_cast<size_t>(h) * p.N * D;
   const int wrow0 = qt * BR + wave * 32;          // this wave's first query row
   const int row0 = wrow0 + l32;                   // this lane's query row
+  const bool live = __builtin_amdgcn_readfirstlane(wrow0) < len_q;   // any row of the wave
   const int nf = p.nf[q];
 
   if (nf > 0) {
@@ -748,7 +769,7 @@ void step_kernel(const StepParams p) {
       const int len_k = min(p.S, p.N - k0);
       reset_state<D>(w);
       attend_keys<D, WAVES, false>(w, p.K + head, p.V + head, p.N, p.S, k0, len_k, len_k, k_lds0, k_lds1, v_lds0,
-                                   v_lds1, map, off, hw, p.scale_log2);
+                                   v_lds1, map, off, hw, p.scale_log2, live);
       const size_t slot = static_cast<size_t>(h) * p.P * p.P + static_cast<size_t>(q) * p.P + k;
       store_state<D>(w, p.O + slot * p.S * D, p.LSE + slot * p.S, row0, len_q, hw, l32);
     }

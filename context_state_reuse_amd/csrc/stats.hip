@@ -24,13 +24,14 @@ namespace ditango {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;        // drift kernel
 constexpr int kStatsThreads = 1024;  // stats kernel
 
 template <int D>
 __global__ __launch_bounds__(kStatsThreads) void stats_kernel(const StatsParams p) {
-  constexpr int C = D / 4;                  // 16-byte chunks per row
+  constexpr int C = D / 4;                  // chunks of 4 values per row (8 bytes of bf16)
   constexpr int RG = kStatsThreads / C;     // rows summed in parallel
   __shared__ f32x4 part[RG][C];
   __shared__ float wpart[kStatsThreads / 64];
@@ -62,11 +63,16 @@ __global__ __launch_bounds__(kStatsThreads) void stats_kernel(const StatsParams 
 
   // signature (block-uniform branch)
   if (!((p.sel[q] >> k) & 1u)) return;
-  const float* o = p.O + slot * p.S * D;
+  const __bf16* o = p.O + slot * p.S * D;
   const int rg = tid / C, c = tid % C;
   if (rg < RG) {
     // four independent accumulators: four loads in flight per thread
-    auto row = [&](int r) { return *reinterpret_cast<const f32x4*>(o + static_cast<size_t>(r) * D + 4 * c); };
+    // bf16 -> fp32 is exact: the pattern in the high half of a word
+    auto row = [&](int r) {
+      const u32x2 u = *reinterpret_cast<const u32x2*>(o + static_cast<size_t>(r) * D + 4 * c);
+      return f32x4{__builtin_bit_cast(float, u.x << 16), __builtin_bit_cast(float, u.x & 0xffff0000u),
+                   __builtin_bit_cast(float, u.y << 16), __builtin_bit_cast(float, u.y & 0xffff0000u)};
+    };
     f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0, a3 = a0;
     int r = rg;
     for (; r + 3 * RG < len_q; r += 4 * RG) {

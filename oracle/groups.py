@@ -49,10 +49,11 @@ def n_slots(P: int, g: int) -> int:
 
 
 def slot_bytes(H: int, N: int, P: int, d: int) -> int:
-    """Device bytes of one slot of the grouped cache: fp32 OUT [H][P][S][d]
-    plus LSE [H][P][S] (the layout the library allocates per slot)."""
+    """Device bytes of one slot of the grouped cache: OUT [H][P][S][d] kept
+    in bf16 (2 bytes) plus LSE [H][P][S] in fp32 (4 bytes), the layout the
+    library allocates per slot."""
     S = -(-N // P)
-    return 4 * H * P * S * (d + 1)
+    return H * P * S * (2 * d + 4)
 
 
 def merges_to_fit(P: int, g: int, k: int, bytes_per_slot: int, budget: int) -> int:

@@ -84,10 +84,12 @@ class StateReuseOracle:
                 "reused": (mask == 0).astype(np.uint8), "tc": self.tc.copy()}
 
 
-def run_workload(w, heads=None, rows=None, steps=None, masks=None, on_step=None):
+def run_workload(w, heads=None, rows=None, steps=None, masks=None, on_step=None, fp32_masters=False):
     """Run the oracle over the steps of workload w (synthetic inputs from synth).
 
     masks: optional {t: mask} overriding the workload's policy.
+    fp32_masters: feed the unrounded fp32 master tensors instead of their bf16
+    copies (for workloads specified in fp32).
     on_step(t, mask, result) is called after each step; returns the last result.
     """
     from synth import InputStream, bf16_bits_to_f64  # the shared seeded generator
@@ -100,8 +102,11 @@ def run_workload(w, heads=None, rows=None, steps=None, masks=None, on_step=None)
     for t in range(n_steps):
         qb, kb, vb = stream.next()
         mask = step_mask(w, t) if masks is None or t not in masks else masks[t]
-        inputs = {h: (bf16_bits_to_f64(qb[i]), bf16_bits_to_f64(kb[i]), bf16_bits_to_f64(vb[i]))
-                  for i, h in enumerate(heads)}
+        if fp32_masters:
+            inputs = {h: tuple(m[i].astype(np.float64) for m in stream.masters) for i, h in enumerate(heads)}
+        else:
+            inputs = {h: (bf16_bits_to_f64(qb[i]), bf16_bits_to_f64(kb[i]), bf16_bits_to_f64(vb[i]))
+                      for i, h in enumerate(heads)}
         res = orc.step(t, mask, inputs)
         if on_step is not None:
             on_step(t, mask, res)

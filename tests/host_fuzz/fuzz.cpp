@@ -37,6 +37,7 @@ static std::mt19937_64 rng(12345);
 static int ri(int a, int b) { return std::uniform_int_distribution<int>(a, b)(rng); }
 static float rf() { return std::uniform_real_distribution<float>(0.f, 1.f)(rng); }
 static float* fake(uintptr_t a) { return reinterpret_cast<float*>(a); }
+static ditango_bf16_t* fake16(uintptr_t a) { return reinterpret_cast<ditango_bf16_t*>(a); }
 
 static float wild() {   // finite, zero, inf, NaN, negative
   switch (ri(0, 9)) {
@@ -90,7 +91,7 @@ int main() {
     std::vector<int32_t> tc(40 * 40, 7);
     size_t ob = 0, lb = 0;
     ditango_states_bytes(&sh, &ob, &lb);
-    int rc = ditango_states_init(&st, &sh, fake(0x100000), fake(0x200000 + (ri(0, 20) ? 0 : 4)), tc.data());
+    int rc = ditango_states_init(&st, &sh, fake16(0x100000), fake(0x200000 + (ri(0, 20) ? 0 : 4)), tc.data());
     ++calls;
     if (rc) continue;
     int P = sh.P;
@@ -129,8 +130,9 @@ int main() {
     ditango_gstates_t st;
     std::memset(&st, 0, sizeof st);
     std::vector<int32_t> tc(40 * DITANGO_MAX_SLOTS, 9);
-    std::vector<float*> O(DITANGO_MAX_SLOTS), L(DITANGO_MAX_SLOTS);
-    for (int s = 0; s < DITANGO_MAX_SLOTS; ++s) { O[s] = fake(0x1000000 + 0x10000 * s); L[s] = fake(0x3000000 + 0x10000 * s); }
+    std::vector<ditango_bf16_t*> O(DITANGO_MAX_SLOTS);
+    std::vector<float*> L(DITANGO_MAX_SLOTS);
+    for (int s = 0; s < DITANGO_MAX_SLOTS; ++s) { O[s] = fake16(0x1000000 + 0x10000 * s); L[s] = fake(0x3000000 + 0x10000 * s); }
     int g = ri(0, 34);
     int rc = ditango_gstates_init(&st, &sh, g, O.data(), L.data(), tc.data());
     ++calls;

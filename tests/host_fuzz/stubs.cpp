@@ -56,6 +56,8 @@ hipError_t launch_step(StepParams& p, int rows, hipStream_t) {
 }
 hipError_t launch_merge(const MergeParams& m, hipStream_t) {
   REQUIRE(m.n_in >= 1 && m.n_in <= DITANGO_MAX_SLOTS);
+  REQUIRE((m.O != nullptr) != (m.Os != nullptr) && m.LSE);   // one output: fp32 rows or a bf16 group slot
+  REQUIRE(m.res_mode == 0 || (m.O && m.res));
   for (int q = 0; q < m.P; ++q) {
     REQUIRE(m.n_in == 32 || (m.live[q] >> m.n_in) == 0);
     for (int k = 0; k < m.n_in; ++k) if ((m.live[q] >> k) & 1u) REQUIRE(m.in_O[k] && m.in_L[k]);

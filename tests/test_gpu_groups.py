@@ -60,7 +60,7 @@ def _compare(w, g, masks=None, steps=None, compose_at=None, rows=None, heads=Non
         ns = cache.n_slots
         assert len(cache.O) == ns
         for s in range(ns):
-            Os, Ls = cache.O[s][hsel].cpu().numpy(), cache.LSE[s][hsel].cpu().numpy()
+            Os, Ls = cache.O[s][hsel].float().cpu().numpy(), cache.LSE[s][hsel].cpu().numpy()
             for hi, h in enumerate(heads):
                 for q in range(w.P):
                     if not slot_members(w.P, cache.g, q, s):

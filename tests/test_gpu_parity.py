@@ -10,8 +10,9 @@ three calls, and each step as one fused launch (ditango_step).
 
 Reduced workloads keep each workload's d, P, mask policy and value recipe at
 sizes the oracle finishes in seconds, with several key tiles, both query-tile
-widths and ragged last partitions; the full-size workloads are checked on
-sampled rows (first, last and interior rows of every partition) of two heads.
+widths and ragged last partitions; the full-size workloads run through the
+fused step launch (the benchmark's configuration) and are checked on sampled
+rows (first, last and interior rows of every partition) of two heads.
 """
 import numpy as np
 import pytest
@@ -69,7 +70,7 @@ def _run_full_compare(w, masks=None, label=None):
         assert np.array_equal(mask, omask), f"step {t}: mask differs from the oracle's"
         assert np.array_equal(reused, res["reused"]), f"step {t}: reused set differs"
         assert np.array_equal(cache.tc_matrix, res["tc"]), f"step {t}: t_c differs"
-        Oc, Lc = cache.O.cpu().numpy(), cache.LSE.cpu().numpy()
+        Oc, Lc = cache.O.float().cpu().numpy(), cache.LSE.cpu().numpy()
         P, S = w.P, w.S
         for h in range(w.H):
             for q in range(P):
@@ -125,6 +126,41 @@ def test_random_masks_each_step():
     _run_full_compare(w, masks=masks, label="churn")
 
 
+def test_tiny_fp32_masters_error():
+    """The tiny workload is specified in fp32; the library computes on bf16
+    copies of the inputs.  Error of the GPU output against the fp64 oracle
+    run on the unrounded fp32 masters, reported and bounded to first order:
+    rounding q and k to bf16 (relative error <= 2^-9 each) moves a score by
+    at most B = scale * 2^-8 * max_ij sum_c |q_ic k_jc|, so the LSE by at most
+    B and OUT by at most (2B + 2^-9) max|v|, on top of the bf16 parity bars."""
+    from synth import InputStream
+    w = synth.get("tiny")
+    scale = 1.0 / np.sqrt(w.d)
+    B, vmax = 0.0, 0.0
+    stream = InputStream(w)
+    for t in range(w.steps):
+        stream.advance()
+        q, k, v = (m.astype(np.float64) for m in stream.masters)
+        for h in range(w.H):
+            B = max(B, scale * 2.0 ** -8 * (np.abs(q[h]) @ np.abs(k[h]).T).max())
+            vmax = max(vmax, np.abs(v[h]).max())
+    ref = {}
+    run_workload(w, fp32_masters=True, on_step=lambda t, m, r: ref.__setitem__(t, r))
+    worst = [0.0, 0.0, 0.0]
+
+    def check(t, mask, reused, cache, O, LSE):
+        for h in range(w.H):
+            e = np.abs(O[h].cpu().numpy().astype(np.float64) - ref[t]["O"][h])
+            le = np.abs(LSE[h].cpu().numpy().astype(np.float64) - ref[t]["LSE"][h])
+            worst[:] = [max(worst[0], e.max()), max(worst[1], e.mean()), max(worst[2], le.max())]
+
+    run_steps(w, on_step=check, fused=True)
+    log(f"  tiny on fp32 masters: merged OUT max {worst[0]:.2e} mean {worst[1]:.2e}, LSE max {worst[2]:.2e} "
+        f"(first-order bounds: LSE {B + TOL_LSE:.2e}, OUT {(2 * B + 2.0 ** -9) * vmax + TOL_O_MAX:.2e})")
+    assert worst[2] <= B + TOL_LSE
+    assert worst[0] <= (2 * B + 2.0 ** -9) * vmax + TOL_O_MAX
+
+
 # ---------------------------------------------------------------- full size
 
 def _sample_rows(w, per_part=4, seed=0):
@@ -155,12 +191,12 @@ def test_full_size_sampled_rows(name):
         r_t = torch.tensor(rows, device="cuda")
         slots = torch.tensor(qidx[:, None] * P + np.arange(P)[None, :], device="cuda")  # [rows, P]
         i_t = torch.tensor(ridx, device="cuda")
-        so = cache.O[h_t[:, None, None], slots[None], i_t[None, :, None]].cpu().numpy()   # [2, rows, P, d]
+        so = cache.O[h_t[:, None, None], slots[None], i_t[None, :, None]].float().cpu().numpy()   # [2, rows, P, d]
         sl = cache.LSE[h_t[:, None, None], slots[None], i_t[None, :, None]].cpu().numpy()
         got[t] = dict(mask=mask.copy(), reused=reused.copy(), tc=cache.tc_matrix,
                       O=O[h_t][:, r_t].cpu().numpy(), LSE=LSE[h_t][:, r_t].cpu().numpy(), so=so, sl=sl)
 
-    run_steps(w, on_step=grab)
+    run_steps(w, on_step=grab, fused=True)           # the launch bench.py times
     prev = None
     worst = [0, 0, 0]
     ref_steps = {}

@@ -1,7 +1,8 @@
 """GPU parity on seeded random shapes and masks (both caches) against the
 fp64 oracles: head dims 64/72/128, 1 to 32 partitions, token counts that
 leave ragged and one-token partitions, several heads, per-step random masks
-including all-reuse steps; group sizes from 1 to P."""
+including all-reuse steps; group sizes from 1 to P.  The per-pair cache runs
+both as three calls per step and as the fused step launch."""
 import numpy as np
 import pytest
 
@@ -59,6 +60,7 @@ def test_random_shape_both_caches(w, masks, g):
                         f"{w.name} step {t} head {h}")
 
     run_steps(w, masks=masks, on_step=check, label=w.name)
+    run_steps(w, masks=masks, on_step=check, label=w.name, fused=True)
 
     from synth import InputStream, bf16_bits_to_f64
     orc = GroupedStateReuseOracle(w.N, w.P, w.d, g)

@@ -61,7 +61,7 @@ def test_slot_bytes():
     shape = lib.make_shape(w.H, w.N, w.d, w.P)
     ob, lb = ctypes.c_size_t(0), ctypes.c_size_t(0)
     tot = binding.lib.ditango_gstates_slot_bytes(ctypes.byref(shape), ctypes.byref(ob), ctypes.byref(lb))
-    assert ob.value == w.H * w.P * w.S * w.d * 4 and lb.value == w.H * w.P * w.S * 4
+    assert ob.value == w.H * w.P * w.S * w.d * 2 and lb.value == w.H * w.P * w.S * 4   # bf16 OUT, fp32 LSE
     assert tot == ob.value + lb.value
     # g = 4: 5 slots per query partition instead of 16 pair slots
     per_pair, _ = lib.ditango_states_bytes(shape)

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_struct_layout():
-    assert lib.ditango_version() == 4
+    assert lib.ditango_version() == 5
     assert ctypes.sizeof(binding.ditango_shape_t) == 20
     assert binding.ditango_states_t.O.offset == 24 and ctypes.sizeof(binding.ditango_states_t) == 48
 
@@ -43,11 +43,12 @@ def test_version_and_struct_layout():
 def test_states_bytes(name):
     w = synth.get(name)
     ob, lb = lib.ditango_states_bytes(lib.make_shape(w.H, w.N, w.d, w.P))
-    assert ob == w.H * w.P * w.P * w.S * w.d * 4
+    assert ob == w.H * w.P * w.P * w.S * w.d * 2       # bf16 OUT
     assert lb == w.H * w.P * w.P * w.S * 4
-    # a state holds d+1 floats per row, about half the 2*d of a KV pair per
-    # key before the fp32-versus-bf16 factor (attention-state section)
-    assert ob // (w.H * w.P * w.P * w.S) == 2 * (2 * w.d)
+    # a state's OUT row is d bf16 values: half the 2*d bf16 values of the K
+    # and V rows of a key (attention-state section: a state is about half the
+    # size of the KV it summarises)
+    assert ob // (w.H * w.P * w.P * w.S) == (2 * w.d * 2) // 2
 
 
 @pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
