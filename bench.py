@@ -314,7 +314,11 @@ def planner_run(args, w, lib, torch, dev):
                                f"target reuse {args.plan_reuse}, drift bound {args.plan_drift})",
                    "tokens": w.N, "heads": w.H, "head_dim": w.d, "partitions": w.P,
                    "reuse_ratio": round(1.0 - float(np.mean([m.mean() for m in masks])), 4),
-                   "parallelism": "none (all partitions on one GPU)"},
+                   "parallelism": "none (all partitions on one GPU)",
+                   **({"inputs": f"specified {w.dtype}: the library computes on bf16 copies of the {w.dtype} "
+                                 f"inputs (error against the fp64 oracle on the unrounded inputs: "
+                                 f"tests/test_gpu_parity.py::test_tiny_fp32_masters_error)"}
+                      if w.dtype != "bf16" else {})},
         "planner": {"anchor_steps": [i for i, a in enumerate(anchors) if a],
                     "reuse_selective_steps": round(1.0 - float(np.mean([masks[i].mean() for i in sel])), 4) if sel else None,
                     "ms_per_step_planned": round(ms_step, 4),
@@ -565,7 +569,11 @@ def main():
                    "cache_bytes": cache_bytes,
                    "fresh_pairs_per_step": float(np.mean([m.sum() for m in masks])),
                    **({"computed_slots_per_step": float(np.mean([c.sum() for c in computed_log]))} if g else {}),
-                   "parallelism": "none (all partitions on one GPU)"},
+                   "parallelism": "none (all partitions on one GPU)",
+                   **({"inputs": f"specified {w.dtype}: the library computes on bf16 copies of the {w.dtype} "
+                                 f"inputs (error against the fp64 oracle on the unrounded inputs: "
+                                 f"tests/test_gpu_parity.py::test_tiny_fp32_masters_error)"}
+                      if w.dtype != "bf16" else {})},
         "roofline": roof,
         "kernels": ({
             "step": {"ms": round(float(t_partial), 4), "tflops": round(partial_tflops, 2),
