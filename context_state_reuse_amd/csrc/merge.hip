@@ -19,8 +19,9 @@
 //      before the first is used -- and accumulates w_k * OUT_k in fp32
 //      registers (bf16 -> fp32 is exact);
 //   3. the R*d outputs are written contiguously.
-// R = 256 / PMAX keeps up to 32 independent loads in flight per thread; the
-// template chosen for a state count is in launch_d.  Each output element is written by the thread that read that
+// R = 256 / PMAX rows (times the passes of weight_passes) keep up to 32
+// independent loads in flight per thread; the template chosen for a state
+// count is in launch_d.  Each output element is written by the thread that read that
 // element of every input, after reading it, so an output may overwrite the
 // rows of one of its inputs (the in-place group merge).
 //
@@ -92,9 +93,23 @@ __device__ inline u32x4 pack8(f32x4 lo, f32x4 hi) {
 // indirection per state) instead of state indices 0 .. n_in with liveness
 // bits; chosen only when it lets a narrower template (fewer lanes per row)
 // serve the launch.
+// Rows per block: the weight pass covers kThreads / PMAX rows (one lane per
+// (row, state)); it runs RM times so that a state's rows give every thread
+// at least one 16-byte chunk to stream (bf16 rows of d = 64 are only 8
+// chunks).
+template <int D, int PMAX>
+constexpr int weight_passes() {
+  constexpr int R1 = kThreads / PMAX, CPR = D / 8;
+  return R1 * CPR >= kThreads ? 1 : kThreads / (R1 * CPR);
+}
+template <int D, int PMAX>
+constexpr int rows_per_block() { return kThreads / PMAX * weight_passes<D, PMAX>(); }
+
 template <int D, int PMAX, int RES, bool COMPACT>
 __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p, int row_tiles) {
-  constexpr int R = kThreads / PMAX;                  // rows per block
+  constexpr int R1 = kThreads / PMAX;                 // rows per weight pass
+  constexpr int RM = weight_passes<D, PMAX>();
+  constexpr int R = rows_per_block<D, PMAX>();        // rows per block
   constexpr int CPR = D / 8;                          // 16-byte bf16 chunks per row
   constexpr int CH = R * CPR;                         // chunks per state block
   constexpr int PER = (CH + kThreads - 1) / kThreads; // chunks per thread
@@ -117,8 +132,9 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p, in
   const int64_t out_row0 = h * p.out_hs + q * p.out_qs + i0;
 
   // 1. weights
-  {
-    const int r = tid / PMAX, k = tid % PMAX;
+#pragma unroll
+  for (int pass = 0; pass < RM; ++pass) {
+    const int r = pass * R1 + tid / PMAX, k = tid % PMAX;
     const bool lv = k < cnt && ((live >> k) & 1u) && r < rows;
     // Lanes without a state take -FLT_MAX and weight 0, so no infinity or
     // NaN arises even in rows past the end of the block's rows.
@@ -217,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p, in
 
 template <int D, int PMAX>
 hipError_t launch(const MergeParams& p, bool compact, hipStream_t stream) {
-  constexpr int R = kThreads / PMAX;
+  constexpr int R = rows_per_block<D, PMAX>();
   const int row_tiles = (p.S + R - 1) / R;
   const int64_t blocks = static_cast<int64_t>(p.H) * p.P * row_tiles;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
