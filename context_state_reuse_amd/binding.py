@@ -393,8 +393,9 @@ class Planner:
 class PlannedSteps:
     """Denoising steps with the planner choosing each step's mask, on one
     stream: the local pairs are computed first and their signatures' drift
-    since the last anchor measured; the planner picks the mask; the other
-    chosen pairs are computed, t_c updated and the states composed; the
+    since the last anchor measured; the planner picks the mask; t_c is
+    updated, then the other chosen pairs are computed and every row composed
+    in one fused launch; the
     signatures of the fresh pairs are refreshed, and at anchor steps the
     importance and every pair's drift against the cache before the step go
     to the planner.  Signature tables stay on the device; only P or P*P
@@ -439,10 +440,11 @@ class PlannedSteps:
         rest = mask.copy()
         if pl.n_anchors:
             rest[self.eye == 1] = 0
-        if rest.any():
-            ditango_attn_partial(Q, K, V, rest, c, stream)
+        # t_c first (host only), so the local pairs computed above count as
+        # cached; then the other chosen pairs and the composition of every row
+        # in one fused launch
         ditango_state_cache_update(c, mask, t)
-        ditango_state_merge(c, self.O, self.LSE, stream)
+        ditango_attn_partial_merge(Q, K, V, rest, c, self.O, self.LSE, stream)
         # signatures of the pairs computed after the plan (the local ones, when
         # already refreshed above, are not read again); the importance of every
         # pair at an anchor
