@@ -3,10 +3,11 @@
 One step = one denoising step of one attention layer through the whole hot
 path: build the step's selection mask, fresh partial attention for every
 COMPUTE pair (states written into the cache), cache metadata update, and the
-LSE-weighted merge of all P states per row.  With the per-pair cache the
-partial attention and the merge run as one fused launch (ditango_step);
---separate runs them as two launches (ditango_attn_partial, then
-ditango_state_merge) and times each.  Inputs of every step are
+LSE-weighted merge of all P states per row.  The partial attention and the
+merge run as one fused launch (ditango_step; with --group,
+ditango_group_attn_partial_merge); --separate runs them as two launches
+(ditango_attn_partial or ditango_group_attn_partial, then the merge) and
+times each.  Inputs of every step are
 resident in HBM before timing; the anchor step (all fresh) runs untimed first,
 then warm-up and timed steps cycle over the workload's steady-state steps
 t = 1 .. steps-1 with their masks.
@@ -56,7 +57,7 @@ def parse():
                     help="window attention with residual sharing: the anchor step computes every pair and caches "
                          "full-minus-window outputs; steady steps compute the window pairs (nearest partitions) only")
     ap.add_argument("--separate", action="store_true",
-                    help="per-pair cache: partial attention and merge as two launches instead of the fused step")
+                    help="partial attention and merge as two launches instead of the fused step (both caches)")
     ap.add_argument("--planner", action="store_true",
                     help="anchor-guided planner picks each step's mask (per-pair cache); extra measurement")
     ap.add_argument("--plan-steps", type=int, default=16, help="denoising steps of the planned run")
@@ -399,7 +400,7 @@ def main():
         mask_of = lambda t: lib.workload_mask(w, t)
         mask_desc = f"{w.policy}-{w.n_fresh}"
 
-    fused = not (g or wr or args.separate)
+    fused = not (wr or args.separate)
 
     def step(t: int, events=None):
         mask = mask_of(t)
@@ -407,7 +408,13 @@ def main():
         if events is not None:
             events[0].record()
         if fused:
-            lib.ditango_step(Q, K, V, mask, step_no[0], cache, O, LSE)
+            if g:
+                lib.ditango_group_attn_partial_merge(Q, K, V, mask, cache, O, LSE)
+                computed = lib.ditango_group_cache_update(cache, mask, step_no[0])
+                if events is not None:
+                    computed_log.append(computed)
+            else:
+                lib.ditango_step(Q, K, V, mask, step_no[0], cache, O, LSE)
             if events is not None:
                 events[1].record()
                 events[2].record()
@@ -526,13 +533,16 @@ def main():
                        "cache_bytes_before": before, "cache_bytes_after": cache.device_bytes}
 
     if fused:
-        roof = {"kernel": "step_kernel", "bound": "mfma", "achieved": round(partial_tflops, 2),
+        roof = {"kernel": "group_step_kernel" if g else "step_kernel", "bound": "mfma",
+                "achieved": round(partial_tflops, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(partial_tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": stored_traffic("step", w.name, src),
+                "traffic": None if g else stored_traffic("step", w.name, src),
                 "avg_launch_ms": round(float(t_partial), 4),
-                "algorithmic_per_launch": f"{fresh:.4e} FLOP (4*len_q*len_k*d per fresh pair and head); the same "
-                                          f"launch moves {mb + sb:.4e} B of states (P*(2d+4) read + (4d+4) "
-                                          f"written per row and head, 2d+4 per fresh pair row stored)"}
+                "algorithmic_per_launch": f"{fresh:.4e} FLOP (4*len_q*len_k*d per fresh "
+                                          f"{'slot, len_k = keys of its members' if g else 'pair'} and head); the "
+                                          f"same launch moves {mb + sb:.4e} B of states "
+                                          f"({'live slots' if g else 'P'}*(2d+4) read + (4d+4) written per row and "
+                                          f"head, 2d+4 per fresh {'slot' if g else 'pair'} row stored)"}
     elif t_partial >= t_merge:
         roof = {"kernel": "partial_kernel", "bound": "mfma", "achieved": round(partial_tflops, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(partial_tflops / PEAK_BF16_TFLOPS, 4),
@@ -580,7 +590,12 @@ def main():
                      "mfma_frac": round(partial_tflops / PEAK_BF16_TFLOPS, 4), "fresh_flop": fresh,
                      "state_bytes": float(mb + sb),
                      "gbs": round((mb + sb) / (t_partial * 1e-3) / 1e9, 1),
-                     "hbm_frac": round((mb + sb) / (t_partial * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+                     "hbm_frac": round((mb + sb) / (t_partial * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     # the fresh FLOP at the MFMA peak plus the state bytes at the HBM peak, over
+                     # the launch: the bound when a block's composition cannot overlap its own
+                     # matrix work (d = 128: a block fills its CU)
+                     "serial_bound_frac": round((fresh / (PEAK_BF16_TFLOPS * 1e12) + (mb + sb) / (PEAK_HBM_GBS * 1e9))
+                                                / (t_partial * 1e-3), 4)},
         } if fused else {
             "partial": {"ms": round(float(t_partial), 4), "tflops": round(partial_tflops, 2),
                         "mfma_frac": round(partial_tflops / PEAK_BF16_TFLOPS, 4), "fresh_flop": fresh,

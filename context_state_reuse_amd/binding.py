@@ -43,7 +43,8 @@ EXPORTED = ("ditango_states_bytes", "ditango_states_init", "ditango_attn_partial
             "ditango_state_cache_update", "ditango_state_merge", "ditango_mask_build",
             "ditango_last_error", "ditango_version",
             "ditango_group_slots", "ditango_gstates_slot_bytes", "ditango_gstates_init",
-            "ditango_group_attn_partial", "ditango_group_cache_update", "ditango_group_merge",
+            "ditango_group_attn_partial", "ditango_group_attn_partial_merge", "ditango_group_cache_update",
+            "ditango_group_merge",
             "ditango_group_compose", "ditango_group_fit", "ditango_group_reset", "ditango_group_mask_build",
             "ditango_window_residual_merge", "ditango_step", "ditango_attn_partial_merge",
             "ditango_pair_stats", "ditango_sig_drift",
@@ -121,6 +122,8 @@ def _load():
     lib.ditango_gstates_init.argtypes = [gst, ctypes.POINTER(ditango_shape_t), i32, ptab, ptab, vp]
     lib.ditango_group_attn_partial.restype = ctypes.c_int
     lib.ditango_group_attn_partial.argtypes = [vp, vp, vp, u8p, gst, vp]
+    lib.ditango_group_attn_partial_merge.restype = ctypes.c_int
+    lib.ditango_group_attn_partial_merge.argtypes = [vp, vp, vp, u8p, gst, vp, vp, vp]
     lib.ditango_group_cache_update.restype = ctypes.c_int
     lib.ditango_group_cache_update.argtypes = [gst, u8p, i32, u8p]
     lib.ditango_group_merge.restype = ctypes.c_int
@@ -640,6 +643,30 @@ def ditango_group_cache_update(cache: GroupedStateCache, mask, step: int) -> np.
     computed = np.zeros((cache.P, cache.n_slots), dtype=np.uint8)
     _check(lib.ditango_group_cache_update(ctypes.byref(cache.st), _u8(m), int(step), _u8(computed)))
     return computed
+
+
+def _group_out(cache, O, LSE):
+    import torch
+    dev = cache.O[0].device
+    if O is None:
+        O = torch.empty((cache.H, cache.N, cache.d), dtype=torch.float32, device=dev)
+    if LSE is None:
+        LSE = torch.empty((cache.H, cache.N), dtype=torch.float32, device=dev)
+    for t, shp, nm in ((O, (cache.H, cache.N, cache.d), "O"), (LSE, (cache.H, cache.N), "LSE")):
+        if not (t.is_cuda and t.dtype == torch.float32 and t.is_contiguous() and tuple(t.shape) == shp):
+            raise ValueError(f"{nm} must be a contiguous float32 device tensor of shape {shp}")
+    return O, LSE
+
+
+def ditango_group_attn_partial_merge(Q, K, V, mask, cache: GroupedStateCache, O=None, LSE=None, stream=None):
+    """Fresh states of the COMPUTE slots and the composition of every row in
+    one launch (t_c unchanged).  Returns (O, LSE)."""
+    m = _mask(mask, cache.P)
+    O, LSE = _group_out(cache, O, LSE)
+    _check(lib.ditango_group_attn_partial_merge(_qkv(Q, cache, "Q"), _qkv(K, cache, "K"), _qkv(V, cache, "V"), _u8(m),
+                                                ctypes.byref(cache.st), ctypes.c_void_p(O.data_ptr()),
+                                                ctypes.c_void_p(LSE.data_ptr()), _stream(stream)))
+    return O, LSE
 
 
 def ditango_group_merge(cache: GroupedStateCache, O=None, LSE=None, stream=None):

@@ -755,6 +755,62 @@ int ditango_group_attn_partial(const void* Q, const void* K, const void* V, cons
   return ok();
 }
 
+int ditango_group_attn_partial_merge(const void* Q, const void* K, const void* V, const uint8_t* mask,
+                                     ditango_gstates_t* st, float* O, float* LSE, void* stream) {
+  int ns = 0;
+  int rc = check_gstates(st, &ns);
+  if (rc) return rc;
+  const int P = st->shape.P, g = st->g;
+  if ((rc = check_mask(mask, P))) return rc;
+  if (!Q || !K || !V) return fail(DITANGO_EINVAL, "Q, K and V must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(Q) | reinterpret_cast<uintptr_t>(K) | reinterpret_cast<uintptr_t>(V)) & 15u)
+    return fail(DITANGO_EINVAL, "Q, K and V must be 16-byte aligned");
+  if (!O || !LSE) return fail(DITANGO_EINVAL, "O and LSE must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(O) | reinterpret_cast<uintptr_t>(LSE)) & 15u)
+    return fail(DITANGO_EINVAL, "O and LSE must be 16-byte aligned");
+  for (int q = 0; q < P; ++q)
+    for (int s = 0; s < ns; ++s)
+      if (slot_live(P, g, q, s) && !slot_fresh(mask, P, g, q, s) && gtc(st, q, s) < 0)
+        return fail(DITANGO_ENOCACHE, "slot (q=%d, s=%d) is REUSE but was never computed", q, s);
+
+  ditango::GroupStepParams p;
+  std::memset(&p, 0, sizeof p);
+  for (int q = 0; q < P; ++q) {
+    int nc = 0, nl = 0;
+    for (int s = 0; s < ns; ++s) {
+      if (!slot_live(P, g, q, s)) continue;
+      p.lslot[q][nl++] = static_cast<uint8_t>(s);
+      if (slot_fresh(mask, P, g, q, s)) p.cslot[q][nc++] = static_cast<uint8_t>(s);
+    }
+    p.nc[q] = static_cast<uint8_t>(nc);
+    p.nl[q] = static_cast<uint8_t>(nl);
+  }
+  p.Q = static_cast<const __bf16*>(Q);
+  p.K = static_cast<const __bf16*>(K);
+  p.V = static_cast<const __bf16*>(V);
+  for (int s = 0; s < ns; ++s) {
+    p.gO[s] = bf16_ptr(st->O[s]);
+    p.gLSE[s] = st->LSE[s];
+  }
+  p.Oout = O;
+  p.LSEout = LSE;
+  p.H = st->shape.H;
+  p.N = st->shape.N;
+  p.P = P;
+  p.S = st->S;
+  p.d = st->shape.d;
+  p.g = g;
+  p.scale_log2 = st->shape.scale * 1.4426950408889634f;
+  const int rows = ditango::partial_rows_per_block(p.d, p.S);
+  p.q_tiles = (p.S + rows - 1) / rows;
+  const int64_t blocks = static_cast<int64_t>(p.H) * P * p.q_tiles;
+  if (blocks > 0x7fffffff) return fail(DITANGO_EINVAL, "grid of %lld blocks is too large", (long long)blocks);
+  p.n_blocks = static_cast<int32_t>(blocks);
+  hipError_t e = ditango::launch_group_step(p, rows, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DITANGO_EHIP, "group step kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int ditango_group_cache_update(ditango_gstates_t* st, const uint8_t* mask, int32_t step, uint8_t* computed_out) {
   int ns = 0;
   int rc = check_gstates(st, &ns);

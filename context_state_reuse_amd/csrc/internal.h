@@ -60,6 +60,29 @@ struct StepParams {
   uint8_t fresh[DITANGO_MAX_P][DITANGO_MAX_P];
 };
 
+// Launch parameters of the fused step kernel of the grouped cache: one block
+// per (head, query partition q, query-row tile) computes the COMPUTE slots
+// cslot[q][0 .. nc[q]) one after the other (slot keys as in PartialParams'
+// grouped items), stores each state into its slot buffer, then composes the
+// live slots lslot[q][0 .. nl[q]) of its rows into O [H][N][d], LSE [H][N].
+struct GroupStepParams {
+  const __bf16* Q;          // [H][N][d]
+  const __bf16* K;
+  const __bf16* V;
+  __bf16* gO[DITANGO_MAX_SLOTS];   // slot buffers [H][P][S][d]
+  float* gLSE[DITANGO_MAX_SLOTS];  // [H][P][S]
+  float* Oout;              // [H][N][d]
+  float* LSEout;            // [H][N]
+  int32_t H, N, P, S, d, g;
+  float scale_log2;
+  int32_t q_tiles;          // query tiles per partition
+  int32_t n_blocks;         // H * P * q_tiles
+  uint8_t nc[DITANGO_MAX_P];
+  uint8_t cslot[DITANGO_MAX_P][DITANGO_MAX_SLOTS];
+  uint8_t nl[DITANGO_MAX_P];
+  uint8_t lslot[DITANGO_MAX_P][DITANGO_MAX_SLOTS];
+};
+
 // Composition (Eq. 4) of n_in states per row.  State k of the rows of
 // (head h, query partition q) starts at in_O[k] + (h*in_hs + q*in_qs)*S*d
 // (LSE: in_L[k] + (h*in_hs + q*in_qs)*S); it takes part when bit k of
@@ -131,6 +154,7 @@ int partial_rows_per_block(int d, int S);
 // Enqueue kernels; return hipSuccess or the launch error.
 hipError_t launch_partial(PartialParams& p, int rows_per_block, hipStream_t stream);
 hipError_t launch_step(StepParams& p, int rows_per_block, hipStream_t stream);
+hipError_t launch_group_step(GroupStepParams& p, int rows_per_block, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_stats(const StatsParams& p, hipStream_t stream);
 hipError_t launch_drift(const DriftParams& p, hipStream_t stream);

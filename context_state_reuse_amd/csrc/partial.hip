@@ -508,6 +508,31 @@ __device__ __attribute__((always_inline)) inline void store_state(const WaveStat
   }
 }
 
+// Keys of slot s of query partition q in the grouped cache: slot 0 is the
+// local partition q, slot 1 + j the member partitions [j g, min(j g + g, P))
+// of group j without q.  The concatenated key index j < len_k lives at token
+// k0 + j, or k0 + j + S once j >= len0 (a gap over q's partition when q sits
+// strictly inside the group; len0 = len_k otherwise).
+__device__ __attribute__((always_inline)) inline void group_keys(int N, int P, int S, int g, int q, int s, int& k0,
+                                                                 int& len_k, int& len0) {
+  const int a = s == 0 ? q : (s - 1) * g;                     // member partitions [a, bnd)
+  const int bnd = s == 0 ? q + 1 : min(a + g, P);
+  int kb = a * S, ke = min(bnd * S, N);
+  len0 = -1;
+  if (s != 0 && a <= q && q < bnd) {                          // the group holds q: leave it out
+    if (q == a) {
+      kb = (a + 1) * S;
+    } else if (q == bnd - 1) {
+      ke = q * S;
+    } else {
+      len0 = q * S - kb;                                      // q is interior, so its partition is full
+    }
+  }
+  k0 = kb;
+  len_k = ke - kb - (len0 >= 0 ? S : 0);
+  if (len0 < 0) len0 = len_k;
+}
+
 // XCD-aware block order: blocks are dealt round-robin to the 8 XCDs; remap
 // so each XCD runs a contiguous range of work items (items sharing K/V then
 // share its L2).
@@ -565,22 +590,7 @@ void partial_kernel(const PartialParams p) {
   } else {
     qp = it >> 6;
     const int s = it & 63;
-    const int a = s == 0 ? qp : (s - 1) * p.g;                 // member partitions [a, bnd)
-    const int bnd = s == 0 ? qp + 1 : min(a + p.g, p.P);
-    int kb = a * p.S, ke = min(bnd * p.S, p.N);
-    len0 = -1;
-    if (s != 0 && a <= qp && qp < bnd) {                        // the group holds q: leave it out
-      if (qp == a) {
-        kb = (a + 1) * p.S;
-      } else if (qp == bnd - 1) {
-        ke = qp * p.S;
-      } else {
-        len0 = qp * p.S - kb;                                   // q is interior, so its partition is full
-      }
-    }
-    k0 = kb;
-    len_k = ke - kb - (len0 >= 0 ? p.S : 0);
-    if (len0 < 0) len0 = len_k;
+    group_keys(p.N, p.P, p.S, p.g, qp, s, k0, len_k, len0);
     const size_t row0 = (static_cast<size_t>(h) * p.P + qp) * p.S;
     obase = p.gO[s] + row0 * D;
     lbase = p.gLSE[s] + row0;
@@ -605,45 +615,44 @@ void partial_kernel(const PartialParams p) {
   store_state<D>(w, obase, lbase, row0, len_q, hw, l32);
 }
 
-// Composition (Eq. 4) of the P pair states of this wave's rows r0 .. r0 +
-// nv - 1 of query partition q, head h, into the output: m = max_k LSE_k,
+// Composition (Eq. 4) of the n states of this wave's rows (nv <= 32 of
+// them) into the output rows at dst_o / dst_l: m = max_k LSE_k,
 // w_k = exp(LSE_k - m) / sum_k exp(LSE_k - m), OUT = sum_k w_k OUT_k,
-// LSE = m + log sum.  Lane l owns row l % 32 and the states k = 2i + l / 32,
-// so all P LSE loads of a row are in flight at once and the weights stay in
-// registers.  The rows' bf16 OUT values of a state are nv*d contiguous
-// elements, streamed in 16-byte chunks of 8 (chunk c = lane + 64 j holds
-// row c / (d/8)), non-temporal; a lane takes its chunk's weight from the
-// lane that owns the row and the state's parity.  The fresh states among
-// them were written by this wave (the caller has fenced those stores).
-template <int D>
-__device__ __attribute__((always_inline)) inline void merge_rows(const StepParams& p, int h, int q, int r0, int nv,
-                                                                 int lane) {
+// LSE = m + log sum.  so(k) / sl(k) give state k's OUT (bf16) and LSE at the
+// wave's first row, for a uniform k < n.  Lane l owns row l % 32 and the
+// states k = 2i + l / 32, so all n LSE loads of a row are in flight at once
+// and the weights stay in registers.  The rows' bf16 OUT values of a state
+// are nv*d contiguous elements, streamed in 16-byte chunks of 8 (chunk
+// c = lane + 64 j holds row c / (d/8)), non-temporal; a lane takes its
+// chunk's weight from the lane that owns the row and the state's parity.
+// Fresh states among them were written by this wave (the caller has fenced
+// those stores).
+template <int D, typename SO, typename SL>
+__device__ __attribute__((always_inline)) inline void merge_rows(int n, SO so, SL sl, float* dst_o, float* dst_l,
+                                                                 int nv, int lane) {
   constexpr int CPR = D / 8;                       // 16-byte chunks per row
   constexpr int J = (32 * CPR + 63) / 64;          // chunks per lane for 32 rows
-  constexpr int KH = DITANGO_MAX_P / 2;            // states per half-wave
+  constexpr int KH = DITANGO_MAX_SLOTS / 2;        // states per half-wave
   constexpr float kLog2e = 1.4426950408889634f;
-  const int P = p.P, S = p.S;
   const int hw = lane >> 5;
-  r0 = __builtin_amdgcn_readfirstlane(r0);         // uniform per wave: keeps the descriptors scalar
-  nv = __builtin_amdgcn_readfirstlane(nv);
-  const size_t slot0 = static_cast<size_t>(h) * P * P + static_cast<size_t>(q) * P;   // slot of pair (q, 0)
-  const float* Ls = p.LSE + slot0 * S + r0 + min(lane & 31, nv - 1);
-  const __bf16* Os = p.O + (slot0 * S + r0) * D;
+  const int rr = min(lane & 31, nv - 1);
   float wk[KH];
 #pragma unroll
   for (int i = 0; i < KH; ++i) {
     const int k = 2 * i + hw;
-    wk[i] = k < P ? Ls[static_cast<size_t>(k) * S] : 0.0f;
+    const float* la = sl(min(2 * i, n - 1));
+    const float* lb = sl(min(2 * i + 1, n - 1));
+    wk[i] = k < n ? (hw ? lb : la)[rr] : 0.0f;
   }
-  float m = hw < P ? wk[0] : kMaskScore;          // half-wave 0 always holds state 0
+  float m = hw < n ? wk[0] : kMaskScore;          // half-wave 0 always holds state 0
 #pragma unroll
   for (int i = 1; i < KH; ++i)
-    if (2 * i + hw < P) m = fmaxf(m, wk[i]);
+    if (2 * i + hw < n) m = fmaxf(m, wk[i]);
   m = fmaxf(m, xor32(m));
   float zh = 0.0f;
 #pragma unroll
   for (int i = 0; i < KH; ++i) {
-    wk[i] = 2 * i + hw < P ? __builtin_amdgcn_exp2f((wk[i] - m) * kLog2e) : 0.0f;
+    wk[i] = 2 * i + hw < n ? __builtin_amdgcn_exp2f((wk[i] - m) * kLog2e) : 0.0f;
     zh += wk[i];
   }
   const float z = zh + xor32(zh);
@@ -663,8 +672,8 @@ __device__ __attribute__((always_inline)) inline void merge_rows(const StepParam
   // loads need no branches or clamps, and chunk j's offset is the lane's
   // offset plus a constant.  Cache policy 2: non-temporal.
   auto load_state = [&](u32x4(&o)[J], int k) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<__bf16*>(Os + static_cast<size_t>(k) * S * D), 0, valid * 16, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(so(k)), 0, valid * 16, 0x00020000);
 #pragma unroll
     for (int j = 0; j < J; ++j)
       o[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + j * 1024, 0, 2));
@@ -692,29 +701,26 @@ __device__ __attribute__((always_inline)) inline void merge_rows(const StepParam
   u32x4 oa[J], ob[J];
   load_state(oa, 0);
 #pragma nounroll
-  for (int i = 0; 2 * i < P; ++i) {
-    load_state(ob, min(2 * i + 1, P - 1));       // P odd: the last pair's second state has weight 0
+  for (int i = 0; 2 * i < n; ++i) {
+    load_state(ob, min(2 * i + 1, n - 1));       // n odd: the last pair's second state has weight 0
     __builtin_amdgcn_sched_barrier(0);
     accumulate(oa, wk[0], 0);
     __builtin_amdgcn_sched_barrier(0);
-    load_state(oa, min(2 * i + 2, P - 1));
+    load_state(oa, min(2 * i + 2, n - 1));
     __builtin_amdgcn_sched_barrier(0);
     accumulate(ob, wk[0], 1);
 #pragma unroll
     for (int t = 0; t + 1 < KH; ++t) wk[t] = wk[t + 1];
   }
-  float* dst = p.Oout + (static_cast<size_t>(h) * p.N + static_cast<size_t>(q) * S + r0) * D;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int c = lane + 64 * j;
     if (c < valid) {
-      __builtin_nontemporal_store(acc[j][0], reinterpret_cast<f32x4*>(dst + 8 * c));
-      __builtin_nontemporal_store(acc[j][1], reinterpret_cast<f32x4*>(dst + 8 * c + 4));
+      __builtin_nontemporal_store(acc[j][0], reinterpret_cast<f32x4*>(dst_o + 8 * c));
+      __builtin_nontemporal_store(acc[j][1], reinterpret_cast<f32x4*>(dst_o + 8 * c + 4));
     }
   }
-  if (hw == 0 && lane < nv)
-    p.LSEout[static_cast<size_t>(h) * p.N + static_cast<size_t>(q) * S + r0 + lane] =
-        m + __builtin_amdgcn_logf(z) * 0.69314718055994531f;
+  if (hw == 0 && lane < nv) dst_l[lane] = m + __builtin_amdgcn_logf(z) * 0.69314718055994531f;
 }
 
 // The whole step of the per-pair cache for one (head, query partition,
@@ -776,8 +782,81 @@ void step_kernel(const StepParams p) {
     // the wave's state stores complete before it reads them back
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
   }
-  const int nv = min(32, len_q - wrow0);
-  if (nv > 0) merge_rows<D>(p, h, q, wrow0, nv, lane);
+  const int r0 = __builtin_amdgcn_readfirstlane(wrow0);   // uniform per wave: keeps the descriptors scalar
+  const int nv = min(32, len_q - r0);
+  if (nv > 0) {
+    const size_t slot0 = static_cast<size_t>(h) * p.P * p.P + static_cast<size_t>(q) * p.P;   // pair (q, 0)
+    const size_t out0 = static_cast<size_t>(h) * p.N + static_cast<size_t>(q0) + r0;
+    merge_rows<D>(
+        p.P, [&](int k) { return p.O + ((slot0 + k) * p.S + r0) * D; },
+        [&](int k) { return p.LSE + (slot0 + k) * p.S + r0; }, p.Oout + out0 * D, p.LSEout + out0, nv, lane);
+  }
+}
+
+// The step of the grouped cache for one (head, query partition, row tile):
+// the COMPUTE slots of q one after the other over the same query rows (each
+// over its members' keys, with the gap over q when q sits inside the
+// group), each state stored into its slot buffer; then each wave composes
+// its rows over q's live slots, as step_kernel does for the pair slots.
+template <int D, int WAVES>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
+                          amdgpu_waves_per_eu(waves_per_simd<D>(), waves_per_simd<D>())))
+void group_step_kernel(const GroupStepParams p) {
+  using G = Geometry<D>;
+  constexpr int kThreads = 64 * WAVES;
+  constexpr int BR = 32 * WAVES;
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds0[kTile * G::KS + G::kpad];
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds1[kTile * G::KS + G::kpad];
+  __shared__ __attribute__((aligned(16))) __bf16 v_lds0[kTile * G::VS];
+  __shared__ __attribute__((aligned(16))) __bf16 v_lds1[kTile * G::VS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hw = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int item = xcd_item(p.n_blocks);
+  const int qt = item % p.q_tiles;
+  const int rest = item / p.q_tiles;
+  const int q = rest % p.P;
+  const int h = rest / p.P;
+  const int q0 = q * p.S;
+  const int len_q = min(p.S, p.N - q0);
+  const size_t head = static_cast<size_t>(h) * p.N * D;
+  const size_t row_base = (static_cast<size_t>(h) * p.P + q) * p.S;   // row 0 of (h, q) in a slot buffer
+  const int wrow0 = qt * BR + wave * 32;
+  const int row0 = wrow0 + l32;
+  const bool live = __builtin_amdgcn_readfirstlane(wrow0) < len_q;
+  const int nc = p.nc[q];
+
+  if (nc > 0) {
+    WaveState<D> w;
+    load_q<D>(w, p.Q + head + static_cast<size_t>(q0) * D, row0, len_q, hw);
+    init_lds_pads<D, kThreads>(tid, k_lds0, k_lds1, v_lds0, v_lds1);
+    const TileLoadMap<D, WAVES> map(wave, lane);
+    const OperandOffsets<D> off(l32, hw, (lane & 15) >> 2, ((lane >> 4) & 1) * 16 + 4 * (lane & 3));
+    for (int i = 0; i < nc; ++i) {
+      if (i > 0) __syncthreads();   // every wave is done with the previous slot's tiles
+      const int s = p.cslot[q][i];
+      int k0, len_k, len0;
+      group_keys(p.N, p.P, p.S, p.g, q, s, k0, len_k, len0);
+      reset_state<D>(w);
+      attend_keys<D, WAVES, true>(w, p.K + head, p.V + head, p.N, p.S, k0, len_k, len0, k_lds0, k_lds1, v_lds0,
+                                  v_lds1, map, off, hw, p.scale_log2, live);
+      store_state<D>(w, p.gO[s] + row_base * D, p.gLSE[s] + row_base, row0, len_q, hw, l32);
+    }
+    // the wave's state stores complete before it reads them back
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+  }
+  const int r0 = __builtin_amdgcn_readfirstlane(wrow0);
+  const int nv = min(32, len_q - r0);
+  if (nv > 0) {
+    const size_t out0 = static_cast<size_t>(h) * p.N + static_cast<size_t>(q0) + r0;
+    merge_rows<D>(
+        p.nl[q], [&](int k) { return p.gO[p.lslot[q][k]] + (row_base + r0) * D; },
+        [&](int k) { return p.gLSE[p.lslot[q][k]] + row_base + r0; }, p.Oout + out0 * D, p.LSEout + out0, nv, lane);
+  }
 }
 
 template <int D, int WAVES>
@@ -793,6 +872,12 @@ hipError_t launch(PartialParams& p, hipStream_t stream) {
 template <int D, int WAVES>
 hipError_t launch_step_d(StepParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((step_kernel<D, WAVES>), dim3(p.n_blocks), dim3(64 * WAVES), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D, int WAVES>
+hipError_t launch_group_step_d(GroupStepParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((group_step_kernel<D, WAVES>), dim3(p.n_blocks), dim3(64 * WAVES), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -829,6 +914,17 @@ hipError_t launch_step(StepParams& p, int rows, hipStream_t stream) {
     case 72: return rows == 128 ? launch_step_d<72, 4>(p, stream) : hipErrorInvalidValue;
     case 128: return rows == 256 ? launch_step_d<128, 8>(p, stream) : rows == 128 ? launch_step_d<128, 4>(p, stream)
                                                                                   : hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_group_step(GroupStepParams& p, int rows, hipStream_t stream) {
+  switch (p.d) {
+    case 64: return rows == 128 ? launch_group_step_d<64, 4>(p, stream) : hipErrorInvalidValue;
+    case 72: return rows == 128 ? launch_group_step_d<72, 4>(p, stream) : hipErrorInvalidValue;
+    case 128: return rows == 256   ? launch_group_step_d<128, 8>(p, stream)
+                     : rows == 128 ? launch_group_step_d<128, 4>(p, stream)
+                                   : hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }

@@ -261,6 +261,19 @@ int ditango_gstates_init(ditango_gstates_t* st, const ditango_shape_t* shape, in
 int ditango_group_attn_partial(const void* Q, const void* K, const void* V, const uint8_t* mask,
                                ditango_gstates_t* st, void* stream);
 
+/* The fresh states of every COMPUTE slot and the composition (Eq. 4) of the
+ * non-empty slots of every row, in one launch: what
+ * ditango_group_attn_partial followed by ditango_group_merge computes (the
+ * same slot states; O and LSE equal up to the rounding order of the
+ * composition), without tc changes.  One block per (head, query partition,
+ * query-row tile) computes that row's COMPUTE slots one after the other and
+ * then composes its rows (ring-based composed attention of the DiTango page:
+ * states are composed as they are produced).  Every non-empty REUSE slot
+ * must hold a state, else DITANGO_ENOCACHE before any launch.  O and LSE as
+ * in ditango_group_merge.  Errors: EINVAL, ENOCACHE, EHIP. */
+int ditango_group_attn_partial_merge(const void* Q, const void* K, const void* V, const uint8_t* mask,
+                                     ditango_gstates_t* st, float* O, float* LSE, void* stream);
+
 /* Commit step `step` (host only): tc[q][s] = step for every COMPUTE slot.
  * If computed_out is not NULL it receives uint8 [P][ditango_group_slots(P, g)]
  * with 1 exactly at the COMPUTE slots (empty slots 0).  Errors: EINVAL (step

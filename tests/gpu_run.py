@@ -56,8 +56,13 @@ def run_steps(w, masks=None, steps=None, on_step=None, label="", fused=False):
     return cache
 
 
-def run_group_steps(w, g, masks=None, steps=None, compose_at=None, on_step=None, label="", budget_at=None):
+def run_group_steps(w, g, masks=None, steps=None, compose_at=None, on_step=None, label="", budget_at=None,
+                    fused=False):
     """Run the grouped-cache path of the library over the steps of workload w.
+
+    fused: the slots' fresh states and the composition in one launch
+    (ditango_group_attn_partial_merge), then the t_c update, instead of
+    partial, t_c update and merge one by one.
 
     compose_at: optional {t: k}: merge groups by k right before step t.
     budget_at: optional {t: bytes}: right before step t, merge groups by 2
@@ -82,15 +87,19 @@ def run_group_steps(w, g, masks=None, steps=None, compose_at=None, on_step=None,
             cache.compose(compose_at[t])
             log(f"  [{label or w.name}] before step {t}: groups merged to g={cache.g}, {cache.n_slots} slots")
         if budget_at and t in budget_at:
-            n = cache.fit(budget_at[t], 2)
-            log(f"  [{label or w.name}] before step {t}: budget {budget_at[t]} B, {n} merge(s), g={cache.g}, "
+            merges = cache.fit(budget_at[t], 2)
+            log(f"  [{label or w.name}] before step {t}: budget {budget_at[t]} B, {merges} merge(s), g={cache.g}, "
                 f"{cache.device_bytes} B")
         mask = lib.workload_mask(w, t) if masks is None or t not in masks else np.asarray(masks[t], np.uint8)
-        lib.ditango_group_attn_partial(Q, K, V, mask, cache)
-        computed = lib.ditango_group_cache_update(cache, mask, t)
-        lib.ditango_group_merge(cache, O, LSE)
+        if fused:
+            lib.ditango_group_attn_partial_merge(Q, K, V, mask, cache, O, LSE)
+            computed = lib.ditango_group_cache_update(cache, mask, t)
+        else:
+            lib.ditango_group_attn_partial(Q, K, V, mask, cache)
+            computed = lib.ditango_group_cache_update(cache, mask, t)
+            lib.ditango_group_merge(cache, O, LSE)
         torch.cuda.synchronize()
-        log(f"  [{label or w.name}] step {t}: g={cache.g}, {int(computed.sum())} slots computed, "
+        log(f"  [{label or w.name}{' fused' if fused else ''}] step {t}: g={cache.g}, {int(computed.sum())} slots computed, "
             f"{time.time() - t0:.1f}s")
         if on_step is not None:
             on_step(t, mask, computed, cache, O, LSE)

@@ -8,7 +8,7 @@
 #include <vector>
 #include "ditango.h"
 namespace ditango {
-extern long g_partial, g_merge, g_stats, g_drift, g_step;
+extern long g_partial, g_merge, g_stats, g_drift, g_step, g_gstep;
 extern int g_last_n, g_last_blocks, g_last_qtiles;
 extern uint16_t g_last_pairs[DITANGO_MAX_P * DITANGO_MAX_P];
 }
@@ -144,6 +144,9 @@ int main() {
       ++calls; oks += ditango_group_attn_partial(fake(0x300000), fake(0x400000), fake(0x500000), m.data(), &st, nullptr) == 0;
       ++calls; oks += ditango_group_cache_update(&st, m.data(), t, comp.data()) == 0;
       ++calls; oks += ditango_group_merge(&st, fake(0x600000), fake(0x700000), nullptr) == 0;
+      ++calls; oks += ditango_group_attn_partial_merge(fake(0x300000), fake(0x400000), ri(0, 20) ? fake(0x500000) : nullptr,
+                                                       m.data(), &st, fake(0x600000),
+                                                       ri(0, 20) ? fake(0x700000) : fake(0x700004), nullptr) == 0;
       if (ri(0, 3) == 0) { ++calls; oks += ditango_group_compose(&st, ri(0, 5), nullptr) == 0; }
       if (ri(0, 3) == 0) {
         const size_t sb = ditango_gstates_slot_bytes(&st.shape, nullptr, nullptr);
@@ -154,7 +157,8 @@ int main() {
       if (ri(0, 7) == 0) { ++calls; oks += ditango_group_reset(&st, O.data(), L.data()) == 0; }
     }
   }
-  printf("calls %ld ok %ld; launches step %ld partial %ld merge %ld stats %ld drift %ld\n", calls, oks, ditango::g_step, ditango::g_partial,
+  printf("calls %ld ok %ld; launches fused_step %ld group_step %ld partial %ld merge %ld stats %ld drift %ld\n", calls, oks,
+         ditango::g_step, ditango::g_gstep, ditango::g_partial,
          ditango::g_merge, ditango::g_stats, ditango::g_drift);
   return 0;
 }

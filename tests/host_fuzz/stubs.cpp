@@ -54,6 +54,29 @@ hipError_t launch_step(StepParams& p, int rows, hipStream_t) {
   REQUIRE(p.O && p.LSE && p.Oout && p.LSEout);
   ++g_step; return hipSuccess;
 }
+long g_gstep = 0;
+hipError_t launch_group_step(GroupStepParams& p, int rows, hipStream_t) {
+  REQUIRE(p.P >= 1 && p.P <= DITANGO_MAX_P && p.S >= 1 && p.N >= p.P && p.H >= 1 && p.g >= 1);
+  REQUIRE(rows == partial_rows_per_block(p.d, p.S));
+  REQUIRE(p.q_tiles == (p.S + rows - 1) / rows);
+  REQUIRE(static_cast<long long>(p.n_blocks) == static_cast<long long>(p.H) * p.P * p.q_tiles);
+  REQUIRE(static_cast<long long>(p.N) * p.d * 2 < (1LL << 31));
+  REQUIRE(p.Oout && p.LSEout);
+  for (int q = 0; q < p.P; ++q) {
+    REQUIRE(p.nl[q] >= 1 && p.nl[q] <= DITANGO_MAX_SLOTS && p.nc[q] <= p.nl[q]);
+    REQUIRE(p.lslot[q][0] == 0);                       // the local slot always takes part
+    for (int i = 0; i < p.nl[q]; ++i) {
+      REQUIRE(p.lslot[q][i] < DITANGO_MAX_SLOTS && p.gO[p.lslot[q][i]] && p.gLSE[p.lslot[q][i]]);
+      if (i) REQUIRE(p.lslot[q][i] > p.lslot[q][i - 1]);
+    }
+    for (int i = 0; i < p.nc[q]; ++i) {
+      bool listed = false;
+      for (int j = 0; j < p.nl[q]; ++j) listed = listed || p.lslot[q][j] == p.cslot[q][i];
+      REQUIRE(listed);                                 // a computed slot is a live one
+    }
+  }
+  ++g_gstep; return hipSuccess;
+}
 hipError_t launch_merge(const MergeParams& m, hipStream_t) {
   REQUIRE(m.n_in >= 1 && m.n_in <= DITANGO_MAX_SLOTS);
   REQUIRE((m.O != nullptr) != (m.Os != nullptr) && m.LSE);   // one output: fp32 rows or a bf16 group slot

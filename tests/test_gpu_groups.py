@@ -82,8 +82,10 @@ def _compare(w, g, masks=None, steps=None, compose_at=None, rows=None, heads=Non
             check_state(Oc[hi, rows_all], Lc[hi, rows_all], res["O"][h], res["LSE"][h],
                         f"{label} step {t} head {h} merged")
 
-    run_group_steps(w, g, masks=masks, steps=steps, compose_at=compose_at, on_step=check, label=label,
-                    budget_at=budget_at)
+    for fused in (False, True):       # two launches per step, then the fused group step launch
+        snap.clear()
+        run_group_steps(w, g, masks=masks, steps=steps, compose_at=compose_at, on_step=check, label=label,
+                        budget_at=budget_at, fused=fused)
     log(f"  {label}: worst slot state OUT max {worst[0]:.2e}, mean {worst[1]:.2e}, LSE {worst[2]:.2e}")
 
 

@@ -78,3 +78,4 @@ def test_random_shape_both_caches(w, masks, g):
                         f"{w.name} grouped g={g} step {t} head {h}")
 
     run_group_steps(w, g, masks=masks, on_step=gcheck, label=f"{w.name} g={g}")
+    run_group_steps(w, g, masks=masks, on_step=gcheck, label=f"{w.name} g={g}", fused=True)

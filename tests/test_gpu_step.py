@@ -81,3 +81,37 @@ def test_partial_merge_leaves_tc_and_checks_cache():
     torch.cuda.synchronize()
     assert torch.equal(O1, O2) and torch.equal(L1, L2)
     assert (cache.tc == 0).all()
+
+
+@pytest.mark.parametrize("name,g", [("stress_small", 4), ("image_small", 3), ("long_small", 4)])
+def test_group_fused_step_equals_two_launches(name, g):
+    """The grouped cache: ditango_group_attn_partial_merge against
+    ditango_group_attn_partial + ditango_group_merge -- slot states bit for
+    bit, the composed output within fp32 rounding of the weight sums."""
+    import torch
+    import context_state_reuse_amd as lib
+    w = {"image_small": lambda: synth.get("image").scaled(name="image_small", F=1, Hh=57, W=97, H=2),
+         "long_small": lambda: synth.get("long").scaled(name="long_small", F=7, Hh=19, W=23, H=2),
+         "stress_small": lambda: synth.get("stress").scaled(name="stress_small", F=5, Hh=16, W=27, H=3)}[name]()
+    a = lib.GroupedStateCache(w.H, w.N, w.d, w.P, g)
+    b = lib.GroupedStateCache(w.H, w.N, w.d, w.P, g)
+    stream = synth.InputStream(w)
+    for t in range(w.steps):
+        Q, K, V = (to_device(x) for x in stream.next())
+        mask = lib.workload_mask(w, t)
+        lib.ditango_group_attn_partial(Q, K, V, mask, a)
+        ca = lib.ditango_group_cache_update(a, mask, t)
+        Oa, La = lib.ditango_group_merge(a)
+        Ob, Lb = lib.ditango_group_attn_partial_merge(Q, K, V, mask, b)
+        cb = lib.ditango_group_cache_update(b, mask, t)
+        torch.cuda.synchronize()
+        assert np.array_equal(ca, cb) and np.array_equal(a.tc, b.tc)
+        rel = ((Oa - Ob).abs().max() / Oa.abs().max()).item()
+        assert rel <= REL_O, f"step {t}: fused output differs by {rel:.3g} of max |O|"
+        assert (La - Lb).abs().max().item() <= ABS_LSE * max(1.0, La.abs().max().item())
+        for s in range(a.n_slots):
+            for q in range(w.P):
+                if not lib.group_slot_live(w.P, g, q, s):
+                    continue
+                n = min(w.S, w.N - q * w.S)
+                assert torch.equal(a.O[s][:, q, :n], b.O[s][:, q, :n]) and torch.equal(a.LSE[s][:, q, :n], b.LSE[s][:, q, :n])

@@ -45,6 +45,7 @@ def test_host_logic_under_sanitizers(tmp_path):
     assert "runtime error" not in out and "AddressSanitizer" not in out, out[-4000:]
     # every launcher was reached, so the contracts were exercised
     fields = r.stdout.split()
-    launches = {fields[i]: int(fields[i + 1]) for i in range(len(fields) - 1) if fields[i] in ("partial", "merge", "stats", "drift")}
-    assert len(launches) == 4 and min(launches.values()) > 100, r.stdout
+    kinds = ("fused_step", "group_step", "partial", "merge", "stats", "drift")
+    launches = {fields[i]: int(fields[i + 1]) for i in range(len(fields) - 1) if fields[i] in kinds}
+    assert len(launches) == len(kinds) and min(launches.values()) > 100, r.stdout
     shutil.rmtree(tmp_path, ignore_errors=True)
