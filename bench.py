@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--window-residual", action="store_true",
                     help="window attention with residual sharing: the anchor step computes every pair and caches "
                          "full-minus-window outputs; steady steps compute the window pairs (nearest partitions) only")
+    ap.add_argument("--state-dtype", choices=("fp32", "bf16"), default="fp32",
+                    help="number format of the cached states' OUT (fp32: the default; bf16 halves the cache)")
     ap.add_argument("--separate", action="store_true",
                     help="partial attention and merge as two launches instead of the fused step (both caches)")
     ap.add_argument("--planner", action="store_true",
@@ -83,9 +85,9 @@ def token_reuse(w, fresh: float) -> float:
     return 1.0 - fresh / (4.0 * w.N * w.N * w.d * w.H)
 
 
-def state_row_bytes(d: int) -> int:
-    """One cached state row: d bf16 OUT values and an fp32 LSE."""
-    return 2 * d + 4
+def state_row_bytes(d: int, bf16: bool = False) -> int:
+    """One cached state row: d OUT values (fp32, or bf16) and an fp32 LSE."""
+    return (2 if bf16 else 4) * d + 4
 
 
 def out_row_bytes(d: int) -> int:
@@ -93,17 +95,17 @@ def out_row_bytes(d: int) -> int:
     return 4 * d + 4
 
 
-def merge_bytes(w) -> float:
+def merge_bytes(w, bf16: bool = False) -> float:
     """Per row and head: read P cached states, write one fp32 output row."""
-    return float(w.H * w.N * (w.P * state_row_bytes(w.d) + out_row_bytes(w.d)))
+    return float(w.H * w.N * (w.P * state_row_bytes(w.d, bf16) + out_row_bytes(w.d)))
 
 
-def state_store_bytes(w, mask) -> float:
+def state_store_bytes(w, mask, bf16: bool = False) -> float:
     lens = np.array([min(w.S, w.N - p * w.S) for p in range(w.P)], dtype=np.float64)
-    return float(w.H * state_row_bytes(w.d) * (lens[:, None] * mask).sum())
+    return float(w.H * state_row_bytes(w.d, bf16) * (lens[:, None] * mask).sum())
 
 
-def group_work(w, g, computed):
+def group_work(w, g, computed, bf16: bool = False):
     """Fresh FLOPs (4 * len_q * keys * d per computed slot and head) and
     merge bytes (the live slots' state rows read plus one output row written
     per row and head) of one grouped step."""
@@ -113,7 +115,8 @@ def group_work(w, g, computed):
     flops = sum(4.0 * w.d * w.H * lens[q] * group_slot_keys(w.N, w.P, g, q, s)
                 for q in range(w.P) for s in range(ns) if computed[q, s])
     live = [sum(1 for s in range(ns) if group_slot_live(w.P, g, q, s)) for q in range(w.P)]
-    mbytes = sum(float(w.H * lens[q] * (live[q] * state_row_bytes(w.d) + out_row_bytes(w.d))) for q in range(w.P))
+    mbytes = sum(float(w.H * lens[q] * (live[q] * state_row_bytes(w.d, bf16) + out_row_bytes(w.d)))
+                 for q in range(w.P))
     return flops, mbytes
 
 
@@ -275,12 +278,13 @@ def planner_run(args, w, lib, torch, dev):
     stream = synth.InputStream(w)
     qkv = [tuple(torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev) for b in stream.next())
            for _ in range(w.steps)]
-    cache = lib.StateCache(w.H, w.N, w.d, w.P)
+    sd = args.state_dtype
+    cache = lib.StateCache(w.H, w.N, w.d, w.P, state_dtype=sd)
     planner = lib.Planner(w.P, args.plan_group, w.H, args.plan_reuse, args.plan_drift)
     run = lib.PlannedSteps(cache, planner)
     dense = 4.0 * w.N * w.N * w.d * w.H
     # untimed: load every kernel once (first launches load code objects)
-    warm = lib.PlannedSteps(lib.StateCache(w.H, w.N, w.d, w.P),
+    warm = lib.PlannedSteps(lib.StateCache(w.H, w.N, w.d, w.P, state_dtype=sd),
                             lib.Planner(w.P, args.plan_group, w.H, args.plan_reuse, args.plan_drift))
     for t in range(3):
         warm.step(t, *qkv[t])
@@ -296,7 +300,7 @@ def planner_run(args, w, lib, torch, dev):
         anchors.append(anchor)
     # the same steps with the planner's masks through the plain step path:
     # the planner's own cost is the difference
-    cache2 = lib.StateCache(w.H, w.N, w.d, w.P)
+    cache2 = lib.StateCache(w.H, w.N, w.d, w.P, state_dtype=sd)
     torch.cuda.synchronize()
     ms_plain = []
     for t in range(w.steps):
@@ -356,6 +360,7 @@ def main():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(1)
     w = synth.get(args.workload)
+    bf16 = args.state_dtype == "bf16"
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     if args.planner:
@@ -371,10 +376,10 @@ def main():
     del stream
     g = args.group
     if g:
-        cache = lib.GroupedStateCache(w.H, w.N, w.d, w.P, g)
+        cache = lib.GroupedStateCache(w.H, w.N, w.d, w.P, g, state_dtype=args.state_dtype)
         cache_bytes = cache.device_bytes
     else:
-        cache = lib.StateCache(w.H, w.N, w.d, w.P)
+        cache = lib.StateCache(w.H, w.N, w.d, w.P, state_dtype=args.state_dtype)
         cache_bytes = sum(lib.ditango_states_bytes(cache.shape))
     O = torch.empty((w.H, w.N, w.d), dtype=torch.float32, device=dev)
     LSE = torch.empty((w.H, w.N), dtype=torch.float32, device=dev)
@@ -485,22 +490,22 @@ def main():
     dense = 4.0 * w.N * w.N * w.d * w.H
     value = dense / (ms_step * 1e-3) / 1e12
     if g:
-        work = [group_work(w, g, c) for c in computed_log]
+        work = [group_work(w, g, c, bf16) for c in computed_log]
         fresh = np.mean([f for f, _ in work])
         mb = np.mean([b for _, b in work])
         lens = np.array([min(w.S, w.N - p * w.S) for p in range(w.P)], dtype=np.float64)
-        sb = np.mean([w.H * (w.d + 1) * 4 * (lens[:, None] * c).sum() for c in computed_log])
+        sb = np.mean([w.H * state_row_bytes(w.d, bf16) * (lens[:, None] * c).sum() for c in computed_log])
         reuse = 1.0 - np.mean([c.sum() / sum(lib.group_slot_live(w.P, g, q, s) for q in range(w.P)
                                               for s in range(c.shape[1])) for c in computed_log])
     else:
         fresh = np.mean([fresh_flops(w, m) for m in masks])
         reuse = 1.0 - np.mean([m.mean() for m in masks])
-        mb = merge_bytes(w)
-        sb = np.mean([state_store_bytes(w, m) for m in masks])
+        mb = merge_bytes(w, bf16)
+        sb = np.mean([state_store_bytes(w, m, bf16) for m in masks])
         if wr:
             # window step: the window states and the residual read, one output written
             lens = np.array([min(w.S, w.N - p * w.S) for p in range(w.P)], dtype=np.float64)
-            mb = float(w.H * (lens * (wmask.sum(axis=1) * state_row_bytes(w.d) + 4 * w.d
+            mb = float(w.H * (lens * (wmask.sum(axis=1) * state_row_bytes(w.d, bf16) + 4 * w.d
                                       + out_row_bytes(w.d))).sum())
 
     partial_tflops = fresh / (t_partial * 1e-3) / 1e12
@@ -520,7 +525,7 @@ def main():
         for q in range(w.P):
             for i in range(m_new):
                 parts = sum(lib.group_slot_live(w.P, g, q, 1 + j) for j in range(k * i, min(k * i + k, m_old)))
-                cbytes += (parts + (1 if parts else 0)) * float(w.H * lens[q] * state_row_bytes(w.d))
+                cbytes += (parts + (1 if parts else 0)) * float(w.H * lens[q] * state_row_bytes(w.d, bf16))
         before = cache.device_bytes
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         torch.cuda.synchronize()
@@ -536,26 +541,26 @@ def main():
         roof = {"kernel": "group_step_kernel" if g else "step_kernel", "bound": "mfma",
                 "achieved": round(partial_tflops, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(partial_tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": None if g else stored_traffic("step", w.name, src),
+                "traffic": None if (g or bf16) else stored_traffic("step", w.name, src),
                 "avg_launch_ms": round(float(t_partial), 4),
                 "algorithmic_per_launch": f"{fresh:.4e} FLOP (4*len_q*len_k*d per fresh "
                                           f"{'slot, len_k = keys of its members' if g else 'pair'} and head); the "
                                           f"same launch moves {mb + sb:.4e} B of states "
-                                          f"({'live slots' if g else 'P'}*(2d+4) read + (4d+4) written per row and "
-                                          f"head, 2d+4 per fresh {'slot' if g else 'pair'} row stored)"}
+                                          f"({'live slots' if g else 'P'}*({2 if bf16 else 4}d+4) read + (4d+4) written per row and "
+                                          f"head, {2 if bf16 else 4}d+4 per fresh {'slot' if g else 'pair'} row stored)"}
     elif t_partial >= t_merge:
         roof = {"kernel": "partial_kernel", "bound": "mfma", "achieved": round(partial_tflops, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(partial_tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": None if (g or wr) else stored_traffic("partial", w.name, src),
+                "traffic": None if (g or wr or bf16) else stored_traffic("partial", w.name, src),
                 "avg_launch_ms": round(float(t_partial), 4),
                 "algorithmic_per_launch": f"{fresh:.4e} FLOP (4*len_q*len_k*d per fresh "
                                           f"{'slot, len_k = keys of its members' if g else 'pair'} and head)"}
     else:
         roof = {"kernel": "merge_kernel", "bound": "hbm", "achieved": round(merge_gbs, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(merge_gbs / PEAK_HBM_GBS, 4),
-                "traffic": None if (g or wr) else stored_traffic("merge", w.name, source_hash("merge.hip")),
+                "traffic": None if (g or wr or bf16) else stored_traffic("merge", w.name, source_hash("merge.hip")),
                 "avg_launch_ms": round(float(t_merge), 4),
-                "algorithmic_per_launch": f"{mb:.4e} B ({'live slots' if g else 'P'}*(2d+4) read + (4d+4) "
+                "algorithmic_per_launch": f"{mb:.4e} B ({'live slots' if g else 'P'}*({2 if bf16 else 4}d+4) read + (4d+4) "
                                           f"written per row and head)"}
 
     out = {
@@ -576,6 +581,7 @@ def main():
                    "partitions": w.P, "reuse_ratio": round(float(reuse), 4),
                    "reuse_ratio_tokens": round(token_reuse(w, float(fresh)), 4),
                    "state_cache": ("per pair, window states only, plus a residual [H][N][d]" if wr else cache_desc),
+                   "state_dtype": f"OUT {args.state_dtype}, LSE fp32",
                    "cache_bytes": cache_bytes,
                    "fresh_pairs_per_step": float(np.mean([m.sum() for m in masks])),
                    **({"computed_slots_per_step": float(np.mean([c.sum() for c in computed_log]))} if g else {}),

@@ -59,7 +59,11 @@ class DitangoError(RuntimeError):
 
 class ditango_shape_t(ctypes.Structure):
     _fields_ = [("H", ctypes.c_int32), ("N", ctypes.c_int32), ("d", ctypes.c_int32),
-                ("P", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("P", ctypes.c_int32), ("scale", ctypes.c_float), ("state_dtype", ctypes.c_int32)]
+
+
+DITANGO_STATE_F32, DITANGO_STATE_BF16 = 0, 1
+STATE_DTYPES = {"fp32": DITANGO_STATE_F32, "bf16": DITANGO_STATE_BF16}
 
 
 class ditango_states_t(ctypes.Structure):
@@ -195,8 +199,17 @@ def _torch_stream(stream):
     return stream
 
 
-def make_shape(H: int, N: int, d: int, P: int, scale: float | None = None) -> ditango_shape_t:
-    return ditango_shape_t(H, N, d, P, float(1.0 / np.sqrt(d) if scale is None else scale))
+def make_shape(H: int, N: int, d: int, P: int, scale: float | None = None, state_dtype: str = "fp32") -> ditango_shape_t:
+    """Layer shape; state_dtype "fp32" (default) or "bf16" is the number
+    format of the cached states' OUT."""
+    if state_dtype not in STATE_DTYPES:
+        raise ValueError(f"state_dtype must be one of {sorted(STATE_DTYPES)}")
+    return ditango_shape_t(H, N, d, P, float(1.0 / np.sqrt(d) if scale is None else scale), STATE_DTYPES[state_dtype])
+
+
+def _torch_state_dtype(shape: ditango_shape_t):
+    import torch
+    return torch.bfloat16 if shape.state_dtype == DITANGO_STATE_BF16 else torch.float32
 
 
 def ditango_states_bytes(shape: ditango_shape_t) -> tuple[int, int]:
@@ -207,16 +220,18 @@ def ditango_states_bytes(shape: ditango_shape_t) -> tuple[int, int]:
 
 
 class StateCache:
-    """The attention-state cache: device O (bfloat16) / LSE (float32) slots
-    (torch) and host t_c."""
+    """The attention-state cache: device O (float32, or bfloat16 with
+    state_dtype="bf16") / LSE (float32) slots (torch) and host t_c."""
 
-    def __init__(self, H: int, N: int, d: int, P: int, scale: float | None = None, device="cuda"):
+    def __init__(self, H: int, N: int, d: int, P: int, scale: float | None = None, device="cuda",
+                 state_dtype: str = "fp32"):
         import torch
-        self.shape = make_shape(H, N, d, P, scale)
+        self.shape = make_shape(H, N, d, P, scale, state_dtype)
         ob, lb = ditango_states_bytes(self.shape)
         S = -(-N // P)
-        assert ob == H * P * P * S * d * 2 and lb == H * P * P * S * 4
-        self.O = torch.empty((H, P * P, S, d), dtype=torch.bfloat16, device=device)
+        dt = _torch_state_dtype(self.shape)
+        assert ob == H * P * P * S * d * torch.tensor([], dtype=dt).element_size() and lb == H * P * P * S * 4
+        self.O = torch.empty((H, P * P, S, d), dtype=dt, device=device)
         self.LSE = torch.empty((H, P * P, S), dtype=torch.float32, device=device)
         self.tc = np.full(P * P, -1, dtype=np.int32)
         self.st = ditango_states_t()
@@ -552,8 +567,9 @@ class GroupedStateCache:
     returns to the allocator; ``reset`` re-creates them for an anchor step.
     """
 
-    def __init__(self, H: int, N: int, d: int, P: int, g: int, scale: float | None = None, device="cuda"):
-        self.shape = make_shape(H, N, d, P, scale)
+    def __init__(self, H: int, N: int, d: int, P: int, g: int, scale: float | None = None, device="cuda",
+                 state_dtype: str = "fp32"):
+        self.shape = make_shape(H, N, d, P, scale, state_dtype)
         self.H, self.N, self.d, self.P = H, N, d, P
         self.S = -(-N // P)
         self.device = device
@@ -571,7 +587,7 @@ class GroupedStateCache:
 
     def _slot_o(self):
         import torch
-        return torch.empty((self.H, self.P, self.S, self.d), dtype=torch.bfloat16, device=self.device)
+        return torch.empty((self.H, self.P, self.S, self.d), dtype=_torch_state_dtype(self.shape), device=self.device)
 
     def _slot_l(self):
         import torch

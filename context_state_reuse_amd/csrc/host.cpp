@@ -54,6 +54,8 @@ int check_shape(const ditango_shape_t* s, int32_t* S_out) {
   if (!(s->scale > 0.0f) || !std::isfinite(s->scale))
     return fail(DITANGO_EINVAL, "scale must be finite and > 0");
   if (s->N < s->P) return fail(DITANGO_EINVAL, "N=%d < P=%d leaves an empty partition", s->N, s->P);
+  if (s->state_dtype != DITANGO_STATE_F32 && s->state_dtype != DITANGO_STATE_BF16)
+    return fail(DITANGO_EINVAL, "state_dtype=%d is neither DITANGO_STATE_F32 nor DITANGO_STATE_BF16", s->state_dtype);
   // K/V of one head are addressed through buffer descriptors with 32-bit
   // byte offsets: N * d * 2 bytes must stay below 2^31.
   if (static_cast<int64_t>(s->N) * s->d >= (int64_t{1} << 30))
@@ -141,10 +143,14 @@ int64_t slot_keys(int N, int P, int S, int g, int q, int s) {
 
 int& gtc(const ditango_gstates_t* st, int q, int s) { return st->tc[q * DITANGO_MAX_SLOTS + s]; }
 
-// Cached OUT values are bf16; the C ABI carries them as their bit patterns.
-__bf16* bf16_ptr(ditango_bf16_t* p) { return reinterpret_cast<__bf16*>(p); }
+// Bytes of one cached OUT element, and the element offset of a slot block
+// as a byte pointer.
+size_t out_elem_bytes(const ditango_shape_t& s) { return s.state_dtype == DITANGO_STATE_BF16 ? 2 : 4; }
+const void* elem_offset(const void* base, size_t elems, const ditango_shape_t& s) {
+  return static_cast<const char*>(base) + elems * out_elem_bytes(s);
+}
 
-int check_slot_buffers(ditango_bf16_t* const* O, float* const* LSE, int n) {
+int check_slot_buffers(void* const* O, float* const* LSE, int n) {
   if (!O || !LSE) return fail(DITANGO_EINVAL, "slot buffer tables are NULL");
   for (int s = 0; s < n; ++s) {
     if (!O[s] || !LSE[s]) return fail(DITANGO_EINVAL, "slot %d buffers are NULL", s);
@@ -189,13 +195,13 @@ extern "C" {
 
 const char* ditango_last_error(void) { return g_err.c_str(); }
 
-int32_t ditango_version(void) { return 5; }
+int32_t ditango_version(void) { return 6; }
 
 size_t ditango_states_bytes(const ditango_shape_t* shape, size_t* o_bytes, size_t* lse_bytes) {
   int32_t S = 0;
   if (check_shape(shape, &S)) return 0;
   const size_t slots = static_cast<size_t>(shape->H) * shape->P * shape->P;
-  const size_t ob = slots * S * shape->d * sizeof(ditango_bf16_t);
+  const size_t ob = slots * S * shape->d * out_elem_bytes(*shape);
   const size_t lb = slots * S * sizeof(float);
   if (o_bytes) *o_bytes = ob;
   if (lse_bytes) *lse_bytes = lb;
@@ -203,7 +209,7 @@ size_t ditango_states_bytes(const ditango_shape_t* shape, size_t* o_bytes, size_
   return ob + lb;
 }
 
-int ditango_states_init(ditango_states_t* st, const ditango_shape_t* shape, ditango_bf16_t* O, float* LSE,
+int ditango_states_init(ditango_states_t* st, const ditango_shape_t* shape, void* O, float* LSE,
                         int32_t* tc) {
   if (!st) return fail(DITANGO_EINVAL, "states is NULL");
   int32_t S = 0;
@@ -247,7 +253,8 @@ int ditango_attn_partial(const void* Q, const void* K, const void* V, const uint
   p.Q = static_cast<const __bf16*>(Q);
   p.K = static_cast<const __bf16*>(K);
   p.V = static_cast<const __bf16*>(V);
-  p.O = bf16_ptr(st->O);
+  p.O = st->O;
+  p.state_bf16 = st->shape.state_dtype == DITANGO_STATE_BF16;
   p.LSE = st->LSE;
   p.H = st->shape.H;
   p.N = st->shape.N;
@@ -299,9 +306,10 @@ int ditango_state_merge(const ditango_states_t* st, float* O, float* LSE, void* 
   // State k of the rows of (h, q) is slot h*P*P + q*P + k.
   ditango::MergeParams m;
   std::memset(&m, 0, sizeof m);
+  m.state_bf16 = st->shape.state_dtype == DITANGO_STATE_BF16;
   const size_t slot_o = static_cast<size_t>(st->S) * st->shape.d;
   for (int k = 0; k < P; ++k) {
-    m.in_O[k] = bf16_ptr(st->O) + k * slot_o;
+    m.in_O[k] = elem_offset(st->O, k * slot_o, st->shape);
     m.in_L[k] = st->LSE + static_cast<size_t>(k) * st->S;
   }
   for (int q = 0; q < P; ++q) m.live[q] = P == 32 ? 0xffffffffu : (1u << P) - 1u;
@@ -337,7 +345,8 @@ int ditango_pair_stats(const ditango_states_t* st, const float* LSE, const uint8
     if (st->tc[i] < 0) return fail(DITANGO_ENOCACHE, "pair (q=%d, k=%d) holds no state", i / P, i % P);
   ditango::StatsParams sp;
   std::memset(&sp, 0, sizeof sp);
-  sp.O = bf16_ptr(st->O);
+  sp.O = st->O;
+  sp.state_bf16 = st->shape.state_dtype == DITANGO_STATE_BF16;
   sp.LSE_slot = st->LSE;
   sp.LSE = LSE;
   sp.W = W;
@@ -555,7 +564,8 @@ static int launch_fused_step(const void* Q, const void* K, const void* V, const 
   sp.Q = static_cast<const __bf16*>(Q);
   sp.K = static_cast<const __bf16*>(K);
   sp.V = static_cast<const __bf16*>(V);
-  sp.O = bf16_ptr(st->O);
+  sp.O = st->O;
+  sp.state_bf16 = st->shape.state_dtype == DITANGO_STATE_BF16;
   sp.LSE = st->LSE;
   sp.Oout = O;
   sp.LSEout = LSE;
@@ -632,6 +642,7 @@ int ditango_window_residual_merge(const ditango_states_t* st, const uint8_t* win
     return fail(DITANGO_EINVAL, "R, O and LSE must be 16-byte aligned");
   ditango::MergeParams m;
   std::memset(&m, 0, sizeof m);
+  m.state_bf16 = st->shape.state_dtype == DITANGO_STATE_BF16;
   for (int q = 0; q < P; ++q) {
     for (int k = 0; k < P; ++k)
       if (window[q * P + k]) m.wlive[q] |= 1u << k;
@@ -644,7 +655,7 @@ int ditango_window_residual_merge(const ditango_states_t* st, const uint8_t* win
         return fail(DITANGO_ENOCACHE, "pair (q=%d, k=%d) holds no state", q, k);
   const size_t slot_o = static_cast<size_t>(st->S) * st->shape.d;
   for (int k = 0; k < P; ++k) {
-    m.in_O[k] = bf16_ptr(st->O) + k * slot_o;
+    m.in_O[k] = elem_offset(st->O, k * slot_o, st->shape);
     m.in_L[k] = st->LSE + static_cast<size_t>(k) * st->S;
   }
   m.in_hs = static_cast<int64_t>(P) * P;
@@ -672,13 +683,13 @@ size_t ditango_gstates_slot_bytes(const ditango_shape_t* shape, size_t* o_bytes,
   int32_t S = 0;
   if (check_shape(shape, &S)) return 0;
   const size_t rows = static_cast<size_t>(shape->H) * shape->P * S;
-  if (o_bytes) *o_bytes = rows * shape->d * sizeof(ditango_bf16_t);
+  if (o_bytes) *o_bytes = rows * shape->d * out_elem_bytes(*shape);
   if (lse_bytes) *lse_bytes = rows * sizeof(float);
   ok();
-  return rows * (shape->d * sizeof(ditango_bf16_t) + sizeof(float));
+  return rows * (shape->d * out_elem_bytes(*shape) + sizeof(float));
 }
 
-int ditango_gstates_init(ditango_gstates_t* st, const ditango_shape_t* shape, int32_t g, ditango_bf16_t* const* O,
+int ditango_gstates_init(ditango_gstates_t* st, const ditango_shape_t* shape, int32_t g, void* const* O,
                          float* const* LSE, int32_t* tc) {
   if (!st) return fail(DITANGO_EINVAL, "states is NULL");
   int32_t S = 0;
@@ -741,8 +752,9 @@ int ditango_group_attn_partial(const void* Q, const void* K, const void* V, cons
   p.n_pairs = static_cast<int32_t>(items.size());
   p.grouped = 1;
   p.g = g;
+  p.state_bf16 = st->shape.state_dtype == DITANGO_STATE_BF16;
   for (int s = 0; s < ns; ++s) {
-    p.gO[s] = bf16_ptr(st->O[s]);
+    p.gO[s] = st->O[s];
     p.gLSE[s] = st->LSE[s];
   }
   const int rows = ditango::partial_rows_per_block(p.d, p.S);
@@ -789,7 +801,7 @@ int ditango_group_attn_partial_merge(const void* Q, const void* K, const void* V
   p.K = static_cast<const __bf16*>(K);
   p.V = static_cast<const __bf16*>(V);
   for (int s = 0; s < ns; ++s) {
-    p.gO[s] = bf16_ptr(st->O[s]);
+    p.gO[s] = st->O[s];
     p.gLSE[s] = st->LSE[s];
   }
   p.Oout = O;
@@ -800,6 +812,7 @@ int ditango_group_attn_partial_merge(const void* Q, const void* K, const void* V
   p.S = st->S;
   p.d = st->shape.d;
   p.g = g;
+  p.state_bf16 = st->shape.state_dtype == DITANGO_STATE_BF16;
   p.scale_log2 = st->shape.scale * 1.4426950408889634f;
   const int rows = ditango::partial_rows_per_block(p.d, p.S);
   p.q_tiles = (p.S + rows - 1) / rows;
@@ -846,6 +859,7 @@ int ditango_group_merge(const ditango_gstates_t* st, float* O, float* LSE, void*
   const int P = st->shape.P, g = st->g;
   ditango::MergeParams m;
   std::memset(&m, 0, sizeof m);
+  m.state_bf16 = st->shape.state_dtype == DITANGO_STATE_BF16;
   for (int q = 0; q < P; ++q)
     for (int s = 0; s < ns; ++s)
       if (slot_live(P, g, q, s)) {
@@ -853,7 +867,7 @@ int ditango_group_merge(const ditango_gstates_t* st, float* O, float* LSE, void*
         m.live[q] |= 1u << s;
       }
   for (int s = 0; s < ns; ++s) {
-    m.in_O[s] = bf16_ptr(st->O[s]);
+    m.in_O[s] = st->O[s];
     m.in_L[s] = st->LSE[s];
   }
   m.out_hs = st->shape.N;
@@ -887,9 +901,10 @@ int ditango_group_compose(ditango_gstates_t* st, int32_t k, void* stream) {
     const int j0 = k * i, j1 = std::min(k * i + k, m_old);
     ditango::MergeParams m;
     std::memset(&m, 0, sizeof m);
+    m.state_bf16 = st->shape.state_dtype == DITANGO_STATE_BF16;
     bool any = false;
     for (int j = j0; j < j1; ++j) {
-      m.in_O[j - j0] = bf16_ptr(st->O[1 + j]);
+      m.in_O[j - j0] = st->O[1 + j];
       m.in_L[j - j0] = st->LSE[1 + j];
     }
     for (int q = 0; q < P; ++q) {
@@ -905,7 +920,7 @@ int ditango_group_compose(ditango_gstates_t* st, int32_t k, void* stream) {
     if (!any) continue;
     m.out_hs = static_cast<int64_t>(P) * st->S;
     m.out_qs = st->S;
-    m.Os = bf16_ptr(st->O[1 + i]);
+    m.Os = st->O[1 + i];
     m.LSE = st->LSE[1 + i];
     hipError_t e = launch_group_merge(m, st, j1 - j0, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(DITANGO_EHIP, "group merge kernel launch: %s", hipGetErrorString(e));
@@ -946,7 +961,7 @@ int ditango_group_fit(ditango_gstates_t* st, size_t budget_bytes, int32_t k, voi
   return ok();
 }
 
-int ditango_group_reset(ditango_gstates_t* st, ditango_bf16_t* const* O, float* const* LSE) {
+int ditango_group_reset(ditango_gstates_t* st, void* const* O, float* const* LSE) {
   if (!st) return fail(DITANGO_EINVAL, "states is NULL");
   int32_t S = 0;
   int rc = check_shape(&st->shape, &S);

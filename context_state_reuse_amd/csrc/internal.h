@@ -24,16 +24,17 @@ struct PartialParams {
   const __bf16* Q;          // [H][N][d]
   const __bf16* K;          // [H][N][d]
   const __bf16* V;          // [H][N][d]
-  __bf16* O;                // per-pair cache [H][P*P][S][d]
+  void* O;                  // per-pair cache [H][P*P][S][d], fp32 or bf16 (state_bf16)
   float* LSE;               // per-pair cache [H][P*P][S]
   int32_t H, N, P, S, d;
+  int32_t state_bf16;       // cached OUT in bf16 (1) or fp32 (0)
   float scale_log2;         // scale * log2(e): scores in base-2 units
   int32_t n_pairs;          // work items in `pairs`
   int32_t q_tiles;          // query tiles per partition, ceil(S / rows per block)
   int32_t n_blocks;         // H * n_pairs * q_tiles
   int32_t grouped;          // 0: per-pair cache, 1: grouped cache
   int32_t g;                // group size (grouped)
-  __bf16* gO[DITANGO_MAX_SLOTS];   // grouped: slot buffers [H][P][S][d]
+  void* gO[DITANGO_MAX_SLOTS];     // grouped: slot buffers [H][P][S][d]
   float* gLSE[DITANGO_MAX_SLOTS];  // grouped: [H][P][S]
   uint16_t pairs[DITANGO_MAX_P * DITANGO_MAX_P];  // work items (see above)
 };
@@ -48,11 +49,12 @@ struct StepParams {
   const __bf16* Q;          // [H][N][d]
   const __bf16* K;
   const __bf16* V;
-  __bf16* O;                // per-pair cache [H][P*P][S][d]
+  void* O;                  // per-pair cache [H][P*P][S][d], fp32 or bf16 (state_bf16)
   float* LSE;               // per-pair cache [H][P*P][S]
   float* Oout;              // [H][N][d]
   float* LSEout;            // [H][N]
   int32_t H, N, P, S, d;
+  int32_t state_bf16;
   float scale_log2;
   int32_t q_tiles;          // query tiles per partition
   int32_t n_blocks;         // H * P * q_tiles
@@ -69,11 +71,12 @@ struct GroupStepParams {
   const __bf16* Q;          // [H][N][d]
   const __bf16* K;
   const __bf16* V;
-  __bf16* gO[DITANGO_MAX_SLOTS];   // slot buffers [H][P][S][d]
+  void* gO[DITANGO_MAX_SLOTS];     // slot buffers [H][P][S][d], fp32 or bf16 (state_bf16)
   float* gLSE[DITANGO_MAX_SLOTS];  // [H][P][S]
   float* Oout;              // [H][N][d]
   float* LSEout;            // [H][N]
   int32_t H, N, P, S, d, g;
+  int32_t state_bf16;
   float scale_log2;
   int32_t q_tiles;          // query tiles per partition
   int32_t n_blocks;         // H * P * q_tiles
@@ -96,7 +99,7 @@ struct GroupStepParams {
 // O): res_mode 1 also writes res = OUT - (composition of the states in
 // wlive[q]); res_mode 2 adds res to OUT.
 struct MergeParams {
-  const __bf16* in_O[DITANGO_MAX_SLOTS];
+  const void* in_O[DITANGO_MAX_SLOTS];  // fp32 or bf16 (state_bf16)
   const float* in_L[DITANGO_MAX_SLOTS];
   uint32_t live[DITANGO_MAX_P];
   uint32_t wlive[DITANGO_MAX_P];
@@ -109,10 +112,11 @@ struct MergeParams {
   int64_t in_hs, in_qs;     // in units of S rows
   int64_t out_hs, out_qs;   // in rows
   float* O;                 // fp32 output rows, or
-  __bf16* Os;               // bf16 output rows (a group slot) when not null
+  void* Os;                 // output rows in the states' format (a group slot) when not null
   float* LSE;
   float* res;
   int32_t res_mode;
+  int32_t state_bf16;       // the states (and Os) hold OUT in bf16 (1) or fp32 (0)
   int32_t n_in;             // <= DITANGO_MAX_SLOTS
   int32_t H, N, P, S, d;
 };
@@ -124,7 +128,8 @@ struct MergeParams {
 // W == nullptr: importance not wanted; the grid then covers the selected
 // pairs only, listed in pairs[0 .. n_pairs).
 struct StatsParams {
-  const __bf16* O;          // per-pair cache [H][P*P][S][d]
+  const void* O;            // per-pair cache [H][P*P][S][d], fp32 or bf16 (state_bf16)
+  int32_t state_bf16;
   const float* LSE_slot;    // [H][P*P][S]
   const float* LSE;         // merged [H][N]
   float* W;                 // [H][P][P] or nullptr

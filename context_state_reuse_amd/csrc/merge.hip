@@ -9,15 +9,16 @@
 // output is a group slot.  Where the states are and which take part come
 // from tables in the launch parameters.
 //
-// HBM-bound: per row and head it reads n states of d bf16 values and one
-// fp32 LSE each, and writes d fp32 values (bf16 for a group slot) and an
-// LSE.  A block owns R consecutive rows of one query partition of one head.
+// HBM-bound: per row and head it reads n states of d OUT values (fp32, or
+// bf16 when the cache keeps them so) and one fp32 LSE each, and writes d
+// fp32 values (a group slot: in the states' format) and an LSE.  A block
+// owns R consecutive rows of one query partition of one head.
 //   1. one lane per (row, state) loads LSE_k, the row's lanes reduce max and
 //      sum with cross-lane shuffles, and the normalised weights go to LDS;
-//   2. for every state k the block streams the R*d contiguous bf16 values of
-//      its rows in 16-byte chunks of 8 -- all states' loads are issued
-//      before the first is used -- and accumulates w_k * OUT_k in fp32
-//      registers (bf16 -> fp32 is exact);
+//   2. for every state k the block streams the R*d contiguous OUT values of
+//      its rows in 16-byte chunks -- all states' loads are issued before the
+//      first is used -- and accumulates w_k * OUT_k in fp32 registers
+//      (bf16 -> fp32 is exact);
 //   3. the R*d outputs are written contiguously.
 // R = 256 / PMAX rows (times the passes of weight_passes) keep up to 32
 // independent loads in flight per thread; the template chosen for a state
@@ -32,6 +33,8 @@
 // the cached res.
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "internal.h"
 
@@ -55,7 +58,7 @@ __device__ inline f32x4 load_stream(const float* p) {
   if constexpr (DITANGO_MERGE_NT) return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
   return *reinterpret_cast<const f32x4*>(p);
 }
-__device__ inline u32x4 load_stream(const __bf16* p) {
+__device__ inline u32x4 load_chunk(const void* p) {
   if constexpr (DITANGO_MERGE_NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return *reinterpret_cast<const u32x4*>(p);
 }
@@ -66,7 +69,7 @@ __device__ inline void store_stream(float* p, f32x4 v) {
     *reinterpret_cast<f32x4*>(p) = v;
   }
 }
-__device__ inline void store_stream(__bf16* p, u32x4 v) {
+__device__ inline void store_chunk(void* p, u32x4 v) {
   if constexpr (DITANGO_MERGE_NT) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
   } else {
@@ -97,20 +100,23 @@ __device__ inline u32x4 pack8(f32x4 lo, f32x4 hi) {
 // (row, state)); it runs RM times so that a state's rows give every thread
 // at least one 16-byte chunk to stream (bf16 rows of d = 64 are only 8
 // chunks).
-template <int D, int PMAX>
+template <int D, int PMAX, typename ST>
 constexpr int weight_passes() {
-  constexpr int R1 = kThreads / PMAX, CPR = D / 8;
+  constexpr int R1 = kThreads / PMAX, CPR = D / (16 / static_cast<int>(sizeof(ST)));
   return R1 * CPR >= kThreads ? 1 : kThreads / (R1 * CPR);
 }
-template <int D, int PMAX>
-constexpr int rows_per_block() { return kThreads / PMAX * weight_passes<D, PMAX>(); }
+template <int D, int PMAX, typename ST>
+constexpr int rows_per_block() { return kThreads / PMAX * weight_passes<D, PMAX, ST>(); }
 
-template <int D, int PMAX, int RES, bool COMPACT>
+template <int D, int PMAX, int RES, bool COMPACT, typename ST>
 __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p, int row_tiles) {
+  constexpr bool kBF = std::is_same<ST, __bf16>::value;
+  constexpr int EPC = 16 / sizeof(ST);                // OUT elements per 16-byte chunk
+  constexpr int NQ = EPC / 4;                         // fp32 quads per chunk
   constexpr int R1 = kThreads / PMAX;                 // rows per weight pass
-  constexpr int RM = weight_passes<D, PMAX>();
-  constexpr int R = rows_per_block<D, PMAX>();        // rows per block
-  constexpr int CPR = D / 8;                          // 16-byte bf16 chunks per row
+  constexpr int RM = weight_passes<D, PMAX, ST>();
+  constexpr int R = rows_per_block<D, PMAX, ST>();    // rows per block
+  constexpr int CPR = D / EPC;                        // 16-byte chunks per row
   constexpr int CH = R * CPR;                         // chunks per state block
   constexpr int PER = (CH + kThreads - 1) / kThreads; // chunks per thread
   __shared__ float w_lds[R][PMAX];
@@ -164,23 +170,27 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p, in
 
   // 2. stream the states
   const int valid = rows * CPR;
-  f32x4 acc[PER][2];
-  f32x4 racc[RES == 1 ? PER : 1][2];
+  f32x4 acc[PER][NQ];
+  f32x4 racc[RES == 1 ? PER : 1][NQ];
   u32x4 o[PMAX][PER];
 #pragma unroll
-  for (int j = 0; j < PER; ++j) acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < PER; ++j)
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) acc[j][u] = f32x4{0.f, 0.f, 0.f, 0.f};
   if constexpr (RES == 1) {
 #pragma unroll
-    for (int j = 0; j < PER; ++j) racc[j][0] = racc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < PER; ++j)
+#pragma unroll
+      for (int u = 0; u < NQ; ++u) racc[j][u] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int k = 0; k < PMAX; ++k) {
     if (k < cnt && ((live >> k) & 1u)) {
-      const __bf16* src = p.in_O[state(k)] + in_row0 * D;
+      const ST* src = static_cast<const ST*>(p.in_O[state(k)]) + in_row0 * D;
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         const int c = tid + j * kThreads;
-        if (c < valid) o[k][j] = load_stream(src + 8 * c);
+        if (c < valid) o[k][j] = load_chunk(src + EPC * c);
       }
     }
   }
@@ -191,15 +201,19 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p, in
       for (int j = 0; j < PER; ++j) {
         const int c = tid + j * kThreads;
         if (c < valid) {
-          f32x4 lo, hi;
-          unpack8(o[k][j], lo, hi);
+          f32x4 x[NQ];
+          if constexpr (kBF) {
+            unpack8(o[k][j], x[0], x[NQ - 1]);
+          } else {
+            x[0] = __builtin_bit_cast(f32x4, o[k][j]);
+          }
           const float wt = w_lds[c / CPR][k];
-          acc[j][0] += wt * lo;
-          acc[j][1] += wt * hi;
+#pragma unroll
+          for (int u = 0; u < NQ; ++u) acc[j][u] += wt * x[u];
           if constexpr (RES == 1) {
             const float wr = wr_lds[c / CPR][k];
-            racc[j][0] += wr * lo;
-            racc[j][1] += wr * hi;
+#pragma unroll
+            for (int u = 0; u < NQ; ++u) racc[j][u] += wr * x[u];
           }
         }
       }
@@ -213,43 +227,53 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p, in
     const int c = tid + j * kThreads;
     if (c < valid) {
       if constexpr (RES == 2) {
-        acc[j][0] += load_stream(rdst + 8 * c);
-        acc[j][1] += load_stream(rdst + 8 * c + 4);
+#pragma unroll
+        for (int u = 0; u < NQ; ++u) acc[j][u] += load_stream(rdst + EPC * c + 4 * u);
       }
-      if (p.Os) {                                      // block-uniform: a group slot
-        store_stream(p.Os + out_row0 * D + 8 * c, pack8(acc[j][0], acc[j][1]));
+      if (p.Os) {                                      // block-uniform: a group slot, in the states' format
+        ST* dst = static_cast<ST*>(p.Os) + out_row0 * D + EPC * c;
+        if constexpr (kBF) {
+          store_chunk(dst, pack8(acc[j][0], acc[j][NQ - 1]));
+        } else {
+          store_stream(reinterpret_cast<float*>(dst), acc[j][0]);
+        }
       } else {
         float* dst = p.O + out_row0 * D;
-        store_stream(dst + 8 * c, acc[j][0]);
-        store_stream(dst + 8 * c + 4, acc[j][1]);
+#pragma unroll
+        for (int u = 0; u < NQ; ++u) store_stream(dst + EPC * c + 4 * u, acc[j][u]);
       }
       if constexpr (RES == 1) {
-        store_stream(rdst + 8 * c, racc[j][0]);
-        store_stream(rdst + 8 * c + 4, racc[j][1]);
+#pragma unroll
+        for (int u = 0; u < NQ; ++u) store_stream(rdst + EPC * c + 4 * u, racc[j][u]);
       }
     }
   }
 }
 
-template <int D, int PMAX>
-hipError_t launch(const MergeParams& p, bool compact, hipStream_t stream) {
-  constexpr int R = rows_per_block<D, PMAX>();
+template <int D, int PMAX, typename ST>
+hipError_t launch_st(const MergeParams& p, bool compact, hipStream_t stream) {
+  constexpr int R = rows_per_block<D, PMAX, ST>();
   const int row_tiles = (p.S + R - 1) / R;
   const int64_t blocks = static_cast<int64_t>(p.H) * p.P * row_tiles;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
   if (p.res_mode == 1) {          // every state of a row takes part: never compacted
-    hipLaunchKernelGGL((merge_kernel<D, PMAX, 1, false>), grid, block, 0, stream, p, row_tiles);
+    hipLaunchKernelGGL((merge_kernel<D, PMAX, 1, false, ST>), grid, block, 0, stream, p, row_tiles);
   } else if (p.res_mode == 2) {
-    if (compact) hipLaunchKernelGGL((merge_kernel<D, PMAX, 2, true>), grid, block, 0, stream, p, row_tiles);
-    else hipLaunchKernelGGL((merge_kernel<D, PMAX, 2, false>), grid, block, 0, stream, p, row_tiles);
+    if (compact) hipLaunchKernelGGL((merge_kernel<D, PMAX, 2, true, ST>), grid, block, 0, stream, p, row_tiles);
+    else hipLaunchKernelGGL((merge_kernel<D, PMAX, 2, false, ST>), grid, block, 0, stream, p, row_tiles);
   } else if (p.res_mode == 0) {
-    if (compact) hipLaunchKernelGGL((merge_kernel<D, PMAX, 0, true>), grid, block, 0, stream, p, row_tiles);
-    else hipLaunchKernelGGL((merge_kernel<D, PMAX, 0, false>), grid, block, 0, stream, p, row_tiles);
+    if (compact) hipLaunchKernelGGL((merge_kernel<D, PMAX, 0, true, ST>), grid, block, 0, stream, p, row_tiles);
+    else hipLaunchKernelGGL((merge_kernel<D, PMAX, 0, false, ST>), grid, block, 0, stream, p, row_tiles);
   } else {
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int D, int PMAX>
+hipError_t launch(const MergeParams& p, bool compact, hipStream_t stream) {
+  return p.state_bf16 ? launch_st<D, PMAX, __bf16>(p, compact, stream) : launch_st<D, PMAX, float>(p, compact, stream);
 }
 
 // State-count template per head dim, from a sweep on MI355X (row merges and

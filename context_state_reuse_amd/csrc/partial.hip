@@ -18,10 +18,11 @@
 // O^T += V^T P^T (keys permuted inside each group of 16, which the V^T
 // operand reproduces).  V stays row-major in LDS and is read transposed with
 // ds_read_b64_tr_b16.  O^T accumulates in fp32 and P is rounded to bf16 for
-// the product.  Two row sums are kept: the fp32 sum of the unrounded
-// probabilities gives LSE, and the sum of the rounded ones (v_dot2c_f32_bf16,
-// or for d = 72 a ones column of V that makes it a row of O^T) normalises
-// OUT, so the weights applied to V sum to one as used.
+// the product.  The fp32 sum of the unrounded probabilities gives LSE and
+// normalises OUT; at d = 72, where O^T is padded to 96 rows anyway, a ones
+// column of V makes the sum of the rounded probabilities a row of O^T for
+// free, and OUT is normalised by that one (the weights applied to V then
+// sum to one as used).
 //
 // Softmax runs in base 2 with the scale folded into one FMA.  A tile's
 // probabilities are taken against the running max without first computing
@@ -144,7 +145,7 @@ struct WaveState {
   f32x16 oacc[G::vTiles];
   f32x16 sacc[2];
   bf16x8 pb[4];
-  float m_run, l_run, lr_run;
+  float m_run, l_run;
 };
 
 // S^T = K Q^T for the 64 keys of one LDS tile.
@@ -164,13 +165,11 @@ __device__ __attribute__((always_inline)) inline void tile_scores(WaveState<D>& 
 }
 
 // Probabilities exp2(s * scale * log2e - m) of the tile against the running
-// max m, as the bf16 P^T operand, with the lane's sums of the unrounded (tl)
-// and rounded (tlr) probabilities.
+// max m, as the bf16 P^T operand, with the lane's sum of the unrounded
+// probabilities (tl).
 template <int D>
-__device__ __attribute__((always_inline)) inline void tile_probs(WaveState<D>& w, float sl2, float& tl, float& tlr) {
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+__device__ __attribute__((always_inline)) inline void tile_probs(WaveState<D>& w, float sl2, float& tl) {
   tl = 0.0f;
-  tlr = 0.0f;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -183,7 +182,6 @@ __device__ __attribute__((always_inline)) inline void tile_probs(WaveState<D>& w
         const bf16x2 pr = {(__bf16)e0, (__bf16)e1};   // one v_cvt_pk_bf16_f32
         words[j / 2] = __builtin_bit_cast(uint32_t, pr);
         tl += e0 + e1;
-        if constexpr (!Geometry<D>::ones_row) tlr = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, tlr, false);
       }
       const u32x4 wv = {words[0], words[1], words[2], words[3]};
       w.pb[2 * kb + half] = __builtin_bit_cast(bf16x8, wv);
@@ -214,8 +212,8 @@ __device__ __attribute__((always_inline)) inline void tile_softmax(WaveState<D>&
       for (int i = 0; i < 16; ++i)
         if (kb * 32 + 8 * (i >> 2) + (i & 3) >= lim_l) w.sacc[kb][i] = kMaskScore;
   }
-  float tl, tlr;
-  tile_probs<D>(w, sl2, tl, tlr);
+  float tl;
+  tile_probs<D>(w, sl2, tl);
   // Sums are >= 0 (never NaN): an integer compare of the bits is true above
   // 2^64 and for +inf.
   if (__builtin_amdgcn_ballot_w64(__builtin_bit_cast(uint32_t, tl) > kSumLimitBits) != 0) {
@@ -230,13 +228,11 @@ __device__ __attribute__((always_inline)) inline void tile_softmax(WaveState<D>&
     const float alpha = __builtin_amdgcn_exp2f(w.m_run - m_new);   // 0 when the max was -inf
     w.m_run = m_new;
     w.l_run *= alpha;
-    w.lr_run *= alpha;
 #pragma unroll
     for (int v = 0; v < G::vTiles; ++v) w.oacc[v] *= alpha;
-    tile_probs<D>(w, sl2, tl, tlr);
+    tile_probs<D>(w, sl2, tl);
   }
   w.l_run += tl;
-  w.lr_run += tlr;
 }
 
 // O^T += V^T P^T for the tile whose V sits in `vl`.  Rows u*16 (+8) added
@@ -359,7 +355,6 @@ __device__ __attribute__((always_inline)) inline void reset_state(WaveState<D>& 
   for (int v = 0; v < G::vTiles; ++v) w.oacc[v] = f32x16{};
   w.m_run = -__builtin_inff();
   w.l_run = 0.0f;
-  w.lr_run = 0.0f;
 }
 
 // Attention of the block's query rows (Q^T in w.qf, state reset) over one
@@ -472,11 +467,13 @@ __device__ __attribute__((always_inline)) inline void attend_keys(
   }
 }
 
-// OUT = O / l_rounded (rounded to bf16), LSE = ln2 * (m + log2 l) of this
-// lane's query row `row` into a state's rows at obase / lbase (rows at or
-// past len_q are not stored).
-template <int D>
-__device__ __attribute__((always_inline)) inline void store_state(const WaveState<D>& w, __bf16* obase, float* lbase,
+// OUT = O / l, LSE = ln2 * (m + log2 l) of this lane's query row `row` into
+// a state's rows at obase / lbase (rows at or past len_q are not stored); OUT
+// in fp32, or rounded to bf16 when ST is __bf16.  l is the fp32 sum of the
+// unrounded probabilities, except at d = 72, where O^T's ones row gives the
+// sum of the rounded ones for free and normalises by it.
+template <int D, typename ST>
+__device__ __attribute__((always_inline)) inline void store_state(const WaveState<D>& w, ST* obase, float* lbase,
                                                                   int row, int len_q, int hw, int l32) {
   using G = Geometry<D>;
   const float l_tot = w.l_run + xor32(w.l_run);
@@ -487,21 +484,27 @@ __device__ __attribute__((always_inline)) inline void store_state(const WaveStat
     static_assert(D % 8 == 0, "ones row must start a 4-row group of half-wave 0");
     lr_tot = __shfl(w.oacc[D / 32][4 * ((D % 32) / 8)], l32);
   } else {
-    lr_tot = w.lr_run + xor32(w.lr_run);
+    lr_tot = l_tot;
   }
   const float inv = 1.0f / lr_tot;
   if (row < len_q) {
-    __bf16* orow = obase + static_cast<size_t>(row) * D;
+    ST* orow = obase + static_cast<size_t>(row) * D;
 #pragma unroll
     for (int v = 0; v < G::vTiles; ++v)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int dim = v * 32 + 8 * g + 4 * hw;
         if (dim < D) {
-          const bf16x2 lo = {(__bf16)(w.oacc[v][4 * g] * inv), (__bf16)(w.oacc[v][4 * g + 1] * inv)};
-          const bf16x2 hi = {(__bf16)(w.oacc[v][4 * g + 2] * inv), (__bf16)(w.oacc[v][4 * g + 3] * inv)};
-          const u32x2 o = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-          *reinterpret_cast<u32x2*>(orow + dim) = o;
+          if constexpr (std::is_same<ST, __bf16>::value) {
+            const bf16x2 lo = {(__bf16)(w.oacc[v][4 * g] * inv), (__bf16)(w.oacc[v][4 * g + 1] * inv)};
+            const bf16x2 hi = {(__bf16)(w.oacc[v][4 * g + 2] * inv), (__bf16)(w.oacc[v][4 * g + 3] * inv)};
+            const u32x2 o = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+            *reinterpret_cast<u32x2*>(orow + dim) = o;
+          } else {
+            const f32x4 o = {w.oacc[v][4 * g] * inv, w.oacc[v][4 * g + 1] * inv, w.oacc[v][4 * g + 2] * inv,
+                             w.oacc[v][4 * g + 3] * inv};
+            *reinterpret_cast<f32x4*>(orow + dim) = o;
+          }
         }
       }
     if (hw == 0) lbase[row] = (w.m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
@@ -543,7 +546,7 @@ __device__ __attribute__((always_inline)) inline int xcd_item(int nb) {
   return xcd * per + (xcd < rem ? xcd : rem) + (b >> 3);
 }
 
-template <int D, int WAVES, bool GROUPED>
+template <int D, int WAVES, bool GROUPED, typename ST>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
                           amdgpu_waves_per_eu(waves_per_simd<D>(), waves_per_simd<D>())))
 void partial_kernel(const PartialParams p) {
@@ -576,7 +579,7 @@ void partial_kernel(const PartialParams p) {
   // partition q at concatenated index len0 when it sits strictly inside a
   // group (len0 = len_k otherwise).
   int qp, k0, len_k, len0;
-  __bf16* obase;  // OUT row 0 of this item's state
+  ST* obase;      // OUT row 0 of this item's state
   float* lbase;   // LSE row 0
   if constexpr (!GROUPED) {
     qp = it / p.P;
@@ -585,14 +588,14 @@ void partial_kernel(const PartialParams p) {
     len_k = min(p.S, p.N - k0);
     len0 = len_k;
     const size_t slot = static_cast<size_t>(h) * p.P * p.P + it;
-    obase = p.O + slot * p.S * D;
+    obase = static_cast<ST*>(p.O) + slot * p.S * D;
     lbase = p.LSE + slot * p.S;
   } else {
     qp = it >> 6;
     const int s = it & 63;
     group_keys(p.N, p.P, p.S, p.g, qp, s, k0, len_k, len0);
     const size_t row0 = (static_cast<size_t>(h) * p.P + qp) * p.S;
-    obase = p.gO[s] + row0 * D;
+    obase = static_cast<ST*>(p.gO[s]) + row0 * D;
     lbase = p.gLSE[s] + row0;
   }
   const int q0 = qp * p.S;
@@ -612,25 +615,28 @@ void partial_kernel(const PartialParams p) {
   const OperandOffsets<D> off(l32, hw, (lane & 15) >> 2, ((lane >> 4) & 1) * 16 + 4 * (lane & 3));
   attend_keys<D, WAVES, GROUPED>(w, p.K + head, p.V + head, p.N, p.S, k0, len_k, len0, k_lds0, k_lds1, v_lds0,
                                  v_lds1, map, off, hw, p.scale_log2, live);
-  store_state<D>(w, obase, lbase, row0, len_q, hw, l32);
+  store_state<D, ST>(w, obase, lbase, row0, len_q, hw, l32);
 }
 
 // Composition (Eq. 4) of the n states of this wave's rows (nv <= 32 of
 // them) into the output rows at dst_o / dst_l: m = max_k LSE_k,
 // w_k = exp(LSE_k - m) / sum_k exp(LSE_k - m), OUT = sum_k w_k OUT_k,
-// LSE = m + log sum.  so(k) / sl(k) give state k's OUT (bf16) and LSE at the
-// wave's first row, for a uniform k < n.  Lane l owns row l % 32 and the
-// states k = 2i + l / 32, so all n LSE loads of a row are in flight at once
-// and the weights stay in registers.  The rows' bf16 OUT values of a state
-// are nv*d contiguous elements, streamed in 16-byte chunks of 8 (chunk
-// c = lane + 64 j holds row c / (d/8)), non-temporal; a lane takes its
-// chunk's weight from the lane that owns the row and the state's parity.
-// Fresh states among them were written by this wave (the caller has fenced
-// those stores).
-template <int D, typename SO, typename SL>
+// LSE = m + log sum.  so(k) / sl(k) give state k's OUT (ST: fp32 or bf16)
+// and LSE at the wave's first row, for a uniform k < n.  Lane l owns row
+// l % 32 and the states k = 2i + l / 32, so all n LSE loads of a row are in
+// flight at once and the weights stay in registers.  The rows' OUT values of
+// a state are nv*d contiguous elements, streamed in 16-byte chunks (4 fp32
+// or 8 bf16; chunk c = lane + 64 j holds row c / (d / chunk)),
+// non-temporal; a lane takes its chunk's weight from the lane that owns the
+// row and the state's parity.  Fresh states among them were written by
+// this wave (the caller has fenced those stores).
+template <int D, typename ST, typename SO, typename SL>
 __device__ __attribute__((always_inline)) inline void merge_rows(int n, SO so, SL sl, float* dst_o, float* dst_l,
                                                                  int nv, int lane) {
-  constexpr int CPR = D / 8;                       // 16-byte chunks per row
+  constexpr bool kBF = std::is_same<ST, __bf16>::value;
+  constexpr int EPC = 16 / sizeof(ST);             // elements per 16-byte chunk
+  constexpr int NQ = EPC / 4;                      // fp32 quads per chunk
+  constexpr int CPR = D / EPC;                     // 16-byte chunks per row
   constexpr int J = (32 * CPR + 63) / 64;          // chunks per lane for 32 rows
   constexpr int KH = DITANGO_MAX_SLOTS / 2;        // states per half-wave
   constexpr float kLog2e = 1.4426950408889634f;
@@ -663,9 +669,11 @@ __device__ __attribute__((always_inline)) inline void merge_rows(int n, SO so, S
   int crow[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) crow[j] = min((lane + 64 * j) / CPR, 31);
-  f32x4 acc[J][2];
+  f32x4 acc[J][NQ];
 #pragma unroll
-  for (int j = 0; j < J; ++j) acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) acc[j][u] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int valid = nv * CPR;                      // chunks of the valid rows
   // Each state's rows are read through a buffer descriptor ending at the
   // last valid row: chunks past it read as zeros (never stored), so the
@@ -673,7 +681,7 @@ __device__ __attribute__((always_inline)) inline void merge_rows(int n, SO so, S
   // offset plus a constant.  Cache policy 2: non-temporal.
   auto load_state = [&](u32x4(&o)[J], int k) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(so(k)), 0, valid * 16, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<ST*>(so(k)), 0, valid * 16, 0x00020000);
 #pragma unroll
     for (int j = 0; j < J; ++j)
       o[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + j * 1024, 0, 2));
@@ -683,12 +691,16 @@ __device__ __attribute__((always_inline)) inline void merge_rows(int n, SO so, S
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const float wt = __shfl(w, crow[j] + 32 * b);
-      const f32x4 lo = {__builtin_bit_cast(float, o[j].x << 16), __builtin_bit_cast(float, o[j].x & 0xffff0000u),
-                        __builtin_bit_cast(float, o[j].y << 16), __builtin_bit_cast(float, o[j].y & 0xffff0000u)};
-      const f32x4 hi = {__builtin_bit_cast(float, o[j].z << 16), __builtin_bit_cast(float, o[j].z & 0xffff0000u),
-                        __builtin_bit_cast(float, o[j].w << 16), __builtin_bit_cast(float, o[j].w & 0xffff0000u)};
-      acc[j][0] += wt * lo;
-      acc[j][1] += wt * hi;
+      if constexpr (kBF) {
+        const f32x4 lo = {__builtin_bit_cast(float, o[j].x << 16), __builtin_bit_cast(float, o[j].x & 0xffff0000u),
+                          __builtin_bit_cast(float, o[j].y << 16), __builtin_bit_cast(float, o[j].y & 0xffff0000u)};
+        const f32x4 hi = {__builtin_bit_cast(float, o[j].z << 16), __builtin_bit_cast(float, o[j].z & 0xffff0000u),
+                          __builtin_bit_cast(float, o[j].w << 16), __builtin_bit_cast(float, o[j].w & 0xffff0000u)};
+        acc[j][0] += wt * lo;
+        acc[j][NQ - 1] += wt * hi;
+      } else {
+        acc[j][0] += wt * __builtin_bit_cast(f32x4, o[j]);
+      }
     }
   };
   // States 2i (half-wave 0's weights) and 2i + 1 (half-wave 1's) per
@@ -716,8 +728,8 @@ __device__ __attribute__((always_inline)) inline void merge_rows(int n, SO so, S
   for (int j = 0; j < J; ++j) {
     const int c = lane + 64 * j;
     if (c < valid) {
-      __builtin_nontemporal_store(acc[j][0], reinterpret_cast<f32x4*>(dst_o + 8 * c));
-      __builtin_nontemporal_store(acc[j][1], reinterpret_cast<f32x4*>(dst_o + 8 * c + 4));
+#pragma unroll
+      for (int u = 0; u < NQ; ++u) __builtin_nontemporal_store(acc[j][u], reinterpret_cast<f32x4*>(dst_o + EPC * c + 4 * u));
     }
   }
   if (hw == 0 && lane < nv) dst_l[lane] = m + __builtin_amdgcn_logf(z) * 0.69314718055994531f;
@@ -731,7 +743,7 @@ __device__ __attribute__((always_inline)) inline void merge_rows(int n, SO so, S
 // still multiply keeps the CU's matrix cores busy with the next blocks'
 // work: the composition's HBM reads overlap the other blocks' MFMA work
 // instead of running as a pass of their own after it.
-template <int D, int WAVES>
+template <int D, int WAVES, typename ST>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
                           amdgpu_waves_per_eu(waves_per_simd<D>(), waves_per_simd<D>())))
 void step_kernel(const StepParams p) {
@@ -777,7 +789,7 @@ void step_kernel(const StepParams p) {
       attend_keys<D, WAVES, false>(w, p.K + head, p.V + head, p.N, p.S, k0, len_k, len_k, k_lds0, k_lds1, v_lds0,
                                    v_lds1, map, off, hw, p.scale_log2, live);
       const size_t slot = static_cast<size_t>(h) * p.P * p.P + static_cast<size_t>(q) * p.P + k;
-      store_state<D>(w, p.O + slot * p.S * D, p.LSE + slot * p.S, row0, len_q, hw, l32);
+      store_state<D, ST>(w, static_cast<ST*>(p.O) + slot * p.S * D, p.LSE + slot * p.S, row0, len_q, hw, l32);
     }
     // the wave's state stores complete before it reads them back
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
@@ -787,8 +799,8 @@ void step_kernel(const StepParams p) {
   if (nv > 0) {
     const size_t slot0 = static_cast<size_t>(h) * p.P * p.P + static_cast<size_t>(q) * p.P;   // pair (q, 0)
     const size_t out0 = static_cast<size_t>(h) * p.N + static_cast<size_t>(q0) + r0;
-    merge_rows<D>(
-        p.P, [&](int k) { return p.O + ((slot0 + k) * p.S + r0) * D; },
+    merge_rows<D, ST>(
+        p.P, [&](int k) { return static_cast<const ST*>(p.O) + ((slot0 + k) * p.S + r0) * D; },
         [&](int k) { return p.LSE + (slot0 + k) * p.S + r0; }, p.Oout + out0 * D, p.LSEout + out0, nv, lane);
   }
 }
@@ -798,7 +810,7 @@ void step_kernel(const StepParams p) {
 // over its members' keys, with the gap over q when q sits inside the
 // group), each state stored into its slot buffer; then each wave composes
 // its rows over q's live slots, as step_kernel does for the pair slots.
-template <int D, int WAVES>
+template <int D, int WAVES, typename ST>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
                           amdgpu_waves_per_eu(waves_per_simd<D>(), waves_per_simd<D>())))
 void group_step_kernel(const GroupStepParams p) {
@@ -844,7 +856,7 @@ void group_step_kernel(const GroupStepParams p) {
       reset_state<D>(w);
       attend_keys<D, WAVES, true>(w, p.K + head, p.V + head, p.N, p.S, k0, len_k, len0, k_lds0, k_lds1, v_lds0,
                                   v_lds1, map, off, hw, p.scale_log2, live);
-      store_state<D>(w, p.gO[s] + row_base * D, p.gLSE[s] + row_base, row0, len_q, hw, l32);
+      store_state<D, ST>(w, static_cast<ST*>(p.gO[s]) + row_base * D, p.gLSE[s] + row_base, row0, len_q, hw, l32);
     }
     // the wave's state stores complete before it reads them back
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
@@ -853,31 +865,48 @@ void group_step_kernel(const GroupStepParams p) {
   const int nv = min(32, len_q - r0);
   if (nv > 0) {
     const size_t out0 = static_cast<size_t>(h) * p.N + static_cast<size_t>(q0) + r0;
-    merge_rows<D>(
-        p.nl[q], [&](int k) { return p.gO[p.lslot[q][k]] + (row_base + r0) * D; },
+    merge_rows<D, ST>(
+        p.nl[q], [&](int k) { return static_cast<const ST*>(p.gO[p.lslot[q][k]]) + (row_base + r0) * D; },
         [&](int k) { return p.gLSE[p.lslot[q][k]] + row_base + r0; }, p.Oout + out0 * D, p.LSEout + out0, nv, lane);
+  }
+}
+
+template <int D, int WAVES, typename ST>
+void launch_st(PartialParams& p, hipStream_t stream) {
+  if (p.grouped) {
+    hipLaunchKernelGGL((partial_kernel<D, WAVES, true, ST>), dim3(p.n_blocks), dim3(64 * WAVES), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((partial_kernel<D, WAVES, false, ST>), dim3(p.n_blocks), dim3(64 * WAVES), 0, stream, p);
   }
 }
 
 template <int D, int WAVES>
 hipError_t launch(PartialParams& p, hipStream_t stream) {
-  if (p.grouped) {
-    hipLaunchKernelGGL((partial_kernel<D, WAVES, true>), dim3(p.n_blocks), dim3(64 * WAVES), 0, stream, p);
+  if (p.state_bf16) {
+    launch_st<D, WAVES, __bf16>(p, stream);
   } else {
-    hipLaunchKernelGGL((partial_kernel<D, WAVES, false>), dim3(p.n_blocks), dim3(64 * WAVES), 0, stream, p);
+    launch_st<D, WAVES, float>(p, stream);
   }
   return hipGetLastError();
 }
 
 template <int D, int WAVES>
 hipError_t launch_step_d(StepParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((step_kernel<D, WAVES>), dim3(p.n_blocks), dim3(64 * WAVES), 0, stream, p);
+  if (p.state_bf16) {
+    hipLaunchKernelGGL((step_kernel<D, WAVES, __bf16>), dim3(p.n_blocks), dim3(64 * WAVES), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((step_kernel<D, WAVES, float>), dim3(p.n_blocks), dim3(64 * WAVES), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
 template <int D, int WAVES>
 hipError_t launch_group_step_d(GroupStepParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((group_step_kernel<D, WAVES>), dim3(p.n_blocks), dim3(64 * WAVES), 0, stream, p);
+  if (p.state_bf16) {
+    hipLaunchKernelGGL((group_step_kernel<D, WAVES, __bf16>), dim3(p.n_blocks), dim3(64 * WAVES), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((group_step_kernel<D, WAVES, float>), dim3(p.n_blocks), dim3(64 * WAVES), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

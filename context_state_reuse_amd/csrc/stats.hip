@@ -18,6 +18,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace ditango {
@@ -29,7 +31,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 256;        // drift kernel
 constexpr int kStatsThreads = 1024;  // stats kernel
 
-template <int D>
+template <int D, typename ST>
 __global__ __launch_bounds__(kStatsThreads) void stats_kernel(const StatsParams p) {
   constexpr int C = D / 4;                  // chunks of 4 values per row (8 bytes of bf16)
   constexpr int RG = kStatsThreads / C;     // rows summed in parallel
@@ -63,15 +65,19 @@ __global__ __launch_bounds__(kStatsThreads) void stats_kernel(const StatsParams 
 
   // signature (block-uniform branch)
   if (!((p.sel[q] >> k) & 1u)) return;
-  const __bf16* o = p.O + slot * p.S * D;
+  const ST* o = static_cast<const ST*>(p.O) + slot * p.S * D;
   const int rg = tid / C, c = tid % C;
   if (rg < RG) {
     // four independent accumulators: four loads in flight per thread
     // bf16 -> fp32 is exact: the pattern in the high half of a word
     auto row = [&](int r) {
-      const u32x2 u = *reinterpret_cast<const u32x2*>(o + static_cast<size_t>(r) * D + 4 * c);
-      return f32x4{__builtin_bit_cast(float, u.x << 16), __builtin_bit_cast(float, u.x & 0xffff0000u),
-                   __builtin_bit_cast(float, u.y << 16), __builtin_bit_cast(float, u.y & 0xffff0000u)};
+      if constexpr (std::is_same<ST, __bf16>::value) {
+        const u32x2 u = *reinterpret_cast<const u32x2*>(o + static_cast<size_t>(r) * D + 4 * c);
+        return f32x4{__builtin_bit_cast(float, u.x << 16), __builtin_bit_cast(float, u.x & 0xffff0000u),
+                     __builtin_bit_cast(float, u.y << 16), __builtin_bit_cast(float, u.y & 0xffff0000u)};
+      } else {
+        return *reinterpret_cast<const f32x4*>(o + static_cast<size_t>(r) * D + 4 * c);
+      }
     };
     f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0, a3 = a0;
     int r = rg;
@@ -142,10 +148,20 @@ hipError_t launch_stats(const StatsParams& p, hipStream_t stream) {
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(blocks)), block(kStatsThreads);
+  const bool bf = p.state_bf16 != 0;
   switch (p.d) {
-    case 64: hipLaunchKernelGGL(stats_kernel<64>, grid, block, 0, stream, p); break;
-    case 72: hipLaunchKernelGGL(stats_kernel<72>, grid, block, 0, stream, p); break;
-    case 128: hipLaunchKernelGGL(stats_kernel<128>, grid, block, 0, stream, p); break;
+    case 64:
+      if (bf) hipLaunchKernelGGL((stats_kernel<64, __bf16>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((stats_kernel<64, float>), grid, block, 0, stream, p);
+      break;
+    case 72:
+      if (bf) hipLaunchKernelGGL((stats_kernel<72, __bf16>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((stats_kernel<72, float>), grid, block, 0, stream, p);
+      break;
+    case 128:
+      if (bf) hipLaunchKernelGGL((stats_kernel<128, __bf16>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((stats_kernel<128, float>), grid, block, 0, stream, p);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -26,9 +26,11 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Work is enqueued on it and the call returns.
  *   - Q, K, V are bfloat16, laid out [H][N][d] contiguous, in device memory.
- *   - Cached states keep OUT as bfloat16 (ditango_bf16_t: the bit pattern,
- *     round to nearest even from the fp32 result) and LSE as fp32; the
- *     composed outputs the merges write are fp32.
+ *   - Cached states keep LSE in fp32 and OUT in fp32 (the default) or, when
+ *     the shape asks for it (state_dtype = DITANGO_STATE_BF16), in bfloat16
+ *     (the bit pattern, rounded to nearest even from the fp32 result), which
+ *     halves the cache and the bytes the composition reads; the composed
+ *     outputs the merges write are fp32 either way.
  *   - The mask is a host array uint8 [P][P] (row = query partition q, column
  *     = KV partition k); 1 = COMPUTE (fresh), 0 = REUSE.
  *   - Return value: DITANGO_OK (0) or a negative code; the message of the
@@ -52,7 +54,8 @@ extern "C" {
 
 #define DITANGO_MAX_P 32       /* largest partition count                             */
 
-typedef uint16_t ditango_bf16_t;  /* a bfloat16 value as its 16-bit pattern              */
+#define DITANGO_STATE_F32  0  /* cached OUT in fp32 (4 bytes per element)            */
+#define DITANGO_STATE_BF16 1  /* cached OUT in bfloat16 (2 bytes per element)        */
 
 /* Shape of one attention layer.  d must be 64, 72 or 128; 1 <= P <= 32;
  * every partition must be non-empty (P * ceil(N/P) - N < ceil(N/P)). */
@@ -62,12 +65,14 @@ typedef struct {
   int32_t d;      /* head dimension                                    */
   int32_t P;      /* partitions                                        */
   float   scale;  /* score scale applied to q.k, normally 1/sqrt(d)    */
+  int32_t state_dtype;  /* DITANGO_STATE_F32 (0) or DITANGO_STATE_BF16 (1): cached OUT */
 } ditango_shape_t;
 
 /* The attention-state cache (attention-state section and the
  * ring-based composed attention section: fresh states are stored for
  * reuse at later steps).  One slot per (head, pair), pair id = q*P + k:
- *   O   device bf16 [H][P*P][S][d]  -- row r of slot (h, q*P+k) is OUT of
+ *   O   device [H][P*P][S][d]       -- fp32 or bf16 (shape.state_dtype); row r
+ *                                     of slot (h, q*P+k) is OUT of
  *                                     query row q*S + r against partition k
  *   LSE device fp32 [H][P*P][S]     -- its log-sum-exp
  *   tc  host int32 [P*P]            -- step at which the pair was last fresh,
@@ -78,7 +83,7 @@ typedef struct {
 typedef struct {
   ditango_shape_t shape;
   int32_t  S;     /* rows per partition, ceil(N/P); set by ditango_states_init */
-  ditango_bf16_t* O;
+  void*    O;     /* fp32 or bf16 elements, per shape.state_dtype */
   float*   LSE;
   int32_t* tc;
 } ditango_states_t;
@@ -86,7 +91,8 @@ typedef struct {
 /* Bytes the caller must allocate for the cache of `shape` (the per-pair
  * state cache of the attention-state section, Fig. 6: one (OUT, LSE) state
  * per head and (query partition, KV partition) pair): *o_bytes for O
- * = H*P*P*S*d*2 and *lse_bytes for LSE = H*P*P*S*4 (either pointer may be
+ * = H*P*P*S*d*e (e = 4 for fp32 states, 2 for bf16) and *lse_bytes for
+ * LSE = H*P*P*S*4 (either pointer may be
  * NULL).  Returns their sum, or 0 if the shape is invalid (message in
  * ditango_last_error()).  No allocation, no device call. */
 size_t ditango_states_bytes(const ditango_shape_t* shape, size_t* o_bytes, size_t* lse_bytes);
@@ -98,7 +104,7 @@ size_t ditango_states_bytes(const ditango_shape_t* shape, size_t* o_bytes, size_
  * Nothing is copied or allocated; the buffers stay the caller's.
  * Errors: DITANGO_EINVAL. */
 int ditango_states_init(ditango_states_t* st, const ditango_shape_t* shape,
-                        ditango_bf16_t* O, float* LSE, int32_t* tc);
+                        void* O, float* LSE, int32_t* tc);
 
 /* Fresh partial attention for every pair with mask[q][k] = 1 (COMPUTE), on
  * every head: the attention state of query partition q against KV partition
@@ -108,7 +114,8 @@ int ditango_states_init(ditango_states_t* st, const ditango_shape_t* shape,
  * with mask = 0 (REUSE) are not touched and no work is launched for them.
  * Computes with bf16 inputs, fp32 accumulation, fp32 softmax statistics;
  * probabilities are rounded to bf16 before the product with V; OUT is
- * stored rounded to bf16, LSE in fp32.  Checks before launching anything
+ * normalised by the fp32 sum of the unrounded probabilities (d = 72: of the
+ * rounded ones) and stored in the cache's format, LSE in fp32.  Checks before launching anything
  * that every REUSE pair holds a
  * state (tc >= 0), else returns DITANGO_ENOCACHE.  Does not change tc (see
  * ditango_state_cache_update).  Errors: EINVAL, ENOCACHE, EHIP. */
@@ -221,7 +228,8 @@ int ditango_window_residual_merge(const ditango_states_t* st, const uint8_t* win
  * which is their composition (Eq. 4) up to rounding.  The row merge composes
  * the non-empty slots.  Slot buffers are separate so that slots released by
  * a group merge can be freed:
- *   O[s]   device bf16 [H][P][S][d]   row r of (h, q) = query row q*S + r
+ *   O[s]   device [H][P][S][d], fp32 or bf16 (shape.state_dtype); row r of
+ *          (h, q) = query row q*S + r
  *   LSE[s] device fp32 [H][P][S]
  *   tc     host int32 [P][DITANGO_MAX_SLOTS]; tc[q][s] = last step slot s of
  *          q was computed (-1: never); entries of empty slots stay -1.
@@ -234,7 +242,7 @@ typedef struct {
   int32_t  S;                      /* ceil(N/P), set by ditango_gstates_init  */
   int32_t  g0;                     /* group size at init and after a reset    */
   int32_t  g;                      /* current group size, g0 * (merge factors) */
-  ditango_bf16_t* O[DITANGO_MAX_SLOTS];   /* slot buffers; NULL beyond the used slots */
+  void*    O[DITANGO_MAX_SLOTS];   /* slot buffers; NULL beyond the used slots */
   float*   LSE[DITANGO_MAX_SLOTS];
   int32_t* tc;
 } ditango_gstates_t;
@@ -252,7 +260,7 @@ size_t ditango_gstates_slot_bytes(const ditango_shape_t* shape, size_t* o_bytes,
  * sizes above) and a host tc array of P * DITANGO_MAX_SLOTS int32; marks
  * every slot empty (tc = -1).  Errors: EINVAL. */
 int ditango_gstates_init(ditango_gstates_t* st, const ditango_shape_t* shape, int32_t g,
-                         ditango_bf16_t* const* O, float* const* LSE, int32_t* tc);
+                         void* const* O, float* const* LSE, int32_t* tc);
 
 /* Fresh partial attention for every COMPUTE slot (see above) on every head,
  * written over the slot.  REUSE slots are not touched and get no work.
@@ -313,7 +321,7 @@ int ditango_group_fit(ditango_gstates_t* st, size_t budget_bytes, int32_t k, voi
 /* Return to the original group size g0 before an anchor step: binds
  * ditango_group_slots(P, g0) slot buffers (kept ones may be passed again)
  * and marks every slot empty.  Errors: EINVAL. */
-int ditango_group_reset(ditango_gstates_t* st, ditango_bf16_t* const* O, float* const* LSE);
+int ditango_group_reset(ditango_gstates_t* st, void* const* O, float* const* LSE);
 
 /* Group-aligned locality mask (state-selection section: selection per group;
  * locality of Fig. 5a): writes the pair mask uint8 [P][P] with, per query

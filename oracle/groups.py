@@ -48,12 +48,12 @@ def n_slots(P: int, g: int) -> int:
     return 1 + n_groups(P, g)
 
 
-def slot_bytes(H: int, N: int, P: int, d: int) -> int:
-    """Device bytes of one slot of the grouped cache: OUT [H][P][S][d] kept
-    in bf16 (2 bytes) plus LSE [H][P][S] in fp32 (4 bytes), the layout the
-    library allocates per slot."""
+def slot_bytes(H: int, N: int, P: int, d: int, out_bytes: int = 4) -> int:
+    """Device bytes of one slot of the grouped cache: OUT [H][P][S][d] of
+    out_bytes per element (4: fp32, the default; 2: bf16) plus LSE [H][P][S]
+    in fp32, the layout the library allocates per slot."""
     S = -(-N // P)
-    return H * P * S * (2 * d + 4)
+    return H * P * S * (out_bytes * d + 4)
 
 
 def merges_to_fit(P: int, g: int, k: int, bytes_per_slot: int, budget: int) -> int:

@@ -18,12 +18,13 @@ def to_device(bits: np.ndarray):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda")
 
 
-def run_steps(w, masks=None, steps=None, on_step=None, label="", fused=False):
+def run_steps(w, masks=None, steps=None, on_step=None, label="", fused=False, state_dtype="fp32"):
     """Run the library over the steps of workload w.
 
     masks: optional {t: mask}; default is the library's own mask builder.
     fused: each step is one ditango_step call (the fused partial + merge
     launch) instead of partial, t_c update and merge called one by one.
+    state_dtype: the cache's OUT format ("fp32" or "bf16").
     on_step(t, mask, reused, cache, O, LSE) is called after each step
     (after a device synchronisation).
     """
@@ -32,7 +33,7 @@ def run_steps(w, masks=None, steps=None, on_step=None, label="", fused=False):
     import context_state_reuse_amd as lib
 
     n = w.steps if steps is None else steps
-    cache = lib.StateCache(w.H, w.N, w.d, w.P)
+    cache = lib.StateCache(w.H, w.N, w.d, w.P, state_dtype=state_dtype)
     stream = synth.InputStream(w)
     O = torch.empty((w.H, w.N, w.d), dtype=torch.float32, device="cuda")
     LSE = torch.empty((w.H, w.N), dtype=torch.float32, device="cuda")
@@ -49,7 +50,7 @@ def run_steps(w, masks=None, steps=None, on_step=None, label="", fused=False):
             reused = lib.ditango_state_cache_update(cache, mask, t)
             lib.ditango_state_merge(cache, O, LSE)
         torch.cuda.synchronize()
-        log(f"  [{label or w.name}{' fused' if fused else ''}] step {t}: fresh {int(mask.sum())}/{w.P * w.P} pairs, {time.time() - t0:.1f}s")
+        log(f"  [{label or w.name}{' fused' if fused else ''} {state_dtype}] step {t}: fresh {int(mask.sum())}/{w.P * w.P} pairs, {time.time() - t0:.1f}s")
         if on_step is not None:
             on_step(t, mask, reused, cache, O, LSE)
         del Q, K, V
@@ -57,12 +58,13 @@ def run_steps(w, masks=None, steps=None, on_step=None, label="", fused=False):
 
 
 def run_group_steps(w, g, masks=None, steps=None, compose_at=None, on_step=None, label="", budget_at=None,
-                    fused=False):
+                    fused=False, state_dtype="fp32"):
     """Run the grouped-cache path of the library over the steps of workload w.
 
     fused: the slots' fresh states and the composition in one launch
     (ditango_group_attn_partial_merge), then the t_c update, instead of
     partial, t_c update and merge one by one.
+    state_dtype: the slots' OUT format ("fp32" or "bf16").
 
     compose_at: optional {t: k}: merge groups by k right before step t.
     budget_at: optional {t: bytes}: right before step t, merge groups by 2
@@ -74,7 +76,7 @@ def run_group_steps(w, g, masks=None, steps=None, compose_at=None, on_step=None,
     import context_state_reuse_amd as lib
 
     n = w.steps if steps is None else steps
-    cache = lib.GroupedStateCache(w.H, w.N, w.d, w.P, g)
+    cache = lib.GroupedStateCache(w.H, w.N, w.d, w.P, g, state_dtype=state_dtype)
     stream = synth.InputStream(w)
     O = torch.empty((w.H, w.N, w.d), dtype=torch.float32, device="cuda")
     LSE = torch.empty((w.H, w.N), dtype=torch.float32, device="cuda")
@@ -99,7 +101,7 @@ def run_group_steps(w, g, masks=None, steps=None, compose_at=None, on_step=None,
             computed = lib.ditango_group_cache_update(cache, mask, t)
             lib.ditango_group_merge(cache, O, LSE)
         torch.cuda.synchronize()
-        log(f"  [{label or w.name}{' fused' if fused else ''}] step {t}: g={cache.g}, {int(computed.sum())} slots computed, "
+        log(f"  [{label or w.name}{' fused' if fused else ''} {state_dtype}] step {t}: g={cache.g}, {int(computed.sum())} slots computed, "
             f"{time.time() - t0:.1f}s")
         if on_step is not None:
             on_step(t, mask, computed, cache, O, LSE)

@@ -37,7 +37,7 @@ static std::mt19937_64 rng(12345);
 static int ri(int a, int b) { return std::uniform_int_distribution<int>(a, b)(rng); }
 static float rf() { return std::uniform_real_distribution<float>(0.f, 1.f)(rng); }
 static float* fake(uintptr_t a) { return reinterpret_cast<float*>(a); }
-static ditango_bf16_t* fake16(uintptr_t a) { return reinterpret_cast<ditango_bf16_t*>(a); }
+static void* fakev(uintptr_t a) { return reinterpret_cast<void*>(a); }
 
 static float wild() {   // finite, zero, inf, NaN, negative
   switch (ri(0, 9)) {
@@ -83,7 +83,8 @@ int main() {
   // per-pair cache
   const int dims[] = {64, 72, 128, 65};
   for (int it = 0; it < 3000; ++it) {
-    ditango_shape_t sh = {ri(0, 3), ri(0, 3000), dims[ri(0, 3)], ri(0, 33), ri(0, 20) ? 0.125f : wild()};
+    ditango_shape_t sh = {ri(0, 3), ri(0, 3000), dims[ri(0, 3)], ri(0, 33), ri(0, 20) ? 0.125f : wild(),
+                          ri(0, 20) ? ri(0, 1) : ri(-1, 3)};
     // now and then a sequence at the 32-bit K/V offset limit (N * d around 2^30)
     if (ri(0, 9) == 0) sh.N = (1 << 30) / sh.d + ri(-2, 1);
     ditango_states_t st;
@@ -91,7 +92,7 @@ int main() {
     std::vector<int32_t> tc(40 * 40, 7);
     size_t ob = 0, lb = 0;
     ditango_states_bytes(&sh, &ob, &lb);
-    int rc = ditango_states_init(&st, &sh, fake16(0x100000), fake(0x200000 + (ri(0, 20) ? 0 : 4)), tc.data());
+    int rc = ditango_states_init(&st, &sh, fakev(0x100000), fake(0x200000 + (ri(0, 20) ? 0 : 4)), tc.data());
     ++calls;
     if (rc) continue;
     int P = sh.P;
@@ -126,13 +127,13 @@ int main() {
   }
   // grouped cache
   for (int it = 0; it < 3000; ++it) {
-    ditango_shape_t sh = {ri(1, 3), ri(1, 3000), dims[ri(0, 2)], ri(0, 33), 0.125f};
+    ditango_shape_t sh = {ri(1, 3), ri(1, 3000), dims[ri(0, 2)], ri(0, 33), 0.125f, ri(0, 20) ? ri(0, 1) : ri(-1, 3)};
     ditango_gstates_t st;
     std::memset(&st, 0, sizeof st);
     std::vector<int32_t> tc(40 * DITANGO_MAX_SLOTS, 9);
-    std::vector<ditango_bf16_t*> O(DITANGO_MAX_SLOTS);
+    std::vector<void*> O(DITANGO_MAX_SLOTS);
     std::vector<float*> L(DITANGO_MAX_SLOTS);
-    for (int s = 0; s < DITANGO_MAX_SLOTS; ++s) { O[s] = fake16(0x1000000 + 0x10000 * s); L[s] = fake(0x3000000 + 0x10000 * s); }
+    for (int s = 0; s < DITANGO_MAX_SLOTS; ++s) { O[s] = fakev(0x1000000 + 0x10000 * s); L[s] = fake(0x3000000 + 0x10000 * s); }
     int g = ri(0, 34);
     int rc = ditango_gstates_init(&st, &sh, g, O.data(), L.data(), tc.data());
     ++calls;

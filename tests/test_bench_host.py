@@ -25,9 +25,11 @@ def test_fresh_flops_and_merge_bytes_image():
     m[0, 0] = m[3, 4] = 1
     # every partition of the image workload holds S = 2048 tokens
     assert bench.fresh_flops(w, m) == 2 * 4.0 * 2048 * 2048 * 72 * 16
-    # a cached state row: 72 bf16 + one fp32 LSE = 148 bytes; an output row: 73 fp32 = 292 bytes
-    assert bench.merge_bytes(w) == 16 * 16384 * (8 * 148 + 292)
-    assert bench.state_store_bytes(w, m) == 16 * 148 * 2 * 2048
+    # a cached state row: 72 fp32 + one fp32 LSE = 292 bytes (bf16 OUT: 148); an output row: 292 bytes
+    assert bench.merge_bytes(w) == 16 * 16384 * 9 * 73 * 4
+    assert bench.state_store_bytes(w, m) == 16 * 73 * 4 * 2 * 2048
+    assert bench.merge_bytes(w, bf16=True) == 16 * 16384 * (8 * 148 + 292)
+    assert bench.state_store_bytes(w, m, bf16=True) == 16 * 148 * 2 * 2048
 
 
 def test_fresh_flops_ragged_stress():

@@ -41,7 +41,8 @@ def _oracle_steps(w, g, masks, steps, compose_at, rows=None, heads=None, budget_
     return out, orc
 
 
-def _compare(w, g, masks=None, steps=None, compose_at=None, rows=None, heads=None, label=None, budget_at=None):
+def _compare(w, g, masks=None, steps=None, compose_at=None, rows=None, heads=None, label=None, budget_at=None,
+             state_dtype="fp32"):
     steps = w.steps if steps is None else steps
     ref, orc = _oracle_steps(w, g, masks, steps, compose_at, rows, heads, budget_at)
     heads = list(range(w.H)) if heads is None else heads
@@ -85,8 +86,8 @@ def _compare(w, g, masks=None, steps=None, compose_at=None, rows=None, heads=Non
     for fused in (False, True):       # two launches per step, then the fused group step launch
         snap.clear()
         run_group_steps(w, g, masks=masks, steps=steps, compose_at=compose_at, on_step=check, label=label,
-                        budget_at=budget_at, fused=fused)
-    log(f"  {label}: worst slot state OUT max {worst[0]:.2e}, mean {worst[1]:.2e}, LSE {worst[2]:.2e}")
+                        budget_at=budget_at, fused=fused, state_dtype=state_dtype)
+    log(f"  {label} ({state_dtype} states): worst slot state OUT max {worst[0]:.2e}, mean {worst[1]:.2e}, LSE {worst[2]:.2e}")
 
 
 GROUPED = [
@@ -105,13 +106,23 @@ def test_grouped_workload_matches_oracle(w, g):
     _compare(w, g, label=f"{w.name} g={g}")
 
 
-def test_group_merges_match_oracle():
-    """g = 1 -> 2 -> 4 with reuse across the merges, then fresh work at g = 4."""
+GROUPED_BF16 = [GROUPED[1], GROUPED[3], GROUPED[4]]
+
+
+@pytest.mark.parametrize("w,g", GROUPED_BF16, ids=[f"{w.name}_g{g}" for w, g in GROUPED_BF16])
+def test_grouped_bf16_states_match_oracle(w, g):
+    _compare(w, g, label=f"{w.name} g={g}", state_dtype="bf16")
+
+
+@pytest.mark.parametrize("state_dtype", ["fp32", "bf16"])
+def test_group_merges_match_oracle(state_dtype):
+    """g = 1 -> 2 -> 4 with reuse across the merges, then fresh work at g = 4
+    (group merges write the merged slot in the cache's own format)."""
     w = synth.get("video_100").scaled(name="merge_p8", F=3, Hh=13, W=21, H=2, P=8, steps=6)
     rng = np.random.default_rng(11)
     masks = {0: all_fresh(8), 1: (rng.random((8, 8)) < 0.4).astype(np.uint8), 2: all_reuse(8),
              3: all_reuse(8), 4: (rng.random((8, 8)) < 0.3).astype(np.uint8), 5: all_reuse(8)}
-    _compare(w, 1, masks=masks, compose_at={2: 2, 4: 2}, label="merges")
+    _compare(w, 1, masks=masks, compose_at={2: 2, 4: 2}, label="merges", state_dtype=state_dtype)
 
 
 def test_memory_budget_merges_match_oracle():
@@ -120,7 +131,7 @@ def test_memory_budget_merges_match_oracle():
     forces two more (g = 8, 2 slots), with reuse across the merges."""
     from oracle.groups import slot_bytes
     w = synth.get("video_100").scaled(name="budget_p8", F=3, Hh=13, W=21, H=2, P=8, steps=6)
-    sb = slot_bytes(w.H, w.N, w.P, w.d)
+    sb = slot_bytes(w.H, w.N, w.P, w.d)       # fp32 slots, the cache's default
     rng = np.random.default_rng(5)
     masks = {0: all_fresh(8), 1: (rng.random((8, 8)) < 0.4).astype(np.uint8), 2: all_reuse(8),
              3: (rng.random((8, 8)) < 0.3).astype(np.uint8), 4: all_reuse(8), 5: all_reuse(8)}
@@ -140,7 +151,7 @@ def test_group_merge_frees_slots_and_reset():
     import context_state_reuse_amd as lib
     w = synth.get("stress").scaled(name="free", F=2, Hh=16, W=27, H=2, steps=3)
     cache = lib.GroupedStateCache(w.H, w.N, w.d, w.P, 2)
-    assert cache.n_slots == 17 and len(cache.O) == 17
+    assert cache.n_slots == 17 and len(cache.O) == 17 and cache.O[0].dtype == torch.float32
     before = cache.device_bytes
     q = torch.zeros((w.H, w.N, w.d), dtype=torch.bfloat16, device="cuda")
     lib.ditango_group_attn_partial(q, q, q, all_fresh(w.P), cache)

@@ -54,7 +54,7 @@ REDUCED = [
 ]
 
 
-def _run_full_compare(w, masks=None, label=None):
+def _run_full_compare(w, masks=None, label=None, state_dtype="fp32"):
     """Whole-tensor comparison of every step of a small workload."""
     ref = {}
 
@@ -92,13 +92,23 @@ def _run_full_compare(w, masks=None, label=None):
 
     for fused in (False, True):       # three calls per step, then the fused step launch
         snap.clear()
-        run_steps(w, masks=masks, on_step=check, label=label, fused=fused)
-    log(f"  {label or w.name}: worst pair state OUT max {worst[0]:.2e}, mean {worst[1]:.2e}, LSE {worst[2]:.2e}")
+        run_steps(w, masks=masks, on_step=check, label=label, fused=fused, state_dtype=state_dtype)
+    log(f"  {label or w.name} ({state_dtype} states): worst pair state OUT max {worst[0]:.2e}, mean {worst[1]:.2e}, LSE {worst[2]:.2e}")
 
 
 @pytest.mark.parametrize("w", REDUCED, ids=[w.name for w in REDUCED])
 def test_reduced_workload_matches_oracle(w):
     _run_full_compare(w)
+
+
+BF16_STATES = [REDUCED[0], REDUCED[1], REDUCED[4], REDUCED[5], REDUCED[6]]
+
+
+@pytest.mark.parametrize("w", BF16_STATES, ids=[w.name for w in BF16_STATES])
+def test_reduced_workload_bf16_states_match_oracle(w):
+    """The opt-in bf16 state format (d = 64, 72, 128; P = 4 to 32) to the
+    same bar: rounding a state's OUT to bf16 adds at most 2^-9 relative."""
+    _run_full_compare(w, state_dtype="bf16")
 
 
 EDGE = [
@@ -172,11 +182,11 @@ def _sample_rows(w, per_part=4, seed=0):
     return np.unique(np.array(rows))
 
 
-FULL = ["image", "video_100", "video_50", "video_25", "long", "stress"]
+FULL = [(n, "fp32") for n in ("image", "video_100", "video_50", "video_25", "long", "stress")] + [("long", "bf16")]
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled_rows(name):
+@pytest.mark.parametrize("name,state_dtype", FULL, ids=[f"{n}_{s}" for n, s in FULL])
+def test_full_size_sampled_rows(name, state_dtype):
     import torch
     w = synth.get(name)
     heads = [0, w.H - 1]
@@ -196,7 +206,7 @@ def test_full_size_sampled_rows(name):
         got[t] = dict(mask=mask.copy(), reused=reused.copy(), tc=cache.tc_matrix,
                       O=O[h_t][:, r_t].cpu().numpy(), LSE=LSE[h_t][:, r_t].cpu().numpy(), so=so, sl=sl)
 
-    run_steps(w, on_step=grab, fused=True)           # the launch bench.py times
+    run_steps(w, on_step=grab, fused=True, state_dtype=state_dtype)   # the launch bench.py times
     prev = None
     worst = [0, 0, 0]
     ref_steps = {}
@@ -220,7 +230,7 @@ def test_full_size_sampled_rows(name):
                         assert np.array_equal(g["so"][hi, sel, k], prev["so"][hi, sel, k])
                         assert np.array_equal(g["sl"][hi, sel, k], prev["sl"][hi, sel, k])
         prev = g
-    log(f"  {name}: sampled merged OUT max {worst[0]:.2e} mean {worst[1]:.2e} LSE {worst[2]:.2e}")
+    log(f"  {name} ({state_dtype} states): sampled merged OUT max {worst[0]:.2e} mean {worst[1]:.2e} LSE {worst[2]:.2e}")
 
 
 # ---------------------------------------------------------------- reuse laws

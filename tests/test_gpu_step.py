@@ -19,11 +19,11 @@ pytestmark = pytest.mark.gpu
 REL_O, ABS_LSE = 1e-5, 1e-5
 
 
-def _compare_paths(w, masks=None):
+def _compare_paths(w, masks=None, state_dtype="fp32"):
     import torch
     import context_state_reuse_amd as lib
-    a = lib.StateCache(w.H, w.N, w.d, w.P)
-    b = lib.StateCache(w.H, w.N, w.d, w.P)
+    a = lib.StateCache(w.H, w.N, w.d, w.P, state_dtype=state_dtype)
+    b = lib.StateCache(w.H, w.N, w.d, w.P, state_dtype=state_dtype)
     stream = synth.InputStream(w)
     for t in range(w.steps):
         Q, K, V = (to_device(x) for x in stream.next())
@@ -44,13 +44,16 @@ def _compare_paths(w, masks=None):
             assert torch.equal(a.O[:, sl, :n], b.O[:, sl, :n]) and torch.equal(a.LSE[:, sl, :n], b.LSE[:, sl, :n])
 
 
-@pytest.mark.parametrize("name", ["tiny", "image_small", "long_small", "stress_small"])
-def test_fused_step_equals_three_calls(name):
-    w = {"tiny": lambda: synth.get("tiny"),
+SMALL = {"tiny": lambda: synth.get("tiny"),
          "image_small": lambda: synth.get("image").scaled(name="image_small", F=1, Hh=57, W=97, H=2),
          "long_small": lambda: synth.get("long").scaled(name="long_small", F=7, Hh=19, W=23, H=2),
-         "stress_small": lambda: synth.get("stress").scaled(name="stress_small", F=5, Hh=16, W=27, H=3)}[name]()
-    _compare_paths(w)
+         "stress_small": lambda: synth.get("stress").scaled(name="stress_small", F=5, Hh=16, W=27, H=3)}
+
+
+@pytest.mark.parametrize("state_dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("name", ["tiny", "image_small", "long_small", "stress_small"])
+def test_fused_step_equals_three_calls(name, state_dtype):
+    _compare_paths(SMALL[name](), state_dtype=state_dtype)
 
 
 def test_fused_rows_without_fresh_pairs():
@@ -83,18 +86,20 @@ def test_partial_merge_leaves_tc_and_checks_cache():
     assert (cache.tc == 0).all()
 
 
-@pytest.mark.parametrize("name,g", [("stress_small", 4), ("image_small", 3), ("long_small", 4)])
-def test_group_fused_step_equals_two_launches(name, g):
+GROUP_CASES = [("stress_small", 4, "fp32"), ("image_small", 3, "fp32"), ("long_small", 4, "fp32"),
+               ("stress_small", 4, "bf16"), ("long_small", 4, "bf16")]
+
+
+@pytest.mark.parametrize("name,g,state_dtype", GROUP_CASES, ids=[f"{n}_g{g}_{s}" for n, g, s in GROUP_CASES])
+def test_group_fused_step_equals_two_launches(name, g, state_dtype):
     """The grouped cache: ditango_group_attn_partial_merge against
     ditango_group_attn_partial + ditango_group_merge -- slot states bit for
     bit, the composed output within fp32 rounding of the weight sums."""
     import torch
     import context_state_reuse_amd as lib
-    w = {"image_small": lambda: synth.get("image").scaled(name="image_small", F=1, Hh=57, W=97, H=2),
-         "long_small": lambda: synth.get("long").scaled(name="long_small", F=7, Hh=19, W=23, H=2),
-         "stress_small": lambda: synth.get("stress").scaled(name="stress_small", F=5, Hh=16, W=27, H=3)}[name]()
-    a = lib.GroupedStateCache(w.H, w.N, w.d, w.P, g)
-    b = lib.GroupedStateCache(w.H, w.N, w.d, w.P, g)
+    w = SMALL[name]()
+    a = lib.GroupedStateCache(w.H, w.N, w.d, w.P, g, state_dtype=state_dtype)
+    b = lib.GroupedStateCache(w.H, w.N, w.d, w.P, g, state_dtype=state_dtype)
     stream = synth.InputStream(w)
     for t in range(w.steps):
         Q, K, V = (to_device(x) for x in stream.next())

@@ -42,10 +42,11 @@ class _FakeG:
 
 
 def test_struct_layout():
-    assert binding.ditango_gstates_t.O.offset == 32
-    assert binding.ditango_gstates_t.LSE.offset == 32 + 8 * MS
-    assert binding.ditango_gstates_t.tc.offset == 32 + 16 * MS
-    assert ctypes.sizeof(binding.ditango_gstates_t) == 40 + 16 * MS
+    # shape (24 B) and three int32, padded to pointer alignment
+    assert binding.ditango_gstates_t.O.offset == 40
+    assert binding.ditango_gstates_t.LSE.offset == 40 + 8 * MS
+    assert binding.ditango_gstates_t.tc.offset == 40 + 16 * MS
+    assert ctypes.sizeof(binding.ditango_gstates_t) == 48 + 16 * MS
 
 
 @pytest.mark.parametrize("P,g,want", [(32, 1, 0), (31, 1, 32), (32, 2, 17), (16, 4, 5), (5, 2, 4), (8, 100, 2),
@@ -61,7 +62,7 @@ def test_slot_bytes():
     shape = lib.make_shape(w.H, w.N, w.d, w.P)
     ob, lb = ctypes.c_size_t(0), ctypes.c_size_t(0)
     tot = binding.lib.ditango_gstates_slot_bytes(ctypes.byref(shape), ctypes.byref(ob), ctypes.byref(lb))
-    assert ob.value == w.H * w.P * w.S * w.d * 2 and lb.value == w.H * w.P * w.S * 4   # bf16 OUT, fp32 LSE
+    assert ob.value == w.H * w.P * w.S * w.d * 4 and lb.value == w.H * w.P * w.S * 4   # fp32 OUT and LSE
     assert tot == ob.value + lb.value
     # g = 4: 5 slots per query partition instead of 16 pair slots
     per_pair, _ = lib.ditango_states_bytes(shape)

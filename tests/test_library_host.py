@@ -4,6 +4,8 @@ call here launches GPU work."""
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import numpy as np
 import pytest
@@ -34,21 +36,48 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_struct_layout():
-    assert lib.ditango_version() == 5
-    assert ctypes.sizeof(binding.ditango_shape_t) == 20
-    assert binding.ditango_states_t.O.offset == 24 and ctypes.sizeof(binding.ditango_states_t) == 48
+    assert lib.ditango_version() == 6
+    assert ctypes.sizeof(binding.ditango_shape_t) == 24
+    assert binding.ditango_states_t.O.offset == 32 and ctypes.sizeof(binding.ditango_states_t) == 56
+
+
+STRUCTS = ("ditango_shape_t", "ditango_states_t", "ditango_gstates_t", "ditango_planner_t")
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="no C compiler")
+def test_ctypes_structs_match_the_c_header(tmp_path):
+    """Every ctypes mirror has the C compiler's field offsets and sizes."""
+    lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "ditango.h"', "int main(void) {"]
+    want = []
+    for name in STRUCTS:
+        cls = getattr(binding, name)
+        lines.append(f'printf("%zu\\n", sizeof({name}));')
+        want.append(ctypes.sizeof(cls))
+        for field, _ in cls._fields_:
+            lines.append(f'printf("%zu\\n", offsetof({name}, {field}));')
+            want.append(getattr(cls, field).offset)
+    lines.append("return 0; }")
+    src, exe = tmp_path / "layout.c", tmp_path / "layout"
+    src.write_text("\n".join(lines))
+    b = subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                       capture_output=True, text=True, timeout=120)
+    assert b.returncode == 0, b.stderr
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, timeout=60).stdout.split()]
+    assert got == want
 
 
 @pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
 def test_states_bytes(name):
     w = synth.get(name)
     ob, lb = lib.ditango_states_bytes(lib.make_shape(w.H, w.N, w.d, w.P))
-    assert ob == w.H * w.P * w.P * w.S * w.d * 2       # bf16 OUT
+    assert ob == w.H * w.P * w.P * w.S * w.d * 4       # fp32 OUT (the default)
     assert lb == w.H * w.P * w.P * w.S * 4
-    # a state's OUT row is d bf16 values: half the 2*d bf16 values of the K
+    ob16, lb16 = lib.ditango_states_bytes(lib.make_shape(w.H, w.N, w.d, w.P, state_dtype="bf16"))
+    assert ob16 * 2 == ob and lb16 == lb
+    # a bf16 state's OUT row is d values: half the 2*d bf16 values of the K
     # and V rows of a key (attention-state section: a state is about half the
     # size of the KV it summarises)
-    assert ob // (w.H * w.P * w.P * w.S) == (2 * w.d * 2) // 2
+    assert ob16 // (w.H * w.P * w.P * w.S) == (2 * w.d * 2) // 2
 
 
 @pytest.mark.parametrize("name", sorted(synth.WORKLOADS))

@@ -255,7 +255,8 @@ def test_memory_trigger_merge_counts():
     with pytest.raises(ValueError):
         merges_to_fit(32, 1, 2, B, 2 * B - 1)              # not even one group fits
     from oracle.groups import slot_bytes
-    assert slot_bytes(2, 10, 4, 64) == 2 * 4 * 3 * (2 * 64 + 4)  # S = ceil(10 / 4) = 3; bf16 OUT, fp32 LSE
+    assert slot_bytes(2, 10, 4, 64) == 4 * 2 * 4 * 3 * 65        # S = ceil(10 / 4) = 3; fp32 OUT and LSE
+    assert slot_bytes(2, 10, 4, 64, out_bytes=2) == 2 * 4 * 3 * (2 * 64 + 4)   # bf16 OUT
 
 
 def test_memory_trigger_merges_like_explicit_compose():
