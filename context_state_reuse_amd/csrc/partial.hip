@@ -739,10 +739,10 @@ __device__ __attribute__((always_inline)) inline void merge_rows(int n, SO so, S
 // row tile): the fresh pairs of the partition's row of the mask, one after
 // the other over the same query rows, each state stored into its slot; then
 // each wave composes its rows' P states (the fresh ones just stored and the
-// cached ones) into the output.  A block whose wave merges while others
-// still multiply keeps the CU's matrix cores busy with the next blocks'
-// work: the composition's HBM reads overlap the other blocks' MFMA work
-// instead of running as a pass of their own after it.
+// cached ones) into the output.  The composition needs no pass of its own
+// over the states: at d = 64 and 72 (three blocks per CU) it overlaps the
+// other blocks' matrix work; at d = 128 a block fills its CU and the phase
+// runs at that CU's memory rate while the other CUs keep multiplying.
 template <int D, int WAVES, typename ST>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES, 64 * WAVES),
                           amdgpu_waves_per_eu(waves_per_simd<D>(), waves_per_simd<D>())))
