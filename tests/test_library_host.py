@@ -80,6 +80,32 @@ def test_states_bytes(name):
     assert ob16 // (w.H * w.P * w.P * w.S) == (2 * w.d * 2) // 2
 
 
+def test_state_dtype_is_checked():
+    """Only DITANGO_STATE_F32 (0) and DITANGO_STATE_BF16 (1) are state formats:
+    any other value is refused before sizes, binding or launches."""
+    assert (lib.DITANGO_STATE_F32, lib.DITANGO_STATE_BF16) == (0, 1)
+    with pytest.raises(ValueError):
+        lib.make_shape(2, 64, 64, 4, state_dtype="fp16")
+    tc = np.zeros(16, np.int32)
+    for bad in (-1, 2, 7):
+        sh = lib.make_shape(2, 64, 64, 4)
+        sh.state_dtype = bad
+        with pytest.raises(lib.DitangoError):
+            lib.ditango_states_bytes(sh)
+        assert "state_dtype" in binding.lib.ditango_last_error().decode()
+        st = binding.ditango_states_t()
+        rc = binding.lib.ditango_states_init(ctypes.byref(st), ctypes.byref(sh), ctypes.c_void_p(0x10000),
+                                             ctypes.c_void_p(0x20000), ctypes.c_void_p(tc.ctypes.data))
+        assert rc == lib.DITANGO_EINVAL
+        assert binding.lib.ditango_gstates_slot_bytes(ctypes.byref(sh), None, None) == 0
+    # a grouped slot's OUT halves with bf16 states, its LSE does not
+    o32, l32, o16, l16 = (ctypes.c_size_t() for _ in range(4))
+    binding.lib.ditango_gstates_slot_bytes(ctypes.byref(lib.make_shape(2, 64, 72, 4)), ctypes.byref(o32), ctypes.byref(l32))
+    binding.lib.ditango_gstates_slot_bytes(ctypes.byref(lib.make_shape(2, 64, 72, 4, state_dtype="bf16")),
+                                           ctypes.byref(o16), ctypes.byref(l16))
+    assert o32.value == 2 * 4 * 16 * 72 * 4 and o16.value * 2 == o32.value and l16.value == l32.value == 2 * 4 * 16 * 4
+
+
 @pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
 def test_mask_builder_matches_oracle(name):
     w = synth.get(name)
