@@ -115,9 +115,9 @@ int ditango_states_init(ditango_states_t* st, const ditango_shape_t* shape,
  * Computes with bf16 inputs, fp32 accumulation, fp32 softmax statistics;
  * probabilities are rounded to bf16 before the product with V; OUT is
  * normalised by the fp32 sum of the unrounded probabilities (d = 72: of the
- * rounded ones) and stored in the cache's format, LSE in fp32.  Checks before launching anything
- * that every REUSE pair holds a
- * state (tc >= 0), else returns DITANGO_ENOCACHE.  Does not change tc (see
+ * rounded ones) and stored in the cache's format, LSE in fp32.  Checks
+ * before launching anything that every REUSE pair holds a state (tc >= 0),
+ * else returns DITANGO_ENOCACHE.  Does not change tc (see
  * ditango_state_cache_update).  Errors: EINVAL, ENOCACHE, EHIP. */
 int ditango_attn_partial(const void* Q, const void* K, const void* V,
                          const uint8_t* mask, ditango_states_t* st, void* stream);
