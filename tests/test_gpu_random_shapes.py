@@ -1,8 +1,9 @@
 """GPU parity on seeded random shapes and masks (both caches) against the
 fp64 oracles: head dims 64/72/128, 1 to 32 partitions, token counts that
 leave ragged and one-token partitions, several heads, per-step random masks
-including all-reuse steps; group sizes from 1 to P.  The per-pair cache runs
-both as three calls per step and as the fused step launch."""
+including all-reuse steps; group sizes from 1 to P.  Both caches run as
+separate launches with fp32 states and as fused launches, with fp32 states
+in even-numbered cases and bf16 states in odd-numbered ones."""
 import numpy as np
 import pytest
 
@@ -59,8 +60,9 @@ def test_random_shape_both_caches(w, masks, g):
             check_state(O[h].cpu().numpy(), LSE[h].cpu().numpy(), ref[t]["O"][h], ref[t]["LSE"][h],
                         f"{w.name} step {t} head {h}")
 
+    fused_dtype = "bf16" if int(w.name[4:]) % 2 else "fp32"
     run_steps(w, masks=masks, on_step=check, label=w.name)
-    run_steps(w, masks=masks, on_step=check, label=w.name, fused=True)
+    run_steps(w, masks=masks, on_step=check, label=w.name, fused=True, state_dtype=fused_dtype)
 
     from synth import InputStream, bf16_bits_to_f64
     orc = GroupedStateReuseOracle(w.N, w.P, w.d, g)
@@ -78,4 +80,5 @@ def test_random_shape_both_caches(w, masks, g):
                         f"{w.name} grouped g={g} step {t} head {h}")
 
     run_group_steps(w, g, masks=masks, on_step=gcheck, label=f"{w.name} g={g}")
+    run_group_steps(w, g, masks=masks, on_step=gcheck, label=f"{w.name} g={g}", fused=True, state_dtype=fused_dtype)
     run_group_steps(w, g, masks=masks, on_step=gcheck, label=f"{w.name} g={g}", fused=True)
