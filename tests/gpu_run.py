@@ -109,7 +109,7 @@ def run_group_steps(w, g, masks=None, steps=None, compose_at=None, on_step=None,
     return cache
 
 
-def run_window_residual_steps(w, window, steps=None, on_step=None, label=""):
+def run_window_residual_steps(w, window, steps=None, on_step=None, label="", state_dtype="fp32"):
     """Window attention with residual sharing through the library: step 0
     computes every pair and caches the residual, later steps compute the
     window pairs only.  on_step(t, cache, R, O, LSE) after each step."""
@@ -118,7 +118,7 @@ def run_window_residual_steps(w, window, steps=None, on_step=None, label=""):
     import context_state_reuse_amd as lib
 
     n = w.steps if steps is None else steps
-    cache = lib.StateCache(w.H, w.N, w.d, w.P)
+    cache = lib.StateCache(w.H, w.N, w.d, w.P, state_dtype=state_dtype)
     stream = synth.InputStream(w)
     R = torch.empty((w.H, w.N, w.d), dtype=torch.float32, device="cuda")
     O = torch.empty_like(R)

@@ -55,14 +55,17 @@ def _oracle_stats(w, orc_cache, merged_lse):
     return W, SIG
 
 
-@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
-def test_pair_stats_match_oracle(w):
+STATS_CASES = [(w, "fp32") for w in CASES] + [(CASES[0], "bf16"), (CASES[2], "bf16")]
+
+
+@pytest.mark.parametrize("w,state_dtype", STATS_CASES, ids=[f"{w.name}_{sd}" for w, sd in STATS_CASES])
+def test_pair_stats_match_oracle(w, state_dtype):
     import torch
 
     import context_state_reuse_amd as lib
     steps = 3
     orc = StateReuseOracle(w.N, w.P, w.d)
-    cache = lib.StateCache(w.H, w.N, w.d, w.P)
+    cache = lib.StateCache(w.H, w.N, w.d, w.P, state_dtype=state_dtype)
     stream = synth.InputStream(w)
     ones = np.ones((w.P, w.P), np.uint8)
     SIG = torch.zeros((w.H, w.P, w.P, w.d), dtype=torch.float32, device="cuda")

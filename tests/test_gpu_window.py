@@ -21,7 +21,7 @@ def _window(w):
     return radius_mask(w.P, 1) if w.policy == "radius" else nearest_mask(w.P, min(w.n_fresh, w.P))
 
 
-def _compare(w, rows=None, heads=None, steps=None, label=None):
+def _compare(w, rows=None, heads=None, steps=None, label=None, state_dtype="fp32"):
     from synth import InputStream, bf16_bits_to_f64
     import torch
     steps = w.steps if steps is None else steps
@@ -47,7 +47,7 @@ def _compare(w, rows=None, heads=None, steps=None, label=None):
                 check_state(Rc[i, rws], np.zeros(len(rws)), resid[h], np.zeros(len(rws)),
                             f"{label} residual head {h}")
 
-    run_window_residual_steps(w, win, steps=steps, on_step=check, label=label)
+    run_window_residual_steps(w, win, steps=steps, on_step=check, label=label, state_dtype=state_dtype)
     log(f"  {label}: ok")
 
 
@@ -64,6 +64,12 @@ CASES = [
 @pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
 def test_window_residual_matches_oracle(w):
     _compare(w, label=w.name)
+
+
+@pytest.mark.parametrize("w", [CASES[1], CASES[3]], ids=[CASES[1].name, CASES[3].name])
+def test_window_residual_bf16_states_match_oracle(w):
+    """The window states composed from bf16 OUT; the residual stays fp32."""
+    _compare(w, label=f"{w.name} bf16 states", state_dtype="bf16")
 
 
 def test_window_residual_full_size_sampled_rows():
