@@ -170,13 +170,15 @@ def test_group_merge_frees_slots_and_reset():
         lib.ditango_group_merge(cache)
 
 
-FULL_GROUPED = [("stress", 4), ("long", 4), ("video_25", 2), ("image", 3)]
+FULL_GROUPED = [("stress", 4, "fp32"), ("long", 4, "fp32"), ("video_25", 2, "fp32"), ("image", 3, "fp32"),
+                ("stress", 4, "bf16")]
 
 
-@pytest.mark.parametrize("name,g", FULL_GROUPED, ids=[f"{n}_g{g}" for n, g in FULL_GROUPED])
-def test_full_size_grouped_sampled_rows(name, g):
+@pytest.mark.parametrize("name,g,state_dtype", FULL_GROUPED, ids=[f"{n}_g{g}_{sd}" for n, g, sd in FULL_GROUPED])
+def test_full_size_grouped_sampled_rows(name, g, state_dtype):
     import torch
     w = synth.get(name)
     steps = min(w.steps, 3)
-    _compare(w, g, steps=steps, rows=_sample_rows(w), heads=[0, w.H - 1], label=f"{name} g={g} full")
+    _compare(w, g, steps=steps, rows=_sample_rows(w), heads=[0, w.H - 1], label=f"{name} g={g} full",
+             state_dtype=state_dtype)
     torch.cuda.empty_cache()

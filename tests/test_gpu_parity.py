@@ -182,7 +182,8 @@ def _sample_rows(w, per_part=4, seed=0):
     return np.unique(np.array(rows))
 
 
-FULL = [(n, "fp32") for n in ("image", "video_100", "video_50", "video_25", "long", "stress")] + [("long", "bf16")]
+FULL = [(n, "fp32") for n in ("image", "video_100", "video_50", "video_25", "long", "stress")] + \
+       [("long", "bf16"), ("stress", "bf16")]
 
 
 @pytest.mark.parametrize("name,state_dtype", FULL, ids=[f"{n}_{s}" for n, s in FULL])
